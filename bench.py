@@ -1,0 +1,261 @@
+"""Benchmark of one DSA sparse decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1_l32k]
+
+A step is the whole hot path for one batch: bf16 indexer query -> fp8 codes,
+fp8 indexer scores over every cached token, exact top-2048 (per split, then
+merged), split-K sparse absorbed-MLA attention over the selected paged fp8
+rows, and the LSE merge.  Inputs are seeded synthetic tensors already resident
+in HBM.  Prints ONE JSON line (rank 0).
+
+The default workload is bulk decode at the metric's point: 64 requests, one
+query row each, 32768 cached tokens each, 256-token pages shuffled in the
+pool, 64 x 128 fp8 indexer, 32 MLA heads over 576-wide fp8 rows, top-2048.
+
+Timing: W untimed steps, then K steps between two device synchronisations,
+replayed from a HIP graph of one step (``--eager`` launches the five kernels
+directly instead).  A second, eager pass of K steps brackets every kernel
+with HIP events on the stream it runs on, for per-kernel durations and the
+roofline of the dominant kernel.  The oracle (fp64, CPU) is timed on a bounded
+sample of the same workload as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode steps/s (index+top-k+sparse MLA) at B=64 L=32k; % peak HBM BW"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c1_l32k")
+    ap.add_argument("--index-splits", type=int, default=None)
+    ap.add_argument("--attn-splits", type=int, default=None)
+    ap.add_argument("--eager", action="store_true", help="launch kernels directly, no HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--seed", type=int, default=None)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(inp) -> dict:
+    """Bytes the method must move per step, from the actual geometry.
+
+    Per row with V visible slots: 132 B per slot of index key + scale,
+    580 B per selected MLA row + scale, 4 B per page-table entry, the bf16
+    indexer query (64 x 128 x 2) and head weights (64 x 4), the bf16 MLA query
+    (H x 576 x 2), the bf16 output (H x 512 x 2) and its lse (H x 4).
+    Intermediates (scores, top-k lists, split partials) are not counted.
+    """
+    vis = inp.row_vis.cpu().tolist()
+    p, k, h = inp.page_size, inp.top_k, inp.mla_heads
+    idx = sum(132 * v + 4 * math.ceil(v / p) + 64 * 128 * 2 + 64 * 4 for v in vis)
+    mla = sum(580 * min(v, k) + h * 576 * 2 + h * 512 * 2 + h * 4 for v in vis)
+    return {"step": idx + mla, "index_kernel": sum(132 * v + 4 * math.ceil(v / p) + 64 * 128 + 64 * 8
+                                                     for v in vis)}
+
+
+def cpu_baseline(inp_gpu, seconds: float) -> dict:
+    """The oracle, as it stands, on rows of the same workload until the time
+    budget is spent; scaled to steps/s of the full batch."""
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    from oracle import dsa_oracle as O
+    from sparse_attention_decode_dsa_amd import workload as W
+
+    rows = list(range(inp_gpu.n_rows))
+    done = 0
+    t_total = 0.0
+    # deterministic order: every 8th row first, then the rest
+    order = rows[::8] + [r for r in rows if r % 8]
+    for r in order:
+        sub = W.as_numpy(W.subset(inp_gpu, [r]))
+        t0 = time.perf_counter()
+        O.decode_step(sub, inp_gpu.cfg.index_splits, inp_gpu.cfg.attn_splits)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": done / t_total / inp_gpu.n_rows, "unit": "steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {inp_gpu.n_rows} rows of one step, timed one row at a time "
+                      f"({t_total:.1f} s), scaled by {inp_gpu.n_rows}/{done} to a whole step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (one process, one MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_decode_dsa_amd import dsa
+    from sparse_attention_decode_dsa_amd import workload as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = W.make(args.config, seed=args.seed, device=dev)
+    step = dsa.DecodeStep(inp, args.index_splits, args.attn_splits)
+    stream = torch.cuda.current_stream()
+
+    # Correctness gate before timing: one eager step, no device faults.
+    step.run()
+    torch.cuda.synchronize()
+    dsa.check_status(step.status)
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    graph = None
+    if not args.eager:
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                step.run()
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step.run()
+        torch.cuda.synchronize()
+
+    def one():
+        if graph is not None:
+            graph.replay()
+        else:
+            step.run()
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    dsa.check_status(step.status)
+
+    # Per-kernel durations: HIP events around each launch on the launch stream.
+    names = ["quantize_q", "index_scores", "topk", "sparse_mla", "lse_merge"]
+    evs = {n: [] for n in names}
+    i = inp
+    for _ in range(args.steps):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        marks[0].record(stream)
+        dsa.quantize_q(i.q_idx, step.q_code, step.q_scale)
+        marks[1].record(stream)
+        dsa.index_scores(step.q_code, step.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table,
+                         i.kv_lens, i.row_req, i.row_vis, group_rows=step.group_rows,
+                         score_stride=step.score_stride, scores=step.scores, status=step.status)
+        marks[2].record(stream)
+        dsa.topk(step.scores, i.row_vis, i.top_k, step.index_splits, workspace=step.workspace,
+                 topk_idx=step.topk_idx, topk_count=step.topk_count, status=step.status)
+        marks[3].record(stream)
+        if step.attn_splits == 1:
+            dsa.sparse_mla_decode(i.q_mla, i.kv_code, i.kv_scale, i.page_table, i.row_req, i.row_vis,
+                                  step.topk_idx, step.topk_count, 1, i.sm_scale, out=step.out,
+                                  out_lse=step.out_lse, status=step.status)
+            marks[4].record(stream)
+        else:
+            dsa.sparse_mla_decode(i.q_mla, i.kv_code, i.kv_scale, i.page_table, i.row_req, i.row_vis,
+                                  step.topk_idx, step.topk_count, step.attn_splits, i.sm_scale,
+                                  part_o=step.part_o, part_lse=step.part_lse, status=step.status)
+            marks[4].record(stream)
+            dsa.lse_merge(step.part_o, step.part_lse, out=step.out, out_lse=step.out_lse)
+        marks[5].record(stream)
+        for j, n in enumerate(names):
+            evs[n].append((marks[j], marks[j + 1]))
+    torch.cuda.synchronize()
+    dsa.check_status(step.status)
+    kern_us = {n: 1e3 * sum(a.elapsed_time(b) for a, b in evs[n]) / len(evs[n]) for n in names}
+
+    ab = algorithmic_bytes(inp)
+    idx_us = kern_us["index_scores"]
+    achieved = ab["index_kernel"] / (idx_us * 1e-6) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "index_scores_c1_l32k_traffic.json")
+    if os.path.exists(tfile) and args.config == "c1_l32k":
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("kernel_source_sha") == _kernel_sha():
+            traffic = t.get("bytes_per_launch")
+
+    line = {
+        "metric": METRIC,
+        "value": 1e3 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {inp.n_rows} decode rows, kv_len "
+                        f"{int(inp.row_vis.min())}..{int(inp.row_vis.max())}, top-{inp.top_k}, "
+                        f"indexer 64x128 fp8, MLA {inp.mla_heads} heads x 576 fp8, page {inp.page_size}",
+            "batch": inp.n_rows, "kv_len_max": int(inp.row_vis.max()), "top_k": inp.top_k,
+            "page_size": inp.page_size, "mla_heads": inp.mla_heads,
+            "index_splits": step.index_splits, "attn_splits": step.attn_splits,
+            "launch": "eager" if graph is None else "hipgraph",
+        },
+        "roofline": {
+            "kernel": "index_scores",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "step_algorithmic_bytes": ab["step"],
+        "step_hbm_frac": ab["step"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("index_scores.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "sparse_attention_decode_dsa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

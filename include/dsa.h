@@ -1,0 +1,194 @@
+/*
+ * dsa.h -- C ABI of libdsa.so: one DSA sparse decode step on an MI355X (gfx950).
+ *
+ * The step (page "[ROCm] Support decode context parallel (DCP) for GLM-5 /
+ * DeepSeek-V3.2", sgl-project/sglang PR #42618, sections Motivation and
+ * Modifications):
+ *   1. dsa_quantize_q        bf16 indexer queries -> fp8 E4M3FN codes + scales
+ *   2. dsa_index_scores      fp8 indexer score of every visible cached token
+ *   3. dsa_topk              exact top-k per row: per-split local top-k, then an
+ *                            exact merge of the candidates
+ *   4. dsa_sparse_mla_decode absorbed-MLA attention over the selected paged fp8
+ *                            rows, split along the selected list into
+ *                            (partial output, natural-log LSE) pairs
+ *   5. dsa_lse_merge         merge of the split partials by their LSE
+ *
+ * Conventions shared by every entry point:
+ *  - Every array pointer is DEVICE memory owned by the caller.  The library
+ *    never allocates, never frees, never synchronises and never falls back to
+ *    another path.  Calls are enqueued on `stream` in order and return before
+ *    the work runs; they are stateless and may be called from several threads.
+ *  - All arrays are dense row-major with the shapes given per call.
+ *  - The return value is the HOST validation status: DSA_OK (0) when the work
+ *    was enqueued, a negative DSA_ERR_* otherwise, in which case nothing was
+ *    enqueued.  dsa_status_string() names every code.
+ *  - Kernels check what only the device can see (page ids, row geometry,
+ *    top-k indices).  A violation ORs a DSA_DEV_* bit into the caller's int32
+ *    `status` word (device memory, not cleared by the library) and the
+ *    offending row's output is written as empty (scores -inf, count 0,
+ *    output 0, lse -inf) rather than read out of bounds.
+ *  - Page pool layout: NP pages of P tokens.  Indexer keys: k_code uint8
+ *    [NP, P, 128] (E4M3FN codes) and k_scale float32 [NP, P].  MLA rows:
+ *    kv_code uint8 [NP, P, 576] (512 latent then 64 rope, E4M3FN) and
+ *    kv_scale float32 [NP, P].  A token's value is code * its scale.
+ *  - Block table: page_table int32 [batch, max_pages]; logical slot t of
+ *    request b lives at physical row page_table[b][t / P] * P + t % P.
+ *    Entries past a request's span are -1 (page "DeepSeek V4 DSpark
+ *    Internals", kernel mapping).
+ *  - Rows are query tokens: row r belongs to request row_req[r] and sees the
+ *    slots [0, row_vis[r]) of it (causal rows of MTP verify and prefill see
+ *    fewer than kv_len).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+/* Host validation status (return value of every entry point). */
+enum {
+    DSA_OK = 0,
+    DSA_ERR_NULL = -1,        /* a required pointer is NULL */
+    DSA_ERR_SHAPE = -2,       /* a size, stride or count is out of range or inconsistent */
+    DSA_ERR_UNSUPPORTED = -3, /* valid but not built: head count, head dim, page size */
+    DSA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the size query */
+    DSA_ERR_LAUNCH = -5       /* the HIP runtime refused a launch */
+};
+
+/* Bits ORed by kernels into the caller's device status word. */
+enum {
+    DSA_DEV_PAGE_OOB = 1,   /* a slot inside a row's span maps to a page id < 0 or >= num_pages */
+    DSA_DEV_TOPK_OOB = 2,   /* a selected index is < 0 or >= row_vis, or top-k count out of range */
+    DSA_DEV_ROW_RANGE = 4,  /* row_req out of [0, batch), or row_vis < 0, > kv_len,
+                               > max_pages * page_size or > score_stride */
+    DSA_DEV_GROUP = 8,      /* rows of one scoring group belong to different requests */
+    DSA_DEV_NAN = 16        /* a NaN score reached the top-k (ordered, but reported) */
+};
+
+/* DSA_ABI_VERSION of the built library; loaders refuse a mismatch. */
+int dsa_abi_version(void);
+
+/* Static, never-NULL name of a DSA_OK / DSA_ERR_* code ("unknown" otherwise). */
+const char* dsa_status_string(int status);
+
+/*
+ * dsa_quantize_q -- input side of the fp8 indexer.
+ * The subject page's indexer scores fp8 keys; the query arrives as bf16, so it
+ * is brought to fp8 E4M3FN with one power-of-two scale per (row, head):
+ * scale = 2^ceil(log2(amax / 448)) (scale 1 for an all-zero head) and
+ * code = round-to-nearest-even(q / scale).
+ *   q_bf16   [n_rows, n_heads, head_dim] bf16 bit patterns
+ *   q_code   [n_rows, n_heads, head_dim] uint8 out
+ *   q_scale  [n_rows, n_heads] float32 out
+ * Supported: head_dim == 128, n_heads >= 1.  n_rows == 0 enqueues nothing.
+ */
+int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
+                   uint8_t* q_code, float* q_scale, hipStream_t stream);
+
+/*
+ * dsa_index_scores -- fp8 lightning-indexer scores (subject page,
+ * Modifications, indexer decode: the index-K cache is scored per token).
+ *   scores[r][t] = k_scale[t] * sum_h (head_w[r][h] * q_scale[r][h])
+ *                  * relu( dec(q_code[r][h]) . dec(k_code[t]) )     for t < row_vis[r]
+ *   scores[r][t] = -inf                      for row_vis[r] <= t < score_stride
+ * which equals sum_h w_h * relu(q_h . k_t) for positive scales.
+ *   q_code [n_rows, 64, 128] uint8, q_scale [n_rows, 64] f32, head_w [n_rows, 64] f32
+ *   k_code [num_pages, page_size, 128] uint8, k_scale [num_pages, page_size] f32
+ *   page_table [batch, max_pages] i32, kv_lens [batch] i32
+ *   row_req [n_rows] i32, row_vis [n_rows] i32
+ *   scores [n_rows, score_stride] f32 out
+ * group_rows (1..8, dividing n_rows): that many consecutive rows are scored
+ * against one stream of keys (MTP verify and prefill rows of one request);
+ * all rows of a group must share a request, else DSA_DEV_GROUP.
+ * Supported: n_heads == 64, head_dim == 128, page_size a power of two in
+ * [16, 1024].  All scales must be finite and > 0.
+ */
+int dsa_index_scores(const uint8_t* q_code, const float* q_scale, const float* head_w,
+                     const uint8_t* k_code, const float* k_scale, const int32_t* page_table,
+                     const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,
+                     int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
+                     int32_t page_size, int32_t n_heads, int32_t head_dim, int32_t group_rows,
+                     float* scores, int32_t score_stride, int32_t* status, hipStream_t stream);
+
+/*
+ * Workspace bytes dsa_topk needs for n_splits > 1: candidate keys and slots
+ * [n_rows, n_splits, top_k] and per-split counts.  0 when n_splits == 1.
+ */
+size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits);
+
+/*
+ * dsa_topk -- exact top-k per row under the total order (score descending,
+ * slot ascending), so equal scores keep the lower slot (subject page,
+ * Motivation: the top 2048 of the whole sequence; Modifications, indexer
+ * decode: local top-k per shard merged into the exact global top-k).
+ * Row r's slots [0, row_vis[r]) are cut into n_splits contiguous ranges of
+ * ceil(row_vis/n_splits); each keeps its top-min(top_k, len) candidates and
+ * one merge keeps the top-k of their union.  n_splits == 1 selects directly.
+ *   scores [n_rows, score_stride] f32 (only [0, row_vis) is read)
+ *   topk_idx [n_rows, top_k] i32 out: selected slots in ascending order, then -1
+ *   topk_count [n_rows] i32 out: min(top_k, row_vis)
+ * Limits: 1 <= top_k <= 8192; ceil(score_stride / n_splits) <= 32768;
+ * n_splits * top_k <= 32768 when n_splits > 1; n_splits <= 64.
+ */
+int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
+             int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes,
+             int32_t* topk_idx, int32_t* topk_count, int32_t* status, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_decode -- split-K absorbed-MLA attention over each row's
+ * selected slots (subject page, Modifications, sparse decode: the split-K
+ * kernel attends the selected slots and also returns the LSE; the per-row
+ * selected count bounds the work; a lone split writes the final output and
+ * natural-log LSE directly).
+ * For row r, head h, split s over entries [s*c, min(n, (s+1)*c)) of
+ * topk_idx[r] with n = topk_count[r], c = ceil(n / n_splits):
+ *   x_t   = dec(kv_code[t]) * kv_scale[t]            (576 wide)
+ *   l_t   = sm_scale * (q[r][h] . x_t)
+ *   o_s   = sum_t e^{l_t - m} x_t[0:512] / sum_t e^{l_t - m},  lse_s = m + ln sum_t e^{l_t - m}
+ * Empty split: o_s = 0, lse_s = -inf.
+ *   q [n_rows, n_heads, 576] bf16 bit patterns
+ *   kv_code [num_pages, page_size, 576] uint8, kv_scale [num_pages, page_size] f32
+ *   page_table [batch, max_pages] i32, row_req / row_vis [n_rows] i32
+ *   topk_idx [n_rows, top_k] i32, topk_count [n_rows] i32
+ * n_splits == 1: writes out [n_rows, n_heads, 512] bf16 (round to nearest
+ *   even) and, if out_lse != NULL, out_lse [n_rows, n_heads] f32; part_* unused.
+ * n_splits > 1: writes part_o [n_rows, n_heads, n_splits, 512] f32 and
+ *   part_lse [n_rows, n_heads, n_splits] f32; out / out_lse unused
+ *   (dsa_lse_merge finishes the row).
+ * Supported: n_heads in {16, 32}, page_size a power of two in [16, 1024],
+ * 1 <= n_splits <= 64, 1 <= top_k <= 8192.
+ */
+int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_code, const float* kv_scale,
+                          const int32_t* page_table, const int32_t* row_req, const int32_t* row_vis,
+                          const int32_t* topk_idx, const int32_t* topk_count, int32_t n_rows,
+                          int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
+                          int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
+                          float* part_o, float* part_lse, uint16_t* out, float* out_lse,
+                          int32_t* status, hipStream_t stream);
+
+/*
+ * dsa_lse_merge -- merge split partials by their natural-log LSE (subject
+ * page, split-K commit note: the reduce can also store the natural-log LSE).
+ *   lse = ln sum_s e^{lse_s};  out = sum_s e^{lse_s - lse} o_s
+ * Splits with lse_s = -inf are skipped; a row with no finite lse_s gets
+ * out = 0 and lse = -inf.
+ *   part_o [n_rows, n_heads, n_splits, d_v] f32, part_lse [n_rows, n_heads, n_splits] f32
+ *   out [n_rows, n_heads, d_v] bf16 (round to nearest even)
+ *   out_lse [n_rows, n_heads] f32, may be NULL
+ * Supported: d_v == 512, 1 <= n_splits <= 64.
+ */
+int dsa_lse_merge(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
+                  int32_t n_splits, int32_t d_v, uint16_t* out, float* out_lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,79 @@
+"""Build libdsa.so in-tree: every HIP source in csrc/ for gfx950 plus the host ABI.
+
+    python -m sparse_attention_decode_dsa_amd.build
+
+Each source is compiled on its own (in parallel) and the objects are linked
+with hipcc.  The library lands next to this file, where the binding loads it.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OBJDIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libdsa.so")
+
+SOURCES = ["dsa_api.cpp", "quantize_q.hip", "index_scores.hip", "topk.hip",
+           "sparse_mla.hip", "lse_merge.hip"]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libdsa.so")
+
+
+def flags() -> list[str]:
+    return [
+        "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+        "-Wall", "-Wextra", "-Werror",
+        # Keep the compiler from forming packed fp32 instructions.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE,
+    ]
+
+
+def _compile(src: str) -> tuple[str, str]:
+    os.makedirs(OBJDIR, exist_ok=True)
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    path = os.path.join(CSRC, src)
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [hipcc()] + flags() + lang + ["-c", path, "-o", obj]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (p.stdout + p.stderr).splitlines() if noise not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{err}")
+    return obj, err
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source for gfx950 and link libdsa.so; returns its path."""
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    for obj, msg in results:
+        if verbose and msg.strip():
+            print(msg, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"linking libdsa.so failed:\n{' '.join(cmd)}\n{p.stdout}{p.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

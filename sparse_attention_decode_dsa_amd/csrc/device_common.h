@@ -1,0 +1,133 @@
+// Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
+// fp8 / bf16 conversions, wavefront reductions and a workgroup scan.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// D(16x16 f32) += A(16x128 fp8) * B(128x16 fp8).  Lane l holds row/column
+// l % 16 of A/B and 32 K-bytes for lane group l / 16; D lane l holds rows
+// 4*(l/16) + i of column l % 16.  Zero scale operands select the unscaled
+// v_mfma_f32_16x16x128_f8f6f4 (format 0 = E4M3 for both operands).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16); lane l holds row/column
+// l % 16 and the 8 K-values of lane group l / 16.
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two E4M3FN bytes (the low or, with HIGH, the high half of `w`) to two
+// bf16; exact, since every E4M3FN value is a bf16 value.
+template <bool HIGH>
+__device__ __forceinline__ v2bf fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH);
+}
+
+// Eight E4M3FN bytes (two dwords) to eight bf16.
+__device__ __forceinline__ v8bf fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    v2bf a = fp8x2_to_bf16x2<false>(lo), b = fp8x2_to_bf16x2<true>(lo);
+    v2bf c = fp8x2_to_bf16x2<false>(hi), d = fp8x2_to_bf16x2<true>(hi);
+    v8bf r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Order-preserving map of an fp32 onto uint32: a < b  <=>  key(a) < key(b)
+// for non-NaN values, and -0.0 and +0.0 share one key (they are equal
+// scores); -inf maps to 0x007FFFFF.
+__device__ __forceinline__ uint32_t monotone_key(float f) {
+    uint32_t u = (f == 0.0f) ? 0u : __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+// Reductions over the 16 lanes that share l / 16.
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Inclusive scan of uint32 over a wavefront.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive scan over a workgroup of NT threads (NT a multiple of 64,
+// NT / 64 <= 64).  `scratch` holds NT / 64 + 1 words of LDS.  Returns the
+// exclusive prefix and writes the total into *total.  Contains barriers:
+// every thread of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    uint32_t inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) scratch[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        uint32_t x = lane < NW ? scratch[lane] : 0u;
+        uint32_t xi = wave_inclusive_scan(x);
+        if (lane < NW) scratch[lane] = xi - x;
+        if (lane == NW - 1) scratch[NW] = xi;
+    }
+    __syncthreads();
+    uint32_t r = inc - v + scratch[w];
+    *total = scratch[NW];
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ void flag(int32_t* status, int32_t bit) {
+    atomicOr(status, bit);
+}
+
+}  // namespace dsa

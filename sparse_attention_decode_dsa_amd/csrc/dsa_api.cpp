@@ -1,0 +1,171 @@
+// C ABI of libdsa.so: host-side validation, then the launchers.
+//
+// Every check here runs before any HIP call, so a rejected call touches
+// neither the device nor the stream.  Rules follow include/dsa.h.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int32_t kMaxRows = 65535;   // one workgroup row per query row in the grid's y dimension
+
+bool is_pow2_in(int32_t v, int32_t lo, int32_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+int log2i(int32_t v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+int check_page_geometry(int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size) {
+    if (batch < 1 || num_pages < 1 || max_pages < 1) return DSA_ERR_SHAPE;
+    if (page_size < 1) return DSA_ERR_SHAPE;
+    if (!is_pow2_in(page_size, 16, 1024)) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)max_pages * page_size > INT32_MAX) return DSA_ERR_SHAPE;
+    if ((int64_t)num_pages * page_size > INT32_MAX) return DSA_ERR_SHAPE;
+    return DSA_OK;
+}
+
+size_t topk_ws_keys(int32_t n_rows, int32_t top_k, int32_t n_splits) {
+    return (size_t)n_rows * n_splits * top_k * sizeof(uint32_t);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(int status) {
+    switch (status) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+        case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size, stride or count is out of range";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: head count, head dim or page size not built";
+        case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+        case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH: the HIP runtime refused a launch";
+        default: return "unknown";
+    }
+}
+
+int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
+                   uint8_t* q_code, float* q_scale, hipStream_t stream) {
+    if (n_rows < 0 || n_heads < 1 || head_dim < 1) return DSA_ERR_SHAPE;
+    if (head_dim != 128) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)n_rows * n_heads > INT32_MAX / 4) return DSA_ERR_SHAPE;
+    if (n_rows == 0) return DSA_OK;
+    if (!q_bf16 || !q_code || !q_scale) return DSA_ERR_NULL;
+    return launch_status(dsa::launch_quantize_q(q_bf16, n_rows * n_heads, q_code, q_scale, stream));
+}
+
+int dsa_index_scores(const uint8_t* q_code, const float* q_scale, const float* head_w,
+                     const uint8_t* k_code, const float* k_scale, const int32_t* page_table,
+                     const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,
+                     int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
+                     int32_t page_size, int32_t n_heads, int32_t head_dim, int32_t group_rows,
+                     float* scores, int32_t score_stride, int32_t* status, hipStream_t stream) {
+    if (n_rows < 0 || n_rows > kMaxRows || score_stride < 1) return DSA_ERR_SHAPE;
+    if (n_heads < 1 || head_dim < 1) return DSA_ERR_SHAPE;
+    if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
+    int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
+    if (rc != DSA_OK) return rc;
+    if (group_rows < 1 || group_rows > 8) return DSA_ERR_SHAPE;
+    if (n_rows % group_rows != 0) return DSA_ERR_SHAPE;
+    if (!q_code || !q_scale || !head_w || !k_code || !k_scale || !page_table || !kv_lens ||
+        !row_req || !row_vis || !scores || !status)
+        return DSA_ERR_NULL;
+    if (n_rows == 0) return DSA_OK;
+    dsa::IndexArgs a;
+    a.q_code = q_code; a.q_scale = q_scale; a.head_w = head_w;
+    a.k_code = k_code; a.k_scale = k_scale; a.page_table = page_table; a.kv_lens = kv_lens;
+    a.row_req = row_req; a.row_vis = row_vis;
+    a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
+    a.page_size = page_size; a.log2_page = log2i(page_size); a.group_rows = group_rows;
+    a.scores = scores; a.score_stride = score_stride; a.status = status;
+    return launch_status(dsa::launch_index_scores(a, stream));
+}
+
+size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits) {
+    if (n_rows <= 0 || top_k <= 0 || n_splits <= 1) return 0;
+    return 2 * topk_ws_keys(n_rows, top_k, n_splits) + (size_t)n_rows * n_splits * sizeof(int32_t);
+}
+
+int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
+             int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes,
+             int32_t* topk_idx, int32_t* topk_count, int32_t* status, hipStream_t stream) {
+    if (n_rows < 0 || n_rows > kMaxRows || score_stride < 1) return DSA_ERR_SHAPE;
+    if (top_k < 1 || top_k > dsa::kTopkMaxK) return DSA_ERR_SHAPE;
+    if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
+    if (((int64_t)score_stride + n_splits - 1) / n_splits > dsa::kTopkMaxList) return DSA_ERR_SHAPE;
+    if (n_splits > 1 && (int64_t)n_splits * top_k > dsa::kTopkMaxList) return DSA_ERR_SHAPE;
+    if (!scores || !row_vis || !topk_idx || !topk_count || !status) return DSA_ERR_NULL;
+    if (n_rows == 0) return DSA_OK;
+    dsa::TopkArgs a;
+    a.scores = scores; a.score_stride = score_stride; a.row_vis = row_vis;
+    a.n_rows = n_rows; a.top_k = top_k; a.n_splits = n_splits;
+    a.cand_key = nullptr; a.cand_slot = nullptr; a.cand_count = nullptr;
+    if (n_splits > 1) {
+        const size_t need = dsa_topk_workspace_size(n_rows, top_k, n_splits);
+        if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+        char* ws = static_cast<char*>(workspace);
+        const size_t kb = topk_ws_keys(n_rows, top_k, n_splits);
+        a.cand_key = reinterpret_cast<uint32_t*>(ws);
+        a.cand_slot = reinterpret_cast<int32_t*>(ws + kb);
+        a.cand_count = reinterpret_cast<int32_t*>(ws + 2 * kb);
+    }
+    a.topk_idx = topk_idx; a.topk_count = topk_count; a.status = status;
+    return launch_status(dsa::launch_topk(a, stream));
+}
+
+int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_code, const float* kv_scale,
+                          const int32_t* page_table, const int32_t* row_req, const int32_t* row_vis,
+                          const int32_t* topk_idx, const int32_t* topk_count, int32_t n_rows,
+                          int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
+                          int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
+                          float* part_o, float* part_lse, uint16_t* out, float* out_lse,
+                          int32_t* status, hipStream_t stream) {
+    if (n_rows < 0 || n_rows > kMaxRows || n_heads < 1) return DSA_ERR_SHAPE;
+    if (top_k < 1 || top_k > dsa::kTopkMaxK) return DSA_ERR_SHAPE;
+    if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
+    if (!isfinite(sm_scale)) return DSA_ERR_SHAPE;
+    if (n_heads != 16 && n_heads != 32) return DSA_ERR_UNSUPPORTED;
+    int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
+    if (rc != DSA_OK) return rc;
+    if (!q || !kv_code || !kv_scale || !page_table || !row_req || !row_vis || !topk_idx ||
+        !topk_count || !status)
+        return DSA_ERR_NULL;
+    if (n_splits == 1 ? !out : (!part_o || !part_lse)) return DSA_ERR_NULL;
+    if (n_rows == 0) return DSA_OK;
+    dsa::MlaArgs a;
+    a.q = q; a.kv_code = kv_code; a.kv_scale = kv_scale; a.page_table = page_table;
+    a.row_req = row_req; a.row_vis = row_vis; a.topk_idx = topk_idx; a.topk_count = topk_count;
+    a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
+    a.page_size = page_size; a.log2_page = log2i(page_size); a.n_heads = n_heads;
+    a.top_k = top_k; a.n_splits = n_splits; a.sm_scale = sm_scale;
+    a.part_o = part_o; a.part_lse = part_lse; a.out = out; a.out_lse = out_lse; a.status = status;
+    return launch_status(dsa::launch_sparse_mla(a, stream));
+}
+
+int dsa_lse_merge(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
+                  int32_t n_splits, int32_t d_v, uint16_t* out, float* out_lse, hipStream_t stream) {
+    if (n_rows < 0 || n_heads < 1 || d_v < 1) return DSA_ERR_SHAPE;
+    if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
+    if ((int64_t)n_rows * n_heads > INT32_MAX / 256) return DSA_ERR_SHAPE;
+    if (d_v != 512) return DSA_ERR_UNSUPPORTED;
+    if (!part_o || !part_lse || !out) return DSA_ERR_NULL;
+    if (n_rows == 0) return DSA_OK;
+    dsa::MergeArgs a;
+    a.part_o = part_o; a.part_lse = part_lse; a.n_rows = n_rows; a.n_heads = n_heads;
+    a.n_splits = n_splits; a.out = out; a.out_lse = out_lse;
+    return launch_status(dsa::launch_lse_merge(a, stream));
+}
+
+}  // extern "C"

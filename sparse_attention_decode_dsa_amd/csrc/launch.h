@@ -1,0 +1,78 @@
+// Internal launchers: the C ABI in dsa_api.cpp validates its arguments and
+// then calls these, which only compute grid shapes and enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct IndexArgs {
+    const uint8_t* q_code;
+    const float* q_scale;
+    const float* head_w;
+    const uint8_t* k_code;
+    const float* k_scale;
+    const int32_t* page_table;
+    const int32_t* kv_lens;
+    const int32_t* row_req;
+    const int32_t* row_vis;
+    int32_t n_rows, batch, num_pages, max_pages, page_size, log2_page, group_rows;
+    float* scores;
+    int32_t score_stride;
+    int32_t* status;
+};
+
+struct TopkArgs {
+    const float* scores;
+    int32_t score_stride;
+    const int32_t* row_vis;
+    int32_t n_rows, top_k, n_splits;
+    uint32_t* cand_key;   // [n_rows, n_splits, top_k]
+    int32_t* cand_slot;   // [n_rows, n_splits, top_k]
+    int32_t* cand_count;  // [n_rows, n_splits]
+    int32_t* topk_idx;
+    int32_t* topk_count;
+    int32_t* status;
+};
+
+struct MlaArgs {
+    const uint16_t* q;
+    const uint8_t* kv_code;
+    const float* kv_scale;
+    const int32_t* page_table;
+    const int32_t* row_req;
+    const int32_t* row_vis;
+    const int32_t* topk_idx;
+    const int32_t* topk_count;
+    int32_t n_rows, batch, num_pages, max_pages, page_size, log2_page, n_heads, top_k, n_splits;
+    float sm_scale;
+    float* part_o;
+    float* part_lse;
+    uint16_t* out;
+    float* out_lse;
+    int32_t* status;
+};
+
+struct MergeArgs {
+    const float* part_o;
+    const float* part_lse;
+    int32_t n_rows, n_heads, n_splits;
+    uint16_t* out;
+    float* out_lse;
+};
+
+// Largest list one top-k workgroup selects from (its keys live in LDS).
+constexpr int kTopkMaxList = 32768;
+constexpr int kTopkMaxK = 8192;
+constexpr int kMaxSplits = 64;
+
+hipError_t launch_quantize_q(const uint16_t* q, int32_t n_pairs, uint8_t* code, float* scale,
+                             hipStream_t stream);
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,281 @@
+"""Thin Python binding of libdsa.so (include/dsa.h), same names as the C ABI.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  Tensors must be contiguous CUDA (HIP) tensors of
+the documented dtypes; outputs are allocated with torch when not given.  A
+nonzero host status raises DsaError; device-detected faults accumulate in an
+int32 status tensor that ``check_status`` turns into DsaError.
+
+There is no fallback: if libdsa.so is missing or was built for another ABI,
+loading fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+ABI_VERSION = 1
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN"}
+
+
+class DsaError(RuntimeError):
+    """A libdsa.so call was rejected, or a kernel reported a device fault."""
+
+
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+_f32 = ctypes.c_float
+_SIGS = {
+    "dsa_abi_version": ([], ctypes.c_int),
+    "dsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "dsa_quantize_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
+    "dsa_index_scores": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                          _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
+    "dsa_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
+    "dsa_topk": ([_p, _i32, _p, _i32, _i32, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p], ctypes.c_int),
+    "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
+    "dsa_lse_merge": ([_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa.so once and check its ABI version."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise DsaError(f"{_LIB_PATH} is not built; run `python -m sparse_attention_decode_dsa_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        v = L.dsa_abi_version()
+        if v != ABI_VERSION:
+            raise DsaError(f"libdsa.so ABI version {v}, binding expects {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().dsa_status_string(code).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise DsaError(f"{what}: {status_string(rc)} ({rc})")
+
+
+def _ptr(t: torch.Tensor | None, dtype=None, name="tensor") -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise DsaError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise DsaError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise DsaError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def new_status(device=None) -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=device or "cuda")
+
+
+def check_status(status: torch.Tensor):
+    """Raise DsaError if any kernel ORed a fault bit into ``status`` (syncs)."""
+    v = int(status.item())
+    if v:
+        names = [n for b, n in DEV_BITS.items() if v & b]
+        raise DsaError(f"device status {v:#x}: {', '.join(names)}")
+
+
+def quantize_q(q_bf16, q_code=None, q_scale=None, stream=None):
+    """bf16 [R, H, 128] -> (fp8 codes uint8 [R, H, 128], scales f32 [R, H])."""
+    r, h, d = q_bf16.shape
+    if q_code is None:
+        q_code = torch.empty((r, h, d), dtype=torch.uint8, device=q_bf16.device)
+    if q_scale is None:
+        q_scale = torch.empty((r, h), dtype=torch.float32, device=q_bf16.device)
+    _check(lib().dsa_quantize_q(_ptr(q_bf16, _BF16, "q_bf16"), r, h, d, _ptr(q_code, _FP8, "q_code"),
+                                _ptr(q_scale, torch.float32, "q_scale"), _stream(stream)),
+           "dsa_quantize_q")
+    return q_code, q_scale
+
+
+def index_scores(q_code, q_scale, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis,
+                 group_rows: int = 1, score_stride: int | None = None, scores=None, status=None,
+                 stream=None):
+    """fp8 indexer scores [R, score_stride] f32 (-inf past each row's span)."""
+    r, h, d = q_code.shape
+    n_pages, p, dk = k_code.shape
+    batch, max_pages = page_table.shape
+    if score_stride is None:
+        score_stride = scores.shape[1] if scores is not None else max_pages * p
+    if scores is None:
+        scores = torch.empty((r, score_stride), dtype=torch.float32, device=q_code.device)
+    if status is None:
+        status = new_status(q_code.device)
+    _check(lib().dsa_index_scores(
+        _ptr(q_code, _FP8, "q_code"), _ptr(q_scale, torch.float32, "q_scale"),
+        _ptr(head_w, torch.float32, "head_w"), _ptr(k_code, _FP8, "k_code"),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(page_table, torch.int32, "page_table"),
+        _ptr(kv_lens, torch.int32, "kv_lens"), _ptr(row_req, torch.int32, "row_req"),
+        _ptr(row_vis, torch.int32, "row_vis"), r, batch, n_pages, max_pages, p, h, d, group_rows,
+        _ptr(scores, torch.float32, "scores"), score_stride, _ptr(status, torch.int32, "status"),
+        _stream(stream)), "dsa_index_scores")
+    return scores, status
+
+
+def topk_workspace_size(n_rows: int, top_k: int, n_splits: int) -> int:
+    return int(lib().dsa_topk_workspace_size(n_rows, top_k, n_splits))
+
+
+def topk(scores, row_vis, top_k: int, n_splits: int = 1, workspace=None, topk_idx=None,
+         topk_count=None, status=None, stream=None):
+    """Exact top-k per row -> (topk_idx i32 [R, k] ascending then -1, topk_count i32 [R])."""
+    r, stride = scores.shape
+    dev = scores.device
+    if topk_idx is None:
+        topk_idx = torch.empty((r, top_k), dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty((r,), dtype=torch.int32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    need = topk_workspace_size(r, top_k, n_splits)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace, None, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dsa_topk(_ptr(scores, torch.float32, "scores"), stride,
+                          _ptr(row_vis, torch.int32, "row_vis"), r, top_k, n_splits, ws_ptr, ws_bytes,
+                          _ptr(topk_idx, torch.int32, "topk_idx"),
+                          _ptr(topk_count, torch.int32, "topk_count"),
+                          _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_topk")
+    return topk_idx, topk_count, status
+
+
+def sparse_mla_decode(q, kv_code, kv_scale, page_table, row_req, row_vis, topk_idx, topk_count,
+                      n_splits: int = 1, sm_scale: float = 1.0 / 24.0, part_o=None, part_lse=None,
+                      out=None, out_lse=None, status=None, stream=None):
+    """Split-K sparse MLA.  n_splits == 1 -> (out bf16 [R,H,512], out_lse f32 [R,H]);
+    otherwise -> (part_o f32 [R,H,S,512], part_lse f32 [R,H,S])."""
+    r, h, dq = q.shape
+    n_pages, p, _ = kv_code.shape
+    batch, max_pages = page_table.shape
+    top_k = topk_idx.shape[1]
+    dev = q.device
+    if status is None:
+        status = new_status(dev)
+    if n_splits == 1:
+        if out is None:
+            out = torch.empty((r, h, 512), dtype=torch.bfloat16, device=dev)
+        if out_lse is None:
+            out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
+    else:
+        if part_o is None:
+            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
+    _check(lib().dsa_sparse_mla_decode(
+        _ptr(q, _BF16, "q"), _ptr(kv_code, _FP8, "kv_code"), _ptr(kv_scale, torch.float32, "kv_scale"),
+        _ptr(page_table, torch.int32, "page_table"), _ptr(row_req, torch.int32, "row_req"),
+        _ptr(row_vis, torch.int32, "row_vis"), _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_count, torch.int32, "topk_count"), r, batch, n_pages, max_pages, p, h, top_k,
+        n_splits, float(sm_scale),
+        _ptr(part_o, torch.float32, "part_o") if n_splits > 1 else None,
+        _ptr(part_lse, torch.float32, "part_lse") if n_splits > 1 else None,
+        _ptr(out, _BF16, "out") if n_splits == 1 else None,
+        _ptr(out_lse, torch.float32, "out_lse") if n_splits == 1 else None,
+        _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_sparse_mla_decode")
+    if n_splits == 1:
+        return out, out_lse, status
+    return part_o, part_lse, status
+
+
+def lse_merge(part_o, part_lse, out=None, out_lse=None, stream=None):
+    """Merge split partials -> (out bf16 [R,H,512], out_lse f32 [R,H])."""
+    r, h, s, dv = part_o.shape
+    dev = part_o.device
+    if out is None:
+        out = torch.empty((r, h, dv), dtype=torch.bfloat16, device=dev)
+    if out_lse is None:
+        out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
+    _check(lib().dsa_lse_merge(_ptr(part_o, torch.float32, "part_o"),
+                               _ptr(part_lse, torch.float32, "part_lse"), r, h, s, dv,
+                               _ptr(out, _BF16, "out"), _ptr(out_lse, torch.float32, "out_lse"),
+                               _stream(stream)), "dsa_lse_merge")
+    return out, out_lse
+
+
+class DecodeStep:
+    """All buffers of one DSA decode step for fixed inputs, allocated once;
+    ``run()`` enqueues quantize -> scores -> top-k -> sparse MLA -> merge on
+    the current stream without allocating or synchronising."""
+
+    def __init__(self, inp, index_splits: int | None = None, attn_splits: int | None = None,
+                 group_rows: int | None = None, score_stride: int | None = None):
+        self.inp = inp
+        cfg = inp.cfg
+        self.index_splits = index_splits or cfg.index_splits
+        self.attn_splits = attn_splits or cfg.attn_splits
+        self.group_rows = group_rows or cfg.group_rows
+        dev = inp.q_idx.device
+        r = inp.n_rows
+        h = inp.mla_heads
+        k = inp.top_k
+        self.score_stride = score_stride or max(1, inp.max_vis())
+        self.q_code = torch.empty((r, 64, 128), dtype=torch.uint8, device=dev)
+        self.q_scale = torch.empty((r, 64), dtype=torch.float32, device=dev)
+        self.scores = torch.empty((r, self.score_stride), dtype=torch.float32, device=dev)
+        need = topk_workspace_size(r, k, self.index_splits)
+        self.workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        self.topk_idx = torch.empty((r, k), dtype=torch.int32, device=dev)
+        self.topk_count = torch.empty((r,), dtype=torch.int32, device=dev)
+        s = self.attn_splits
+        self.part_o = torch.empty((r, h, s, 512), dtype=torch.float32, device=dev) if s > 1 else None
+        self.part_lse = torch.empty((r, h, s), dtype=torch.float32, device=dev) if s > 1 else None
+        self.out = torch.empty((r, h, 512), dtype=torch.bfloat16, device=dev)
+        self.out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
+        self.status = new_status(dev)
+
+    def run(self, stream=None):
+        i = self.inp
+        quantize_q(i.q_idx, self.q_code, self.q_scale, stream=stream)
+        index_scores(self.q_code, self.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table,
+                     i.kv_lens, i.row_req, i.row_vis, group_rows=self.group_rows,
+                     score_stride=self.score_stride, scores=self.scores, status=self.status,
+                     stream=stream)
+        topk(self.scores, i.row_vis, i.top_k, self.index_splits, workspace=self.workspace,
+             topk_idx=self.topk_idx, topk_count=self.topk_count, status=self.status, stream=stream)
+        if self.attn_splits == 1:
+            sparse_mla_decode(i.q_mla, i.kv_code, i.kv_scale, i.page_table, i.row_req, i.row_vis,
+                              self.topk_idx, self.topk_count, 1, i.sm_scale, out=self.out,
+                              out_lse=self.out_lse, status=self.status, stream=stream)
+        else:
+            sparse_mla_decode(i.q_mla, i.kv_code, i.kv_scale, i.page_table, i.row_req, i.row_vis,
+                              self.topk_idx, self.topk_count, self.attn_splits, i.sm_scale,
+                              part_o=self.part_o, part_lse=self.part_lse, status=self.status,
+                              stream=stream)
+            lse_merge(self.part_o, self.part_lse, out=self.out, out_lse=self.out_lse, stream=stream)
+        return self.out, self.out_lse

@@ -1,0 +1,130 @@
+"""CPU checks of the C ABI: libdsa.so loads, exports every function that
+include/dsa.h declares, and rejects invalid arguments with the documented
+status before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_decode_dsa_amd import dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, NULL, SHAPE, UNSUP, WS = 0, -1, -2, -3, -4
+P = 0x1000  # a non-NULL dummy device pointer; never dereferenced on these paths
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(dsa_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dsa.lib_path()):
+        pytest.fail("libdsa.so is not built; run __graft_entry__.build()")
+    return dsa.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_index_scores",
+            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_merge"} <= set(names)
+    raw = ctypes.CDLL(dsa.lib_path())
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(dsa._SIGS), "binding and header disagree"
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.dsa_abi_version() == dsa.ABI_VERSION == 1
+    for code in (OK, NULL, SHAPE, UNSUP, WS, -5):
+        assert dsa.status_string(code).startswith("DSA_")
+    assert dsa.status_string(12345) == "unknown"
+
+
+def _idx(L, **kw):
+    a = dict(q_code=P, q_scale=P, head_w=P, k_code=P, k_scale=P, page_table=P, kv_lens=P,
+             row_req=P, row_vis=P, n_rows=4, batch=2, num_pages=10, max_pages=5, page_size=256,
+             n_heads=64, head_dim=128, group_rows=1, scores=P, score_stride=1280, status=P,
+             stream=None)
+    a.update(kw)
+    return L.dsa_index_scores(*a.values())
+
+
+def test_index_scores_validation(L):
+    assert _idx(L, n_heads=32) == UNSUP
+    assert _idx(L, head_dim=64) == UNSUP
+    assert _idx(L, page_size=100) == UNSUP
+    assert _idx(L, page_size=8) == UNSUP
+    assert _idx(L, page_size=0) == SHAPE
+    assert _idx(L, n_rows=-1) == SHAPE
+    assert _idx(L, batch=0) == SHAPE
+    assert _idx(L, group_rows=3) == SHAPE      # 4 rows not divisible by 3
+    assert _idx(L, group_rows=9, n_rows=9) == SHAPE
+    assert _idx(L, score_stride=0) == SHAPE
+    assert _idx(L, q_code=None) == NULL
+    assert _idx(L, status=None) == NULL
+    assert _idx(L, n_rows=0) == OK             # nothing to enqueue
+
+
+def _tk(L, **kw):
+    a = dict(scores=P, score_stride=32768, row_vis=P, n_rows=4, top_k=2048, n_splits=1,
+             workspace=None, workspace_bytes=0, topk_idx=P, topk_count=P, status=P, stream=None)
+    a.update(kw)
+    return L.dsa_topk(*a.values())
+
+
+def test_topk_validation_and_workspace(L):
+    assert L.dsa_topk_workspace_size(4, 2048, 1) == 0
+    need = L.dsa_topk_workspace_size(4, 2048, 16)
+    assert need == 4 * 16 * 2048 * 8 + 4 * 16 * 4
+    assert _tk(L, top_k=0) == SHAPE
+    assert _tk(L, top_k=8193) == SHAPE
+    assert _tk(L, score_stride=32769) == SHAPE                   # one split longer than 32768
+    assert _tk(L, n_splits=65) == SHAPE
+    assert _tk(L, n_splits=17, score_stride=131072) == SHAPE    # 17 * 2048 candidates > 32768
+    assert _tk(L, n_splits=16, score_stride=131072) == WS       # no workspace
+    assert _tk(L, n_splits=16, score_stride=131072, workspace=P, workspace_bytes=need - 1) == WS
+    assert _tk(L, scores=None) == NULL
+    assert _tk(L, n_rows=0) == OK
+
+
+def _mla(L, **kw):
+    a = dict(q=P, kv_code=P, kv_scale=P, page_table=P, row_req=P, row_vis=P, topk_idx=P,
+             topk_count=P, n_rows=4, batch=4, num_pages=100, max_pages=20, page_size=256,
+             n_heads=32, top_k=2048, n_splits=4, sm_scale=0.04, part_o=P, part_lse=P, out=None,
+             out_lse=None, status=P, stream=None)
+    a.update(kw)
+    return L.dsa_sparse_mla_decode(*a.values())
+
+
+def test_sparse_mla_validation(L):
+    assert _mla(L, n_heads=128) == UNSUP
+    assert _mla(L, n_heads=0) == SHAPE
+    assert _mla(L, n_splits=0) == SHAPE
+    assert _mla(L, n_splits=65) == SHAPE
+    assert _mla(L, sm_scale=float("nan")) == SHAPE
+    assert _mla(L, sm_scale=float("inf")) == SHAPE
+    assert _mla(L, part_o=None) == NULL                      # split path needs partials
+    assert _mla(L, n_splits=1, out=None) == NULL             # lone split needs out
+    assert _mla(L, page_size=48) == UNSUP
+    assert _mla(L, n_rows=0) == OK
+
+
+def test_lse_merge_and_quantize_validation(L):
+    m = L.dsa_lse_merge
+    assert m(P, P, 4, 32, 4, 256, P, None, None) == UNSUP
+    assert m(P, P, 4, 32, 0, 512, P, None, None) == SHAPE
+    assert m(P, P, 4, 32, 65, 512, P, None, None) == SHAPE
+    assert m(None, P, 4, 32, 4, 512, P, None, None) == NULL
+    assert m(P, P, 4, 32, 4, 512, None, None, None) == NULL
+    assert m(P, P, 0, 32, 4, 512, P, None, None) == OK
+    q = L.dsa_quantize_q
+    assert q(P, 4, 64, 64, P, P, None) == UNSUP
+    assert q(P, -1, 64, 128, P, P, None) == SHAPE
+    assert q(None, 4, 64, 128, P, P, None) == NULL
+    assert q(P, 0, 64, 128, P, P, None) == OK

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs are seeded and synthetic (sparse_attention_decode_dsa_amd.workload);
+the oracle never sees anything the GPU computed.  Rules and tolerances are in
+tests/parity_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+from parity_util import (bf16_to_f64, check_out, check_scores, check_topk_row)
+from sparse_attention_decode_dsa_amd import dsa
+from sparse_attention_decode_dsa_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_step(inp, index_splits=None, attn_splits=None, group_rows=None, score_stride=None):
+    step = dsa.DecodeStep(inp, index_splits, attn_splits, group_rows, score_stride)
+    step.run()
+    torch.cuda.synchronize()
+    dsa.check_status(step.status)
+    return step
+
+
+def compare_step(inp, step, rows, max_swap_rows=None):
+    """Oracle on `rows` of `inp` vs the GPU step; returns rows with tie swaps."""
+    rows = list(rows)
+    sub = W.subset(inp, rows)
+    ref = O.decode_step(W.as_numpy(sub), step.index_splits, step.attn_splits)
+    np.testing.assert_array_equal(step.q_code[rows].cpu().numpy(), ref["q_code"])
+    np.testing.assert_array_equal(step.q_scale[rows].cpu().double().numpy(), ref["q_scale"])
+    vis = sub.row_vis.numpy()
+    g_scores = step.scores[rows].cpu().double().numpy()
+    r_scores = np.full_like(g_scores, -np.inf)
+    r_scores[:, :ref["scores"].shape[1]] = ref["scores"]
+    check_scores(g_scores, r_scores, vis)
+    g_idx = step.topk_idx[rows].cpu().numpy()
+    g_cnt = step.topk_count[rows].cpu().numpy()
+    g_out = bf16_to_f64(step.out[rows])
+    g_lse = step.out_lse[rows].cpu().double().numpy()
+    swapped = []
+    for i in range(len(rows)):
+        sw = check_topk_row(g_idx[i], g_cnt[i], ref["topk_idx"][i], ref["topk_count"][i],
+                            ref["scores"][i], vis[i], inp.top_k)
+        if sw:
+            swapped.append(rows[i])
+            continue
+        check_out(g_out[i], g_lse[i], ref["out"][i], ref["lse"][i])
+    if max_swap_rows is not None:
+        assert len(swapped) <= max_swap_rows, swapped
+    return ref, sub, swapped
+
+
+def mla_on_oracle_selection(sub, ref, n_splits):
+    """The GPU attention kernels fed the oracle's own top-k, vs the oracle."""
+    g = W.to(sub, "cuda")
+    idx = torch.from_numpy(ref["topk_idx"].astype(np.int32)).cuda()
+    cnt = torch.from_numpy(ref["topk_count"].astype(np.int32)).cuda()
+    st = dsa.new_status()
+    if n_splits == 1:
+        out, lse, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_code, g.kv_scale, g.page_table, g.row_req,
+                                            g.row_vis, idx, cnt, 1, g.sm_scale, status=st)
+    else:
+        po, pl, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_code, g.kv_scale, g.page_table, g.row_req,
+                                          g.row_vis, idx, cnt, n_splits, g.sm_scale, status=st)
+        out, lse = dsa.lse_merge(po, pl)
+    torch.cuda.synchronize()
+    dsa.check_status(st)
+    return check_out(bf16_to_f64(out), lse.cpu().double().numpy(), ref["out"], ref["lse"])
+
+
+# ------------------------------------------------------------------ quantize
+
+def test_quantize_q_bit_exact():
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(37, 64, 128, generator=g) * torch.exp(torch.randn(37, 64, 1, generator=g) * 4)
+    q[0, 0] = 0.0                      # all-zero head
+    q[0, 1] = 0.0
+    q[0, 1, 3] = 448.0                 # amax exactly 448
+    q[0, 2] = -0.0                     # negative zeros
+    q[1, 5] *= 1e-30                   # tiny head
+    q[2, 7] *= 1e30                    # huge head
+    qb = q.to(torch.bfloat16)
+    codes, scale = dsa.quantize_q(qb.cuda())
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_q(qb.view(torch.int16).numpy().view(np.uint16))
+    np.testing.assert_array_equal(scale.cpu().double().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+# ------------------------------------------------------------------ top-k alone
+
+def _synthetic_scores(rng, r, stride, vis, tie_frac=0.3):
+    s = rng.normal(size=(r, stride)).astype(np.float32)
+    ties = rng.random((r, stride)) < tie_frac
+    s[ties] = rng.choice(np.array([-0.5, 0.0, 0.75, 1.5, 2.25], dtype=np.float32), size=ties.sum())
+    for i, v in enumerate(vis):
+        s[i, v:] = -np.inf
+    return s
+
+
+@pytest.mark.parametrize("k,n_splits", [(2048, 1), (2048, 4), (2048, 16), (7, 3), (1, 1), (100, 64)])
+def test_topk_bit_exact_on_synthetic_scores(k, n_splits):
+    rng = np.random.default_rng(1000 + k + n_splits)
+    stride = 32768 if n_splits == 1 else 40000
+    vis = [0, 1, k - 1 if k > 1 else 1, k, k + 1, 5000, stride // 2 + 3, stride]
+    vis = [min(v, stride) for v in vis]
+    s = _synthetic_scores(rng, len(vis), stride, vis)
+    say(f"topk k={k} splits={n_splits} vis={vis}")
+    idx, cnt, st = dsa.topk(torch.from_numpy(s).cuda(), torch.tensor(vis, dtype=torch.int32).cuda(),
+                            k, n_splits)
+    torch.cuda.synchronize()
+    dsa.check_status(st)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for i, v in enumerate(vis):
+        ri, rc = O.topk_split_merge(s[i].astype(np.float64), v, k, n_splits)
+        gi, gc = O.topk_global(s[i].astype(np.float64), v, k)
+        np.testing.assert_array_equal(ri, gi)   # the oracle's own split/merge invariant
+        assert cnt[i] == rc, (i, v)
+        np.testing.assert_array_equal(idx[i], ri)
+
+
+def test_topk_all_equal_scores_keep_lowest_slots():
+    s = np.zeros((2, 9000), dtype=np.float32)
+    vis = [9000, 4097]
+    for n_splits in (1, 3):
+        idx, cnt, st = dsa.topk(torch.from_numpy(s).cuda(), torch.tensor(vis, dtype=torch.int32).cuda(),
+                                2048, n_splits)
+        torch.cuda.synchronize()
+        dsa.check_status(st)
+        assert cnt.cpu().tolist() == [2048, 2048]
+        np.testing.assert_array_equal(idx.cpu().numpy(), np.tile(np.arange(2048), (2, 1)))
+
+
+# ------------------------------------------------------------------ LSE merge alone
+
+def test_lse_merge_synthetic():
+    rng = np.random.default_rng(7)
+    r, h, s = 5, 32, 7
+    po = rng.normal(size=(r, h, s, 512)).astype(np.float32)
+    pl = (rng.normal(size=(r, h, s)) * 5).astype(np.float32)
+    pl[0, :, 2] = -np.inf                 # an empty split
+    pl[1, 3, :] = -np.inf                 # an empty row
+    po[0, :, 2] = 0.0
+    po[1, 3, :] = 0.0
+    out, lse = dsa.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    ro, rl = O.lse_merge(po.astype(np.float64), pl.astype(np.float64))
+    check_out(bf16_to_f64(out), lse.cpu().double().numpy(), ro, rl)
+    assert np.all(out[1, 3].float().cpu().numpy() == 0) and np.isneginf(lse[1, 3].item())
+
+
+# ------------------------------------------------------------------ whole step, C0
+
+@pytest.mark.parametrize("splits", [(4, 4), (1, 1), (2, 3)])
+def test_c0_step_matches_oracle(splits):
+    inp = W.to(W.make("c0"), "cuda")
+    say(f"c0 step splits={splits}")
+    step = run_step(inp, *splits)
+    ref, sub, swapped = compare_step(inp, step, range(inp.n_rows), max_swap_rows=1)
+    # request 0 is shorter than top-k: every slot selected, attention is dense
+    assert step.topk_count[0].item() == 1500
+    np.testing.assert_array_equal(step.topk_idx[0, :1500].cpu().numpy(), np.arange(1500))
+
+
+@pytest.mark.parametrize("n_splits", [1, 4, 64])
+def test_c0_attention_on_oracle_selection(n_splits):
+    inp = W.make("c0")
+    ref = O.decode_step(W.as_numpy(inp), 4, n_splits)
+    say(f"c0 mla splits={n_splits}")
+    mla_on_oracle_selection(inp, ref, n_splits)
+
+
+# ------------------------------------------------------------------ bulk decode, sampled rows
+
+@pytest.mark.parametrize("name", ["c1", "c1_l32k"])
+def test_bulk_decode_sampled_rows(name):
+    inp = W.make(name, device="cuda")
+    say(f"{name}: B={inp.n_rows} pages={inp.n_pages} splits=({inp.cfg.index_splits},{inp.cfg.attn_splits})")
+    step = run_step(inp)
+    vis = inp.row_vis.cpu().numpy()
+    rows = sorted({int(np.argmin(vis)), int(np.argmax(vis)), 0, 17, 63})
+    ref, sub, swapped = compare_step(inp, step, rows, max_swap_rows=2)
+    say(f"{name}: rows {rows} swapped {swapped}")
+    mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
+
+
+# ------------------------------------------------------------------ properties
+
+def test_page_permutation_and_run_to_run_determinism():
+    inp = W.to(W.make("c0"), "cuda")
+    a = run_step(inp)
+    out_a = a.out.clone()
+    b = run_step(inp)
+    assert torch.equal(out_a, b.out) and torch.equal(a.topk_idx, b.topk_idx)
+    # permute the physical pages and remap the block table
+    n = inp.n_pages
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(3)).cuda()
+    inv = torch.argsort(perm)
+    pt = inp.page_table.long()
+    new_pt = torch.where(pt >= 0, perm[pt.clamp(min=0)], pt).to(torch.int32)
+    from dataclasses import replace
+    p = replace(inp, k_code=inp.k_code[inv], k_scale=inp.k_scale[inv], kv_code=inp.kv_code[inv],
+                kv_scale=inp.kv_scale[inv], page_table=new_pt.contiguous())
+    c = run_step(p)
+    assert torch.equal(out_a, c.out) and torch.equal(a.topk_idx, c.topk_idx)
+    assert torch.equal(a.scores, c.scores)
+
+
+def test_bad_page_id_is_reported_not_read():
+    inp = W.to(W.make("c0"), "cuda")
+    pt = inp.page_table.clone()
+    pt[1, 10] = inp.n_pages + 5           # inside request 1's span
+    from dataclasses import replace
+    bad = replace(inp, page_table=pt)
+    step = dsa.DecodeStep(bad)
+    step.run()
+    torch.cuda.synchronize()
+    with pytest.raises(dsa.DsaError, match="PAGE_OOB"):
+        dsa.check_status(step.status)
