@@ -38,6 +38,8 @@ def flags() -> list[str]:
         "-Wall", "-Wextra", "-Werror",
         # Keep the compiler from forming packed fp32 instructions.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: no AGPR copies around accumulator updates.
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", INCLUDE,
     ]
 

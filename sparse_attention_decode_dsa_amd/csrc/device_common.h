@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 
 namespace dsa {
 
@@ -78,26 +78,50 @@ __device__ __forceinline__ float wave_sum(float v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     return v;
 }
-// Reductions over the 16 lanes that share l / 16.
+// Lane exchange inside rows of 16 lanes by DPP (a VALU operand modifier,
+// no LDS round trip).  0xB1 / 0x4E: quad_perm [1,0,3,2] / [2,3,0,1];
+// 0x141: mirror within each half row; 0x140: mirror within the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// All-reductions over the 16 lanes that share l / 16: after the two quad
+// steps every lane holds its quad's result, the half-row mirror pairs the
+// two quads of a half row, the row mirror pairs the two half rows.
 __device__ __forceinline__ float row16_max(float v) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
     return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x140>(v);
     return v;
 }
 
-// Inclusive scan of uint32 over a wavefront.
+// Lane i receives lane i - N of its row of 16 (0 below the row start).
+template <int N>
+__device__ __forceinline__ uint32_t row_shr(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x110 + N, 0xF, 0xF, true);
+}
+
+// Inclusive scan of uint32 over a wavefront: four DPP row shifts scan each
+// row of 16 lanes, then the three lower rows' totals are added in.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
     const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
+    v += row_shr<1>(v);
+    v += row_shr<2>(v);
+    v += row_shr<4>(v);
+    v += row_shr<8>(v);
+    const uint32_t t0 = __builtin_amdgcn_readlane(v, 15);
+    const uint32_t t1 = __builtin_amdgcn_readlane(v, 31);
+    const uint32_t t2 = __builtin_amdgcn_readlane(v, 47);
+    v += (lane >= 16 ? t0 : 0u) + (lane >= 32 ? t1 : 0u) + (lane >= 48 ? t2 : 0u);
     return v;
 }
 
@@ -124,6 +148,13 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     *total = scratch[NW];
     __syncthreads();
     return r;
+}
+
+// Forces a value into registers at this point and hides where it came
+// from, so the compiler cannot re-create it later by reloading memory.
+template <typename T>
+__device__ __forceinline__ void pin(T& v) {
+    asm volatile("" : "+v"(v));
 }
 
 __device__ __forceinline__ void flag(int32_t* status, int32_t bit) {

@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "launch.h"
 
 namespace {

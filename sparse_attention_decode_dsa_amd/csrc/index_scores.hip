@@ -20,6 +20,10 @@
 // group of G rows of one request; wavefronts take 64-token groups in turn.
 // With G > 1 (MTP verify, prefill) the keys of a 64-token group are loaded
 // once and reused for every row of the group, whose queries sit in LDS.
+//
+// Latency hiding: the chunk's page ids are read once into LDS, so key
+// addresses never wait on a block-table load; each wavefront issues the
+// loads of its next 64-token group before computing the current one.
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,11 +34,7 @@ namespace {
 constexpr int kChunk = 2048;    // tokens per workgroup
 constexpr int kQStride = 144;   // LDS bytes per query head row (128 + 16 pad: conflict-free b128 reads)
 
-struct KeyBlock {
-    v8i b;
-    float scale;
-    bool live;
-};
+constexpr int kMaxChunkPages = kChunk / 16;  // pages of one chunk at the smallest page size
 
 __device__ __forceinline__ v8i load_q_operand(const uint8_t* head_row, int g) {
     const uint4 lo = *reinterpret_cast<const uint4*>(head_row + 16 * g);
@@ -45,21 +45,27 @@ __device__ __forceinline__ v8i load_q_operand(const uint8_t* head_row, int g) {
     return r;
 }
 
-// Score of this lane's token column (lane % 16) for one row: 4 MFMAs over
-// the head blocks, ReLU-weighted head sum, then the key scale.
-__device__ __forceinline__ float score_block(const v8i (&qa)[4], const float (&wq)[4][4],
-                                             const KeyBlock& kb) {
+// The keys of one 64-token group in MFMA B layout: block j (tokens
+// 16j..16j+15) in b[j]; lane l holds the scale of token l of the group.
+struct KeyGroup {
+    v8i b[4];
+    float scale;
+};
+
+// Score of this lane's token column (lane % 16) of one 16-token block for
+// one row: 4 MFMAs over the head blocks, ReLU-weighted head sum.
+__device__ __forceinline__ float block_dot(const v8i (&qa)[4], const float (&wq)[4][4], const v8i& kb) {
     float part = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = mfma_fp8_16x16x128(qa[hb], kb.b, acc);
+        acc = mfma_fp8_16x16x128(qa[hb], kb, acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) part += wq[hb][i] * fmaxf(acc[i], 0.0f);
     }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
-    return part * kb.scale;
+    return part;
 }
 
 template <int G>
@@ -74,6 +80,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
 
     __shared__ int s_req[G];
     __shared__ int s_vis[G];
+    __shared__ int s_page[kMaxChunkPages];
     __shared__ __attribute__((aligned(16))) uint8_t s_q[G > 1 ? G * 64 * kQStride : 16];
     __shared__ __attribute__((aligned(16))) float s_wq[G > 1 ? G * 64 : 4];
 
@@ -116,12 +123,31 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     int vmax = 0;
 #pragma unroll
     for (int j = 0; j < G; ++j) vmax = max(vmax, s_vis[j]);
-    const int* pt = a.page_table + (size_t)b * a.max_pages;
     const int pmask = a.page_size - 1;
-
     // Tokens [t0, t_comp) are computed in 64-token groups; the rest of the
     // chunk only needs -inf.
     const int t_comp = min(t_end, t0 + ((max(vmax - t0, 0) + 63) & ~63));
+
+    // Block table of the chunk, once: page ids of the pages [t0, t_comp)
+    // touches (-1 for invalid ones, which are reported).
+    {
+        const int p0 = t0 >> a.log2_page;
+        const int np = t_comp > t0 ? ((t_comp - 1) >> a.log2_page) - p0 + 1 : 0;
+        const int* pt = a.page_table + (size_t)b * a.max_pages;
+        for (int i = threadIdx.x; i < np; i += 256) {
+            int page = -1;
+            if (((p0 + i) << a.log2_page) < vmax) {
+                page = pt[p0 + i];
+                if (page < 0 || page >= a.num_pages) {
+                    flag(a.status, DSA_DEV_PAGE_OOB);
+                    page = -1;
+                }
+            }
+            s_page[i] = page;
+        }
+    }
+    __syncthreads();
+    const int p0 = t0 >> a.log2_page;
 
     v8i qa[4];
     float wq[4][4];
@@ -130,6 +156,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
             qa[hb] = load_q_operand(a.q_code + ((size_t)r * 64 + hb * 16 + n) * 128, g);
+            pin(qa[hb]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const size_t hi = (size_t)r * 64 + hb * 16 + 4 * g + i;
@@ -138,25 +165,36 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
         }
     }
 
-    for (int tg = t0 + wv * 64; tg < t_comp; tg += 256) {
-        KeyBlock kb[4];
+    // Loads of the group starting at token tg, branch-free: a block past
+    // vmax or on an invalid page reads row n of page 0 instead (always
+    // inside the cache) and is masked out of the scores later.  Keeping
+    // every path's loads identical lets the compiler wait for exactly the
+    // group it needs.
+    auto load_group = [&](int tg, KeyGroup& kg) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int tb = tg + 16 * j;
-            kb[j].live = tb < vmax;
-            kb[j].scale = 0.0f;
-            if (kb[j].live) {
-                const int page = pt[tb >> a.log2_page];
-                if (page < 0 || page >= a.num_pages) {
-                    if (lane == 0) flag(a.status, DSA_DEV_PAGE_OOB);
-                    kb[j].live = false;
-                } else {
-                    const size_t row = (size_t)page * a.page_size + (tb & pmask) + n;
-                    kb[j].b = load_q_operand(a.k_code + row * 128, g);
-                    kb[j].scale = a.k_scale[row];
-                }
-            }
+            const int page = tb < vmax ? s_page[(tb >> a.log2_page) - p0] : -1;
+            const size_t row = page >= 0 ? (size_t)page * a.page_size + (tb & pmask) + n : (size_t)n;
+            kg.b[j] = load_q_operand(a.k_code + row * 128, g);
         }
+        const int t = tg + lane;
+        const int page = t < vmax ? s_page[(t >> a.log2_page) - p0] : -1;
+        kg.scale = a.k_scale[page >= 0 ? (size_t)page * a.page_size + (t & pmask) : 0];
+    };
+
+    // Scores of the group at tg for every row of the group.
+    auto process = [&](const KeyGroup& kg, int tg) {
+        bool live[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tb = tg + 16 * j;
+            live[j] = tb < vmax && s_page[(tb >> a.log2_page) - p0] >= 0;
+        }
+        // Scale of this lane's token column in block j is held by lane 16j+n.
+        float ks[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ks[j] = __shfl(kg.scale, 16 * j + n);
 #pragma unroll 1
         for (int rr = 0; rr < G; ++rr) {
             const int r = r0 + rr;
@@ -173,13 +211,36 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int tb = tg + 16 * j;
-                if (kb[j].live && tb < v) {
-                    const float s = score_block(qa, wq, kb[j]);
-                    if (g == j && tb + n < v) mine = s;
+                if (live[j] && tb < v) {
+                    const float sc = block_dot(qa, wq, kg.b[j]) * ks[j];
+                    if (g == j && tb + n < v) mine = sc;
                 }
             }
             const int t = tg + lane;
             if (t < t_end) a.scores[(size_t)r * a.score_stride + t] = mine;
+        }
+    };
+
+    // Two key buffers in turn: the loads of the next group are in flight
+    // while the current one is computed, and no register copy forces a wait
+    // on them (or on the score stores) before the next loads go out.
+    // The last prefetch of a wavefront re-reads its current group (an L2
+    // hit) rather than branching around the loads.
+    KeyGroup ka, kb;
+    int tg = t0 + wv * 64;
+    if (tg < t_comp) {
+        load_group(tg, ka);
+        while (true) {
+            const bool m1 = tg + 256 < t_comp;
+            load_group(m1 ? tg + 256 : tg, kb);
+            process(ka, tg);
+            tg += 256;
+            if (!m1) break;
+            const bool m2 = tg + 256 < t_comp;
+            load_group(m2 ? tg + 256 : tg, ka);
+            process(kb, tg);
+            tg += 256;
+            if (!m2) break;
         }
     }
 
