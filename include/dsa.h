@@ -148,7 +148,9 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
  * selected count bounds the work; a lone split writes the final output and
  * natural-log LSE directly).
  * For row r, head h, split s over entries [s*c, min(n, (s+1)*c)) of
- * topk_idx[r] with n = topk_count[r], c = ceil(n / n_splits):
+ * topk_idx[r] with n = topk_count[r], c = ceil(top_k / n_splits) (fixed by
+ * top_k, so a split's range is known before the count is read; when
+ * n < top_k the last splits may be empty):
  *   x_t   = dec(kv_code[t]) * kv_scale[t]            (576 wide)
  *   l_t   = sm_scale * (q[r][h] . x_t)
  *   o_s   = sum_t e^{l_t - m} x_t[0:512] / sum_t e^{l_t - m},  lse_s = m + ln sum_t e^{l_t - m}

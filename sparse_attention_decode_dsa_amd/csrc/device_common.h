@@ -26,6 +26,14 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, co
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// D(16x16 f32) += A(16x32 fp8) * B(32x16 fp8) (v_mfma_f32_16x16x32_fp8_fp8,
+// E4M3 both); lane l holds row/column l % 16 and 8 K-bytes for lane group
+// l / 16.
+__device__ __forceinline__ v4f mfma_fp8_16x16x32(const v2i& a, const v2i& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b),
+                                                     c, 0, 0, 0);
+}
+
 // D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16); lane l holds row/column
 // l % 16 and the 8 K-values of lane group l / 16.
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, const v4f& c) {
@@ -150,11 +158,67 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     return r;
 }
 
+// Maximum / sum over the four 16-lane rows of a wavefront for each lane
+// position l % 16 (every lane gets the result).  permlane16_swap(x, x)
+// returns (rows 0,0,2,2) and (rows 1,1,3,3) of x; permlane32_swap(y, y)
+// returns (rows 0,1,0,1) and (rows 2,3,2,3) of y.  Every lane adds in the
+// same order, so the sum is identical across the rows.
+__device__ __forceinline__ float rows4_max(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float w = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    const uint32_t uw = __float_as_uint(w);
+    const auto t = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float w = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    const uint32_t uw = __float_as_uint(w);
+    const auto t = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 // Forces a value into registers at this point and hides where it came
 // from, so the compiler cannot re-create it later by reloading memory.
 template <typename T>
 __device__ __forceinline__ void pin(T& v) {
     asm volatile("" : "+v"(v));
+}
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() is a release /
+// acquire fence at workgroup scope, which drains every outstanding global
+// load of the wavefront (vmcnt(0)), LDS-direct loads included; a kernel
+// that keeps such loads in flight across barriers waits for them itself,
+// with counts it knows, and synchronises with this: each wavefront's LDS
+// reads and writes complete (lgkmcnt(0)), then the barrier.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // vmcnt 63: no wait; lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS byte offset of a pointer into __shared__ memory (its low 32 bits).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
+// LDS-direct loads (global_load_lds_dwordx4 / _dword): lane i's 16 (4)
+// bytes at `src` land at LDS byte lds + 16 i (4 i); `lds` is wave-uniform
+// and goes to M0.  They are written as inline assembly so that the
+// compiler neither tracks them nor inserts its own waits for them: its
+// wait insertion cannot always tell which LDS accesses such a load may
+// overlap, and then drains every load in flight before an unrelated LDS
+// access.  The caller waits with explicit vmcnt counts (in-order completion)
+// before the data is read, and synchronises the workgroup with lds_sync().
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ void flag(int32_t* status, int32_t bit) {

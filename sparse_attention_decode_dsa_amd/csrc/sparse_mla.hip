@@ -4,35 +4,52 @@
 // the row's selected list, walked in tiles of 64 tokens with an online
 // softmax.  Per tile:
 //   gather  the 64 selected 576-byte fp8 rows through the block table into
-//           LDS (rows padded to 592 bytes so 16 consecutive rows start on 16
-//           distinct bank groups), with their fp32 scales;
-//   QK      wavefront w computes the logits of tokens [16w, 16w+16) for all
-//           heads: heads are the M dimension of v_mfma_f32_16x16x32_bf16 (one
-//           chain per block of 16 heads sharing the token operand), tokens N,
-//           the 576 latent+rope dims K.  The query sits in LDS for the whole
-//           split (rows padded to 1168 bytes: conflict-free 16-byte reads);
-//           each fp8 byte converts exactly to bf16 once; the token scale and
-//           sm_scale multiply the fp32 logits;
-//   softmax the tile maximum per head goes through LDS, every wavefront
-//           keeps the same running max (the output is rescaled only when it
-//           moved); P' = exp(l - m) * token scale is written to LDS in bf16;
+//           LDS (rows padded to 592 bytes), with their fp32 scales;
+//   QK      on fp8 matrix cores: the tokens' fp8 bytes are the A operand as
+//           they are (M = tokens), the query the B operand (N = heads).  The
+//           bf16 query is split exactly into two fp8 terms per head,
+//           q = s_h (hi + lo / 16) with s_h a power of two (a bf16 value has
+//           8 significant bits, an E4M3 value 4), so two accumulator chains
+//           give the exact products without converting any key byte; both
+//           terms stay in registers for the whole split.  Wavefront w owns
+//           head block w % HB and 16 HB tokens; K steps of 128 use
+//           v_mfma_f32_16x16x128_f8f6f4, the last 64 bytes
+//           v_mfma_f32_16x16x32_fp8_fp8;
+//   softmax a lane holds 4 tokens of one head per token block, so the
+//           per-head maximum and sum reduce in-lane and then across the four
+//           16-lane rows with two permlane swaps; the tile maximum per head
+//           goes through LDS and every wavefront keeps the same running max
+//           (the output is rescaled only when it moved); P' = exp(l - m) *
+//           token scale goes to LDS in bf16, 4 tokens per 8-byte store;
 //   PV      wavefront w owns output columns [128w, 128w+128) for all heads:
 //           A = P' (heads x tokens), B = the fp8 rows read transposed by
 //           ds_read_b64_tr_b8 (8 tokens of one column per lane), in bf16.
 // The value rows are the first 512 entries of the same rows (absorbed MLA),
 // so a tile is read from HBM once for both products.
 //
-// Latency hiding: the block table is walked once for the whole split (slot ->
-// page -> physical row, kept in LDS).  Tiles are gathered by LDS-direct
-// loads (global_load_lds_dwordx4: each lane's 16 bytes land at the
-// wavefront's LDS base + 16 * lane), so the gather of tile i+1 needs no
-// registers and runs while tile i is computed from the other buffer.
+// Latency hiding: a split's range of the selected list depends only on top_k,
+// so its entries are loaded together with the row's metadata; the block
+// table is then walked once for the whole split (slot -> page -> physical
+// row, kept in LDS).  Tiles are gathered by LDS-direct loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the wavefront's LDS
+// base + 16 * lane), which need no registers: with four tile buffers, three
+// tiles are in flight while the fourth is computed.  Each wavefront waits
+// with an explicit count for its own loads of the tile it needs next, and
+// barriers order LDS only, so loads of later tiles stay in flight.
 //
-// K ordering in QK: lane group g supplies, for the MFMA pair p, dims
-// [64p + 16g, 64p + 16g + 8) and then [64p + 16g + 8, 64p + 16g + 16), so one
-// 16-byte LDS read of a row feeds two MFMAs; the query operand uses the same
-// dims.  Accumulator rows 4*(l/16)+i of a lane are the same heads in the QK
-// and PV layouts, so the running max and sum are per-lane state.
+// LDS banking (gfx950: 16-byte reads are served 32 lanes at a time, 8-byte
+// accesses 64 lanes at a time, over 512 bytes of banks): rows are 592 bytes
+// apart (37 chunks of 16), so 16 consecutive rows fall on 16 distinct odd
+// multiples of 16 bytes and the next 16 rows on the other half.  QK's K
+// order therefore gives lane groups g = 0..3 the 16-byte chunks
+// c + {0, 16, 8, 24} of a row: the two groups served together differ by
+// 256 bytes and never collide.  For the 128-wide step p the chunks are
+// c = 2p and 2p + 1; the rope tail is chunk 32 + g.  Both operands use the
+// same byte positions, so the sums are the plain dot products.  P' is laid
+// out as [token group of 8][head][8 tokens] with 768 bytes per token group,
+// which makes both its 8-byte stores and its 16-byte A-operand reads
+// conflict-free.  ds_read_b64_tr_b8 over 32 rows of 592 bytes is
+// conflict-free as it is.
 #include "device_common.h"
 #include "launch.h"
 
@@ -43,301 +60,477 @@ namespace {
 constexpr int kT = 64;            // tokens per tile
 constexpr int kRowBytes = 576;
 constexpr int kXStride = 592;     // LDS bytes per gathered row
-constexpr int kPStride = 144;     // LDS bytes per head of P' (64 bf16 + 16 pad)
-constexpr int kQStride = 1168;    // LDS bytes per query head (576 bf16 + 16 pad)
+constexpr int kPGroup = 768;      // LDS bytes per group of 8 tokens of P' (up to 32 heads x 16 B + pad)
 constexpr int kDv = 512;
 constexpr int kRowChunks = kXStride / 16;        // 37: 36 data chunks + 1 pad chunk
 constexpr int kTileChunks = kT * kRowChunks;       // 2368 chunks of 16 bytes
 constexpr int kDmaInsts = kTileChunks / kWave;     // 37 wavefront-wide LDS-direct loads
-constexpr int kDmaPerWave = (kDmaInsts + 3) / 4;   // 10
-constexpr int kMaxSplitLen = kTopkMaxK;  // selected entries one workgroup may own
 
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int HB>
-__global__ __launch_bounds__(256) void sparse_mla_kernel(MlaArgs a) {
+// LDS-direct loads of one tile: the 37 loads go round-robin over the NW
+// wavefronts (load j by wavefront j % NW); the last wavefront also loads the
+// 64 token scales.
+template <int NW>
+struct DmaPlan {
+    static constexpr int kPer = (kDmaInsts + NW - 1) / NW;   // loads per wavefront, at most
+    static constexpr int count(int w) { return (kDmaInsts - w + NW - 1) / NW + (w == NW - 1 ? 1 : 0); }
+};
+static_assert(DmaPlan<4>::count(0) == 10 && DmaPlan<4>::count(1) == 9 && DmaPlan<4>::count(3) == 10,
+              "per-wavefront load counts, 4 wavefronts");
+static_assert(DmaPlan<8>::count(0) == 5 && DmaPlan<8>::count(4) == 5 && DmaPlan<8>::count(5) == 4 &&
+              DmaPlan<8>::count(7) == 5, "per-wavefront load counts, 8 wavefronts");
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most this wavefront's loads of the `younger` tiles issued
+// after the one needed now are outstanding (0 <= younger <= 2).  A
+// wavefront issues kPer or kPer - 1 loads per tile.
+template <int NW, int N>
+__device__ __forceinline__ void wait_tiles_n(int wv) {
+    constexpr int kPer = DmaPlan<NW>::kPer;
+    if (DmaPlan<NW>::count(wv) == kPer) wait_vm<N * kPer>();
+    else wait_vm<N * (kPer - 1)>();
+}
+template <int NW>
+__device__ __forceinline__ void wait_tiles(int wv, int younger) {
+    if (younger <= 0) wait_vm<0>();
+    else if (younger == 1) wait_tiles_n<NW, 1>(wv);
+    else wait_tiles_n<NW, 2>(wv);
+}
+
+// NB tile buffers: 4 (three tiles in flight while one is computed) when a
+// split holds at most 1024 entries, else 2, which leaves LDS for the physical
+// rows of a split of up to top_k = 8192 entries.
+template <int NB>
+struct MlaGeom {
+    static_assert(NB == 2 || NB == 4, "tile buffers");
+    static constexpr int kRowsCap = NB == 4 ? 1024 : kTopkMaxK;  // split entries kept in LDS
+};
+
+// 16-byte chunk of a 592-byte LDS row that lane group g reads for half h
+// of the 128-wide K step p (see the banking note above).
+__device__ __forceinline__ int qk_chunk(int p, int h, int g) {
+    return 2 * p + h + ((g & 1) << 4) + ((g >> 1) << 3);
+}
+
+template <int HB, int NB>
+__global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     constexpr int H = 16 * HB;
-    __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kT * kXStride];
-    __shared__ __attribute__((aligned(16))) uint8_t s_p[H * kPStride];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[H * kQStride];
-    __shared__ int32_t s_rows[kMaxSplitLen];
-    __shared__ float s_scale[2][kT];
-    __shared__ float s_red[4][H];
-    __shared__ int s_geo[4];
+    constexpr int NW = 4 * HB;          // wavefronts: one per (token block, head block) in QK
+    constexpr int NT = 64 * NW;
+    constexpr int CW = kDv / NW;        // output columns per wavefront in PV
+    constexpr int NCB = CW / 16;
+    constexpr int kDmaPer = DmaPlan<NW>::kPer;
+    constexpr int kRowsCap = MlaGeom<NB>::kRowsCap;
+    constexpr int kTileBytes = kT * kXStride;
+    // Tile buffers; the loads into them are issued as inline assembly and
+    // waited for with explicit counts, so the compiler never waits for them.
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[NB][kTileBytes];
+    __shared__ __attribute__((aligned(16))) float s_sc[NB][kT];
+    __shared__ float s_qsc[H];                                            // per-head power-of-two scale
+    __shared__ __attribute__((aligned(16))) uint8_t s_p[8 * kPGroup];
+    __shared__ int32_t s_rows[kRowsCap];
+    __shared__ __attribute__((aligned(16))) float s_red[H][4];           // per-head values of the wavefronts
+    __shared__ __attribute__((aligned(16))) float s_alpha[H];
+    __shared__ __attribute__((aligned(16))) float s_m[H];
+    __shared__ int s_moved[HB];
+    __shared__ int s_bad;
+    // The query terms are staged in the last tile buffer, which the first
+    // gathers leave free until the first tile's barrier.
+    uint8_t* const s_qh = s_x[NB - 1];
+    uint8_t* const s_ql = s_qh + H * kXStride;
+    static_assert(2 * H * kXStride <= kTileBytes, "query terms fit one tile buffer");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
     const int nn = lane & 15;
     const int g = lane >> 4;
+    const int hb = wv % HB;         // head block of this wavefront in QK
+    const int tbk = wv / HB;        // its token block: tokens [16 tbk, 16 tbk + 16) of a tile
     const int r = blockIdx.y;
     const int sp = blockIdx.x;
     const int ns = gridDim.x;
 
-    if (tid == 0) {
-        const int b = a.row_req[r];
-        const int v = a.row_vis[r];
-        const int cnt = a.topk_count[r];
-        bool ok = b >= 0 && b < a.batch && v >= 0 && v <= a.max_pages * a.page_size;
-        if (!ok) flag(a.status, DSA_DEV_ROW_RANGE);
-        if (ok && (cnt < 0 || cnt > a.top_k || cnt > v)) {
-            flag(a.status, DSA_DEV_TOPK_OOB);
-            ok = false;
+    // Row metadata (uniform loads) and the split's range of the selected
+    // list.  The range depends only on top_k, so the list entries can be
+    // loaded together with the metadata.
+    const int b_raw = a.row_req[r];
+    const int v_raw = a.row_vis[r];
+    const int c_raw = a.topk_count[r];
+    const int chunk = (a.top_k + ns - 1) / ns;
+    const int lo = min(a.top_k, sp * chunk);
+    const int hi_list = min(a.top_k, lo + chunk);
+    const int32_t* sel = a.topk_idx + (size_t)r * a.top_k;
+
+    // First batch of list entries (8 per thread), issued before anything
+    // else; indexes are clamped into the list.
+    constexpr int kBatch = 8 * NT;
+    int slot[8];
+    auto load_slots = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (base + NT * u < hi_list) slot[u] = sel[min(base + NT * u + tid, hi_list - 1)];
+    };
+    load_slots(lo);
+
+    // Query -> two fp8 terms per head, staged in LDS rows of 592 bytes.
+    // Wavefront wv takes heads wv, wv+NW, ...; lane l holds 16-byte chunk l
+    // (and 64 + l for l < 8) of the 1152-byte bf16 row.  With
+    // s = 2^ceil(log2(max|q| / 448)) (1 for a zero head): hi = RNE_E4M3(q / s),
+    // lo = RNE_E4M3(16 (q / s - hi)); q / s - hi is exact, and so is lo
+    // wherever 16 (q / s - hi) is an E4M3 value.
+    constexpr int kQH = H / NW;   // heads per wavefront
+    uint4 qc0[kQH], qc1[kQH];
+#pragma unroll
+    for (int j = 0; j < kQH; ++j) {   // all loads first, then the arithmetic
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q + ((size_t)r * H + wv + NW * j) * kRowBytes);
+        qc0[j] = *reinterpret_cast<const uint4*>(src + 16 * lane);
+        qc1[j] = uint4{0u, 0u, 0u, 0u};
+        if (lane < 8) qc1[j] = *reinterpret_cast<const uint4*>(src + 16 * (64 + lane));
+    }
+#pragma unroll
+    for (int j = 0; j < kQH; ++j) {
+        const int hq = wv + NW * j;
+        const uint4 c0 = qc0[j], c1 = qc1[j];
+        float v[16];
+        const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+            amax = fmaxf(amax, fmaxf(fabsf(v[2 * k]), fabsf(v[2 * k + 1])));
         }
-        s_geo[0] = ok ? b : 0;
-        s_geo[1] = ok ? v : 0;
-        s_geo[2] = ok ? cnt : 0;
-        s_geo[3] = 0;
+        amax = wave_max(amax);
+        float s = 1.0f;
+        if (amax > 0.0f) {
+            int e;
+            const float m = frexpf(amax / 448.0f, &e);   // amax / 448 = m 2^e, m in [0.5, 1)
+            s = ldexpf(1.0f, m == 0.5f ? e - 1 : e);      // smallest power of two >= amax / 448
+        }
+        const float inv = 1.0f / s;                        // exact: s is a power of two
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float l4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float x = v[4 * k + u] * inv;
+                const uint32_t hbyte = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xFFu;
+                l4[u] = 16.0f * (x - __builtin_amdgcn_cvt_f32_fp8(hbyte, 0));
+            }
+            int hp = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k] * inv, v[4 * k + 1] * inv, 0, false);
+            hp = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k + 2] * inv, v[4 * k + 3] * inv, hp, true);
+            int lp = __builtin_amdgcn_cvt_pk_fp8_f32(l4[0], l4[1], 0, false);
+            lp = __builtin_amdgcn_cvt_pk_fp8_f32(l4[2], l4[3], lp, true);
+            hw[k] = (uint32_t)hp;
+            lw[k] = (uint32_t)lp;
+        }
+        // chunk l covers bf16 elements [8l, 8l+8): fp8 bytes [8l, 8l+8)
+        *reinterpret_cast<uint2*>(s_qh + hq * kXStride + 8 * lane) = uint2{hw[0], hw[1]};
+        *reinterpret_cast<uint2*>(s_ql + hq * kXStride + 8 * lane) = uint2{lw[0], lw[1]};
+        if (lane < 8) {
+            *reinterpret_cast<uint2*>(s_qh + hq * kXStride + 8 * (64 + lane)) = uint2{hw[2], hw[3]};
+            *reinterpret_cast<uint2*>(s_ql + hq * kXStride + 8 * (64 + lane)) = uint2{lw[2], lw[3]};
+        }
+        if (lane == 0) s_qsc[hq] = s;
     }
 
-    // Query of all heads into LDS.
-    {
-        const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (size_t)r * H * kRowBytes);
-        for (int c = tid; c < H * 72; c += 256) {
-            const int h = c / 72, part = c - h * 72;
-            *reinterpret_cast<uint4*>(s_q + h * kQStride + part * 16) =
-                *reinterpret_cast<const uint4*>(qsrc + (size_t)h * kRowBytes * 2 + part * 16);
-        }
+    bool ok = b_raw >= 0 && b_raw < a.batch && v_raw >= 0 && v_raw <= a.max_pages * a.page_size;
+    if (!ok && tid == 0) flag(a.status, DSA_DEV_ROW_RANGE);
+    if (ok && (c_raw < 0 || c_raw > a.top_k || c_raw > v_raw)) {
+        if (tid == 0) flag(a.status, DSA_DEV_TOPK_OOB);
+        ok = false;
     }
-    __syncthreads();
-    const int vis = s_geo[1];
-    const int cnt = s_geo[2];
-    const int chunk = (cnt + ns - 1) / ns;
-    const int lo = min(cnt, sp * chunk);
-    const int hi = min(cnt, lo + chunk);
-    const int n_tiles = (hi - lo + kT - 1) / kT;
-    const int32_t* sel = a.topk_idx + (size_t)r * a.top_k;
-    const int32_t* pt = a.page_table + (size_t)s_geo[0] * a.max_pages;
+    const int vis = ok ? v_raw : 0;
+    const int hi = ok ? min(hi_list, c_raw) : lo;    // entries [lo, hi) of the list are ours
+    const int n_tiles = hi > lo ? (hi - lo + kT - 1) / kT : 0;
+    const int32_t* pt = a.page_table + (size_t)(ok ? b_raw : 0) * a.max_pages;
     const int pmask = a.page_size - 1;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+
+    // The query operand of this lane (head 16 hb + nn, lane group g) for the
+    // whole split: 9 chunks per term, in the QK K order.
+    v4i qh[9], ql[9];
+    {
+        const int qo = (16 * hb + nn) * kXStride;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                qh[2 * p + h] = *reinterpret_cast<const v4i*>(s_qh + qo + 16 * qk_chunk(p, h, g));
+                ql[2 * p + h] = *reinterpret_cast<const v4i*>(s_ql + qo + 16 * qk_chunk(p, h, g));
+            }
+        qh[8] = *reinterpret_cast<const v4i*>(s_qh + qo + 16 * (32 + g));
+        ql[8] = *reinterpret_cast<const v4i*>(s_ql + qo + 16 * (32 + g));
+    }
+    const float cq = a.sm_scale * s_qsc[16 * hb + nn];
 
     // Block-table walk for the whole split, once: selected slot -> page ->
     // physical row, kept in LDS (-1 for invalid entries, which are reported).
-    // Loads go out in batches of 8 per thread before their results are used.
-    for (int base = lo; base < hi; base += 256 * 8) {
-        int slot[8], page[8];
+    // All page-table loads of a batch go out before any result is used;
+    // their indexes are clamped into the table so that they need no branch,
+    // and validity is decided afterwards.
+    auto walk = [&](int base) {
+        int page[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (base + NT * u < hi) page[u] = pt[min(max(slot[u], 0) >> a.log2_page, a.max_pages - 1)];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int e = base + 256 * u + tid;
-            slot[u] = e < hi ? sel[e] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = base + 256 * u + tid;
-            page[u] = -1;
-            if (e < hi) {
-                if (slot[u] < 0 || slot[u] >= vis) flag(a.status, DSA_DEV_TOPK_OOB);
-                else page[u] = pt[slot[u] >> a.log2_page];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = base + 256 * u + tid;
-            if (e < hi) {
+            const int e = base + NT * u + tid;
+            if (base + NT * u < hi && e < hi) {
                 int32_t row = -1;
-                if (page[u] >= a.num_pages || (page[u] < 0 && slot[u] >= 0 && slot[u] < vis)) {
+                if (slot[u] < 0 || slot[u] >= vis) {
+                    flag(a.status, DSA_DEV_TOPK_OOB);
+                } else if (page[u] < 0 || page[u] >= a.num_pages) {
                     flag(a.status, DSA_DEV_PAGE_OOB);
-                } else if (page[u] >= 0) {
+                } else {
                     row = page[u] * a.page_size + (slot[u] & pmask);
                 }
-                if (row < 0) s_geo[3] = 1;
+                if (row < 0) s_bad = 1;
                 s_rows[e - lo] = row;
             }
         }
+    };
+    walk(lo);
+    if constexpr (NB == 2) {   // splits longer than one batch
+        for (int base = lo + kBatch; base < hi; base += kBatch) {
+            load_slots(base);
+            walk(base);
+        }
     }
+    static_assert(MlaGeom<4>::kRowsCap <= 2048, "a four-buffer split is one batch (kBatch >= 2048)");
+    __syncthreads();
+    const bool any_bad = s_bad != 0;
 
     // Row of tile-local token t of the tile starting at split entry `base`.
-    auto row_at = [&](int base, int t) -> int32_t { return base + t < hi ? s_rows[base + t - lo] : -1; };
+    // The read is clamped into the array and its value discarded past the end,
+    // so it needs no branch.
+    auto row_at = [&](int base, int t) -> int32_t {
+        const int32_t v = s_rows[min(base + t - lo, kRowsCap - 1)];
+        return base + t < hi ? v : -1;
+    };
 
-    // LDS-direct gather.  Wavefront wv issues the loads j = wv, wv+4, ... of
+    // LDS-direct gather.  Wavefront wv issues the loads j = wv, wv+NW, ... of
     // a tile; lane i of load j fills tile chunk 64j + i, i.e. row t =
     // chunk / 37, part chunk % 37 (part 36 is the row's pad and repeats part
-    // 35).  Dead rows read row 0 of page 0 and are zeroed afterwards.
-    int dma_t[kDmaPerWave], dma_off[kDmaPerWave];
-#pragma unroll
-    for (int jj = 0; jj < kDmaPerWave; ++jj) {
-        const int c = 64 * (wv + 4 * jj) + lane;
-        const int t = c / kRowChunks;
-        const int part = min(c - t * kRowChunks, 35);
-        dma_t[jj] = t;
-        dma_off[jj] = part * 16;
-    }
-    auto gather_issue = [&](int buf, int base) {
-#pragma unroll
-        for (int jj = 0; jj < kDmaPerWave; ++jj) {
-            const int j = wv + 4 * jj;
-            if (j < kDmaInsts) {
-                const int32_t row = max(row_at(base, dma_t[jj]), 0);
-                const uint8_t* gp = a.kv_code + (size_t)row * kRowBytes + dma_off[jj];
-                __builtin_amdgcn_global_load_lds(gp, (lds_void*)&s_x[buf][j * 1024], 16, 0, 0);
-            }
-        }
-        if (wv == 0) {
-            const int32_t row = max(row_at(base, lane), 0);
-            __builtin_amdgcn_global_load_lds(a.kv_scale + row, (lds_void*)&s_scale[buf][0], 4, 0, 0);
-        }
+    // 35).  Dead rows read row 0 of page 0 and are zeroed afterwards.  All
+    // row ids are read from LDS before the first load is issued.
+    // Tile row and byte offset of lane `lane` in load j (recomputed at each
+    // issue rather than kept in registers).
+    auto dma_geo = [&](int j, int& t, int& off) {
+        const int c = 64 * j + lane;
+        t = c / kRowChunks;
+        off = min(c - t * kRowChunks, 35) * 16;
     };
-    // Tiles that may hold dead rows: a partial last tile, or any invalid entry.
-    auto zero_dead = [&](int buf, int base) {
-        for (int c = tid; c < kT * 36; c += 256) {
+    auto issue = [&](int buf, int base) {
+        const uint32_t xl = lds_offset(s_x[buf]);
+        const uint32_t sl = lds_offset(s_sc[buf]);
+        int32_t row[kDmaPer], off[kDmaPer];
+#pragma unroll
+        for (int jj = 0; jj < kDmaPer; ++jj) {
+            int t;
+            dma_geo(min(wv + NW * jj, kDmaInsts - 1), t, off[jj]);
+            row[jj] = max(row_at(base, t), 0);
+        }
+        const int32_t srow = max(row_at(base, lane), 0);
+        // Loads j = wv + NW jj; the last one exists only while j < 37.
+#pragma unroll
+        for (int jj = 0; jj < kDmaPer - 1; ++jj)
+            lds_dma16(a.kv_code + (size_t)row[jj] * kRowBytes + off[jj], xl + (wv + NW * jj) * 1024);
+        if (wv + NW * (kDmaPer - 1) < kDmaInsts)
+            lds_dma16(a.kv_code + (size_t)row[kDmaPer - 1] * kRowBytes + off[kDmaPer - 1],
+                      xl + (wv + NW * (kDmaPer - 1)) * 1024);
+        if (wv == NW - 1) lds_dma4(a.kv_scale + srow, sl);
+    };
+    // Tiles with dead rows (past the split's end, or invalid entries) have
+    // those rows zeroed, so no stale or garbage bytes reach the PV product.
+    auto zero_dead = [&](uint8_t* xb, int base) {
+        for (int c = tid; c < kT * 36; c += NT) {
             const int t = c / 36, part = c - t * 36;
-            if (row_at(base, t) < 0) *reinterpret_cast<uint4*>(&s_x[buf][t * kXStride + part * 16]) = uint4{0u, 0u, 0u, 0u};
+            if (row_at(base, t) < 0) *reinterpret_cast<uint4*>(xb + t * kXStride + part * 16) = uint4{0u, 0u, 0u, 0u};
         }
     };
 
-    // Prologue: tile 0.
-    __syncthreads();
-    const bool maybe_dead = ((hi - lo) % kT) != 0 || s_geo[3] != 0;
-    if (n_tiles > 0) {
-        gather_issue(0, lo);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (maybe_dead) zero_dead(0, lo);
-    }
-    __syncthreads();
+    // Prologue: the first NB-1 tiles in flight (into buffers other than the
+    // query staging buffer).
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j)
+        if (j < n_tiles) issue(j, lo + j * kT);
 
-    float m_run[HB][4], l_run[HB][4];
-    v4f o_acc[HB][8];
+    // Softmax state: in the QK layout a lane owns head 16 hb + nn (m_run,
+    // and l_run: this wavefront's share of the denominator); in the PV
+    // layout accumulator row i of lane group g is head 16 h2 + 4g + i.
+    float m_run = -INFINITY, l_run = 0.0f;
+    v4f o_acc[HB][NCB];
 #pragma unroll
-    for (int h2 = 0; h2 < HB; ++h2) {
+    for (int h2 = 0; h2 < HB; ++h2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m_run[h2][i] = -INFINITY;
-            l_run[h2][i] = 0.0f;
-        }
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) o_acc[h2][cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+        for (int cb = 0; cb < NCB; ++cb) o_acc[h2][cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int it = 0; it < n_tiles; ++it) {
-        const int cur = it & 1, nxt = cur ^ 1;
+    // Per tile: wait for its data, start the gather NB-1 tiles ahead into the
+    // buffer freed by the previous tile, then QK, softmax and PV.
+    for (int it = 0, buf = 0; it < n_tiles; ++it, buf = buf == NB - 1 ? 0 : buf + 1) {
+        uint8_t* xb = s_x[buf];
+        const float* scb = s_sc[buf];
         const int tile = lo + it * kT;
         const int nt = min(kT, hi - tile);
-        if (it + 1 < n_tiles) gather_issue(nxt, tile + kT);
-
-        // QK for tokens [16 wv, 16 wv + 16), all heads.
-        v4f s_acc[HB];
-#pragma unroll
-        for (int h2 = 0; h2 < HB; ++h2) s_acc[h2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        const uint8_t* xrow = &s_x[cur][(16 * wv + nn) * kXStride + 16 * g];
-#pragma unroll
-        for (int p = 0; p < 9; ++p) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(xrow + 64 * p);
-            const v8bf b0 = fp8x8_to_bf16x8(xv.x, xv.y);
-            const v8bf b1 = fp8x8_to_bf16x8(xv.z, xv.w);
-#pragma unroll
-            for (int h2 = 0; h2 < HB; ++h2) {
-                const uint8_t* qrow = s_q + (h2 * 16 + nn) * kQStride + (64 * p + 16 * g) * 2;
-                s_acc[h2] = mfma_bf16_16x16x32(*reinterpret_cast<const v8bf*>(qrow), b0, s_acc[h2]);
-                s_acc[h2] = mfma_bf16_16x16x32(*reinterpret_cast<const v8bf*>(qrow + 16), b1, s_acc[h2]);
-            }
+        wait_tiles<NW>(wv, min(NB - 2, n_tiles - 1 - it));
+        lds_sync();   // tile `it` is in LDS; every wavefront is done with tile it-1
+        if (it + NB - 1 < n_tiles) issue(buf == 0 ? NB - 1 : buf - 1, tile + (NB - 1) * kT);
+        if (nt < kT || any_bad) {
+            zero_dead(xb, tile);
+            lds_sync();
         }
 
-        // Logits and this wavefront's maximum per head.
-        const int tk = 16 * wv + nn;
-        const bool live = tk < nt && row_at(tile, tk) >= 0;
-        const float tsc = s_scale[cur][tk];
-        const float lsc = live ? a.sm_scale * tsc : 0.0f;
-        float lg[HB][4];
+        // QK: token block tbk (A, rows), head block hb (B).
+        v4f ah = v4f{0.0f, 0.0f, 0.0f, 0.0f}, al = ah;
+        {
+            const uint8_t* xr = xb + (16 * tbk + nn) * kXStride;
 #pragma unroll
-        for (int h2 = 0; h2 < HB; ++h2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lg[h2][i] = live ? s_acc[h2][i] * lsc : -INFINITY;
-                const float mx = row16_max(lg[h2][i]);
-                if (nn == 0) s_red[wv][h2 * 16 + 4 * g + i] = mx;
+            for (int p = 0; p < 4; ++p) {
+                const v4i x0 = *reinterpret_cast<const v4i*>(xr + 16 * qk_chunk(p, 0, g));
+                const v4i x1 = *reinterpret_cast<const v4i*>(xr + 16 * qk_chunk(p, 1, g));
+                const v8i xa = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                const v4i h0 = qh[2 * p], h1 = qh[2 * p + 1], l0 = ql[2 * p], l1 = ql[2 * p + 1];
+                ah = mfma_fp8_16x16x128(xa, v8i{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w}, ah);
+                al = mfma_fp8_16x16x128(xa, v8i{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w}, al);
             }
+            const v4i xt = *reinterpret_cast<const v4i*>(xr + 16 * (32 + g));
+            ah = mfma_fp8_16x16x32(v2i{xt.x, xt.y}, v2i{qh[8].x, qh[8].y}, ah);
+            ah = mfma_fp8_16x16x32(v2i{xt.z, xt.w}, v2i{qh[8].z, qh[8].w}, ah);
+            al = mfma_fp8_16x16x32(v2i{xt.x, xt.y}, v2i{ql[8].x, ql[8].y}, al);
+            al = mfma_fp8_16x16x32(v2i{xt.z, xt.w}, v2i{ql[8].z, ql[8].w}, al);
         }
-        __syncthreads();
 
-        // Running max; probabilities of this wavefront's token.
-        float alpha[HB][4];
-        bool moved = false;
+        // Logits of this lane's tokens tk0 + i (tk0 = 16 tbk + 4g) for head
+        // 16 hb + nn, and this wavefront's maximum.
+        const int tk0 = 16 * tbk + 4 * g;
+        const float4 t4 = *reinterpret_cast<const float4*>(scb + tk0);
+        const float ts[4] = {t4.x, t4.y, t4.z, t4.w};
+        bool live[4];
 #pragma unroll
-        for (int h2 = 0; h2 < HB; ++h2) {
+        for (int i = 0; i < 4; ++i) live[i] = tk0 + i < nt;
+        if (any_bad) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = h2 * 16 + 4 * g + i;
-                const float mt = fmaxf(fmaxf(s_red[0][h], s_red[1][h]), fmaxf(s_red[2][h], s_red[3][h]));
-                const float mn = fmaxf(m_run[h2][i], mt);
-                moved |= mn != m_run[h2][i];
-                alpha[h2][i] = (m_run[h2][i] == -INFINITY) ? 0.0f : __expf(m_run[h2][i] - mn);
-                m_run[h2][i] = mn;
-                const float pv = live ? __expf(lg[h2][i] - mn) : 0.0f;
-                l_run[h2][i] = l_run[h2][i] * alpha[h2][i] + row16_sum(pv);
-                *reinterpret_cast<uint16_t*>(s_p + h * kPStride + tk * 2) = f32_to_bf16_rne(live ? pv * tsc : 0.0f);
-            }
+            for (int i = 0; i < 4; ++i) live[i] = live[i] && row_at(tile, tk0 + i) >= 0;
         }
+        float lg[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lg[i] = live[i] ? (ah[i] + 0.0625f * al[i]) * (cq * ts[i]) : -INFINITY;
+            mx = fmaxf(mx, lg[i]);
+        }
+        mx = rows4_max(mx);
+        const int h = 16 * hb + nn;
+        if (g == 0) s_red[h][tbk] = mx;
+        lds_sync();
+
+        // Running max (over the four token blocks); probabilities.
+        const float4 r4 = *reinterpret_cast<const float4*>(&s_red[h][0]);
+        const float mn = fmaxf(m_run, fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)));
+        const bool moved = mn != m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.0f : __expf(m_run - mn);
+        m_run = mn;
+        float pv[4], ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = live[i] ? __expf(lg[i] - mn) : 0.0f;
+            ps += pv[i];
+        }
+        l_run = l_run * alpha + rows4_sum(ps);
+        // tokens t = 16 tbk + 4g + i: group t / 8 = 2 tbk + g / 2, slot 4 (g & 1) + i
+        const v2bf p01 = v2bf{(__bf16)(pv[0] * ts[0]), (__bf16)(pv[1] * ts[1])};
+        const v2bf p23 = v2bf{(__bf16)(pv[2] * ts[2]), (__bf16)(pv[3] * ts[3])};
+        *reinterpret_cast<uint2*>(s_p + (2 * tbk + (g >> 1)) * kPGroup + h * 16 + 8 * (g & 1)) =
+            uint2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+        const bool any_moved = __ballot(moved) != 0ull;   // same in the 4 wavefronts of head block hb
+        if (tbk == 0) {
+            if (g == 0) s_alpha[h] = alpha;
+            if (lane == 0) s_moved[hb] = any_moved;
+        }
+        lds_sync();
+
         // alpha is exactly 1 for every head whose max did not move.
-        if (__ballot(moved) != 0ull) {
 #pragma unroll
-            for (int h2 = 0; h2 < HB; ++h2)
+        for (int h2 = 0; h2 < HB; ++h2) {
+            if (s_moved[h2]) {
+                const float4 al4 = *reinterpret_cast<const float4*>(&s_alpha[16 * h2 + 4 * g]);
+                const float av[4] = {al4.x, al4.y, al4.z, al4.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int cb = 0; cb < 8; ++cb) o_acc[h2][cb][i] *= alpha[h2][i];
+                    for (int cb = 0; cb < NCB; ++cb) o_acc[h2][cb][i] *= av[i];
+            }
         }
-        __syncthreads();
 
-        // PV for columns [128 wv, 128 wv + 128), all heads.
+        // PV for columns [CW wv, CW wv + CW), all heads.  Lane group g's
+        // 8 K values are tokens 32 ks + 8 g + [0, 8) in both operands.
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             v8bf pa[HB];
 #pragma unroll
             for (int h2 = 0; h2 < HB; ++h2)
-                pa[h2] = *reinterpret_cast<const v8bf*>(s_p + (h2 * 16 + nn) * kPStride + (32 * ks + 8 * g) * 2);
-            const uint8_t* trow = &s_x[cur][(32 * ks + 8 * g + (nn >> 1)) * kXStride + 128 * wv + 8 * (nn & 1)];
+                pa[h2] = *reinterpret_cast<const v8bf*>(s_p + (4 * ks + g) * kPGroup + (16 * h2 + nn) * 16);
+            const uint8_t* trow = xb + (32 * ks + 8 * g + (nn >> 1)) * kXStride + CW * wv + 8 * (nn & 1);
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb) {
+            for (int cb = 0; cb < NCB; ++cb) {
                 const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(trow + 16 * cb));
                 const v8bf bx = fp8x8_to_bf16x8((uint32_t)t.x, (uint32_t)t.y);
 #pragma unroll
                 for (int h2 = 0; h2 < HB; ++h2) o_acc[h2][cb] = mfma_bf16_16x16x32(pa[h2], bx, o_acc[h2][cb]);
             }
         }
-        // The next tile's loads were this wavefront's only memory traffic.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (it + 1 < n_tiles && maybe_dead) {
-            zero_dead(nxt, tile + kT);
-            __syncthreads();
-        }
     }
 
-    // Softmax denominators: sum of the four wavefronts' partial sums.
-#pragma unroll
-    for (int h2 = 0; h2 < HB; ++h2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (nn == 0) s_red[wv][h2 * 16 + 4 * g + i] = l_run[h2][i];
+    // Denominators (sum of the wavefronts' shares) and the running max,
+    // moved to the PV layout through LDS.  s_red and s_m are free: every
+    // wavefront read the last tile's maxima before the last barrier.
+    if (g == 0) s_red[16 * hb + nn][tbk] = l_run;
+    if (tbk == 0 && g == 0) s_m[16 * hb + nn] = m_run;
     __syncthreads();
 #pragma unroll
     for (int h2 = 0; h2 < HB; ++h2) {
+        const float4 m4 = *reinterpret_cast<const float4*>(&s_m[16 * h2 + 4 * g]);
+        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int h = h2 * 16 + 4 * g + i;
-            const float l = s_red[0][h] + s_red[1][h] + s_red[2][h] + s_red[3][h];
+            const int hh = h2 * 16 + 4 * g + i;
+            const float4 l4 = *reinterpret_cast<const float4*>(&s_red[hh][0]);
+            const float l = (l4.x + l4.y) + (l4.z + l4.w);
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-            const float lse = l > 0.0f ? m_run[h2][i] + __logf(l) : -INFINITY;
-            const size_t rh = (size_t)r * H + h;
+            const float lse = l > 0.0f ? mv[i] + __logf(l) : -INFINITY;
+            const size_t rh = (size_t)r * H + hh;
             if (ns == 1) {
-                uint16_t* dst = a.out + rh * kDv + 128 * wv + nn;
+                uint16_t* dst = a.out + rh * kDv + CW * wv + nn;
 #pragma unroll
-                for (int cb = 0; cb < 8; ++cb) dst[16 * cb] = f32_to_bf16_rne(o_acc[h2][cb][i] * inv);
+                for (int cb = 0; cb < NCB; ++cb) dst[16 * cb] = f32_to_bf16_rne(o_acc[h2][cb][i] * inv);
                 if (a.out_lse != nullptr && wv == 0 && nn == 0) a.out_lse[rh] = lse;
             } else {
-                float* dst = a.part_o + (rh * ns + sp) * kDv + 128 * wv + nn;
+                float* dst = a.part_o + (rh * ns + sp) * kDv + CW * wv + nn;
 #pragma unroll
-                for (int cb = 0; cb < 8; ++cb) dst[16 * cb] = o_acc[h2][cb][i] * inv;
+                for (int cb = 0; cb < NCB; ++cb) dst[16 * cb] = o_acc[h2][cb][i] * inv;
                 if (wv == 0 && nn == 0) a.part_lse[rh * ns + sp] = lse;
             }
         }
     }
 }
 
-template <int HB>
+template <int HB, int NB>
 hipError_t launch_hb(const MlaArgs& a, hipStream_t stream) {
-    sparse_mla_kernel<HB><<<dim3(a.n_splits, a.n_rows), 256, 0, stream>>>(a);
+    sparse_mla_kernel<HB, NB><<<dim3(a.n_splits, a.n_rows), 256 * HB, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -345,9 +538,11 @@ hipError_t launch_hb(const MlaArgs& a, hipStream_t stream) {
 
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
     if (a.n_rows == 0) return hipSuccess;
+    const int chunk = (a.top_k + a.n_splits - 1) / a.n_splits;
+    const bool ring4 = chunk <= MlaGeom<4>::kRowsCap;
     switch (a.n_heads) {
-        case 16: return launch_hb<1>(a, stream);
-        case 32: return launch_hb<2>(a, stream);
+        case 16: return ring4 ? launch_hb<1, 4>(a, stream) : launch_hb<1, 2>(a, stream);
+        case 32: return ring4 ? launch_hb<2, 4>(a, stream) : launch_hb<2, 2>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
