@@ -180,12 +180,12 @@ def main():
                  topk_idx=step.topk_idx, topk_count=step.topk_count, status=step.status)
         marks[3].record(stream)
         if step.attn_splits == 1:
-            dsa.sparse_mla_decode(i.q_mla, i.kv_code, i.kv_scale, i.page_table, i.row_req, i.row_vis,
+            dsa.sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
                                   step.topk_idx, step.topk_count, 1, i.sm_scale, out=step.out,
                                   out_lse=step.out_lse, status=step.status)
             marks[4].record(stream)
         else:
-            dsa.sparse_mla_decode(i.q_mla, i.kv_code, i.kv_scale, i.page_table, i.row_req, i.row_vis,
+            dsa.sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
                                   step.topk_idx, step.topk_count, step.attn_splits, i.sm_scale,
                                   part_o=step.part_o, part_lse=step.part_lse, status=step.status)
             marks[4].record(stream)

@@ -29,8 +29,11 @@
  *    output 0, lse -inf) rather than read out of bounds.
  *  - Page pool layout: NP pages of P tokens.  Indexer keys: k_code uint8
  *    [NP, P, 128] (E4M3FN codes) and k_scale float32 [NP, P].  MLA rows:
- *    kv_code uint8 [NP, P, 576] (512 latent then 64 rope, E4M3FN) and
- *    kv_scale float32 [NP, P].  A token's value is code * its scale.
+ *    kv_cache uint8 [NP, P, 640], one 640-byte row per token: bytes
+ *    0..575 the E4M3FN codes (512 latent then 64 rope), bytes 576..579 the
+ *    token's fp32 scale (little-endian), bytes 580..639 unused.  A token's
+ *    value is code * its scale.  The scale shares the row so that a gathered
+ *    token costs exactly the five 128-byte lines of its row.
  *  - Block table: page_table int32 [batch, max_pages]; logical slot t of
  *    request b lives at physical row page_table[b][t / P] * P + t % P.
  *    Entries past a request's span are -1 (page "DeepSeek V4 DSpark
@@ -50,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -151,12 +154,12 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
  * topk_idx[r] with n = topk_count[r], c = ceil(top_k / n_splits) (fixed by
  * top_k, so a split's range is known before the count is read; when
  * n < top_k the last splits may be empty):
- *   x_t   = dec(kv_code[t]) * kv_scale[t]            (576 wide)
+ *   x_t   = dec(codes of row t) * scale of row t       (576 wide)
  *   l_t   = sm_scale * (q[r][h] . x_t)
  *   o_s   = sum_t e^{l_t - m} x_t[0:512] / sum_t e^{l_t - m},  lse_s = m + ln sum_t e^{l_t - m}
  * Empty split: o_s = 0, lse_s = -inf.
  *   q [n_rows, n_heads, 576] bf16 bit patterns
- *   kv_code [num_pages, page_size, 576] uint8, kv_scale [num_pages, page_size] f32
+ *   kv_cache [num_pages, page_size, 640] uint8 (layout above)
  *   page_table [batch, max_pages] i32, row_req / row_vis [n_rows] i32
  *   topk_idx [n_rows, top_k] i32, topk_count [n_rows] i32
  * n_splits == 1: writes out [n_rows, n_heads, 512] bf16 (round to nearest
@@ -167,9 +170,9 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
  * Supported: n_heads in {16, 32}, page_size a power of two in [16, 1024],
  * 1 <= n_splits <= 64, 1 <= top_k <= 8192.
  */
-int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_code, const float* kv_scale,
-                          const int32_t* page_table, const int32_t* row_req, const int32_t* row_vis,
-                          const int32_t* topk_idx, const int32_t* topk_count, int32_t n_rows,
+int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
+                          const int32_t* row_req, const int32_t* row_vis, const int32_t* topk_idx,
+                          const int32_t* topk_count, int32_t n_rows,
                           int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
                           int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
                           float* part_o, float* part_lse, uint16_t* out, float* out_lse,

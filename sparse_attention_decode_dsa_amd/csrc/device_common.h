@@ -206,19 +206,16 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)p;
 }
 
-// LDS-direct loads (global_load_lds_dwordx4 / _dword): lane i's 16 (4)
-// bytes at `src` land at LDS byte lds + 16 i (4 i); `lds` is wave-uniform
-// and goes to M0.  They are written as inline assembly so that the
-// compiler neither tracks them nor inserts its own waits for them: its
+// LDS-direct load (global_load_lds_dwordx4): lane i's 16 bytes at `src`
+// land at LDS byte lds + 16 i; `lds` is wave-uniform
+// and goes to M0.  It is written as inline assembly so that the
+// compiler neither tracks it nor inserts its own waits for it: its
 // wait insertion cannot always tell which LDS accesses such a load may
 // overlap, and then drains every load in flight before an unrelated LDS
 // access.  The caller waits with explicit vmcnt counts (in-order completion)
 // before the data is read, and synchronises the workgroup with lds_sync().
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ void flag(int32_t* status, int32_t bit) {

@@ -125,9 +125,9 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
     return launch_status(dsa::launch_topk(a, stream));
 }
 
-int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_code, const float* kv_scale,
-                          const int32_t* page_table, const int32_t* row_req, const int32_t* row_vis,
-                          const int32_t* topk_idx, const int32_t* topk_count, int32_t n_rows,
+int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
+                          const int32_t* row_req, const int32_t* row_vis, const int32_t* topk_idx,
+                          const int32_t* topk_count, int32_t n_rows,
                           int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
                           int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
                           float* part_o, float* part_lse, uint16_t* out, float* out_lse,
@@ -139,13 +139,13 @@ int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_code, const float
     if (n_heads != 16 && n_heads != 32) return DSA_ERR_UNSUPPORTED;
     int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
     if (rc != DSA_OK) return rc;
-    if (!q || !kv_code || !kv_scale || !page_table || !row_req || !row_vis || !topk_idx ||
+    if (!q || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx ||
         !topk_count || !status)
         return DSA_ERR_NULL;
     if (n_splits == 1 ? !out : (!part_o || !part_lse)) return DSA_ERR_NULL;
     if (n_rows == 0) return DSA_OK;
     dsa::MlaArgs a;
-    a.q = q; a.kv_code = kv_code; a.kv_scale = kv_scale; a.page_table = page_table;
+    a.q = q; a.kv_cache = kv_cache; a.page_table = page_table;
     a.row_req = row_req; a.row_vis = row_vis; a.topk_idx = topk_idx; a.topk_count = topk_count;
     a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
     a.page_size = page_size; a.log2_page = log2i(page_size); a.n_heads = n_heads;

@@ -39,8 +39,7 @@ struct TopkArgs {
 
 struct MlaArgs {
     const uint16_t* q;
-    const uint8_t* kv_code;
-    const float* kv_scale;
+    const uint8_t* kv_cache;   // [num_pages, page_size, 640]: codes, fp32 scale, pad
     const int32_t* page_table;
     const int32_t* row_req;
     const int32_t* row_vis;

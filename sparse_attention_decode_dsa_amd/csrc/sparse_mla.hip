@@ -58,7 +58,9 @@ namespace dsa {
 namespace {
 
 constexpr int kT = 64;            // tokens per tile
-constexpr int kRowBytes = 576;
+constexpr int kRowBytes = 576;    // elements of a query head / code bytes of a cache row
+constexpr int kKvRow = 640;       // bytes of a cache row: 576 codes, fp32 scale at 576, pad
+constexpr int kScaleAt = 576;     // byte of the scale within a (cache or LDS) row
 constexpr int kXStride = 592;     // LDS bytes per gathered row
 constexpr int kPGroup = 768;      // LDS bytes per group of 8 tokens of P' (up to 32 heads x 16 B + pad)
 constexpr int kDv = 512;
@@ -69,18 +71,18 @@ constexpr int kDmaInsts = kTileChunks / kWave;     // 37 wavefront-wide LDS-dire
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS-direct loads of one tile: the 37 loads go round-robin over the NW
-// wavefronts (load j by wavefront j % NW); the last wavefront also loads the
-// 64 token scales.
+// LDS-direct loads of one tile: the first 592 bytes (37 chunks: codes,
+// scale, 12 pad bytes) of each of the 64 rows, 37 loads of 64 chunks that go
+// round-robin over the NW wavefronts (load j by wavefront j % NW).
 template <int NW>
 struct DmaPlan {
     static constexpr int kPer = (kDmaInsts + NW - 1) / NW;   // loads per wavefront, at most
-    static constexpr int count(int w) { return (kDmaInsts - w + NW - 1) / NW + (w == NW - 1 ? 1 : 0); }
+    static constexpr int count(int w) { return (kDmaInsts - w + NW - 1) / NW; }
 };
-static_assert(DmaPlan<4>::count(0) == 10 && DmaPlan<4>::count(1) == 9 && DmaPlan<4>::count(3) == 10,
+static_assert(DmaPlan<4>::count(0) == 10 && DmaPlan<4>::count(1) == 9 && DmaPlan<4>::count(3) == 9,
               "per-wavefront load counts, 4 wavefronts");
 static_assert(DmaPlan<8>::count(0) == 5 && DmaPlan<8>::count(4) == 5 && DmaPlan<8>::count(5) == 4 &&
-              DmaPlan<8>::count(7) == 5, "per-wavefront load counts, 8 wavefronts");
+              DmaPlan<8>::count(7) == 4, "per-wavefront load counts, 8 wavefronts");
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (expcnt and lgkmcnt left at their no-wait maxima).
@@ -134,7 +136,6 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     // Tile buffers; the loads into them are issued as inline assembly and
     // waited for with explicit counts, so the compiler never waits for them.
     __shared__ __attribute__((aligned(16))) uint8_t s_x[NB][kTileBytes];
-    __shared__ __attribute__((aligned(16))) float s_sc[NB][kT];
     __shared__ float s_qsc[H];                                            // per-head power-of-two scale
     __shared__ __attribute__((aligned(16))) uint8_t s_p[8 * kPGroup];
     __shared__ int32_t s_rows[kRowsCap];
@@ -324,19 +325,18 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
 
     // LDS-direct gather.  Wavefront wv issues the loads j = wv, wv+NW, ... of
     // a tile; lane i of load j fills tile chunk 64j + i, i.e. row t =
-    // chunk / 37, part chunk % 37 (part 36 is the row's pad and repeats part
-    // 35).  Dead rows read row 0 of page 0 and are zeroed afterwards.  All
-    // row ids are read from LDS before the first load is issued.
+    // chunk / 37, part chunk % 37 (part 36 holds the scale).  Dead rows read
+    // row 0 of page 0 and are zeroed afterwards.  All row ids are read from
+    // LDS before the first load is issued.
     // Tile row and byte offset of lane `lane` in load j (recomputed at each
     // issue rather than kept in registers).
     auto dma_geo = [&](int j, int& t, int& off) {
         const int c = 64 * j + lane;
         t = c / kRowChunks;
-        off = min(c - t * kRowChunks, 35) * 16;
+        off = (c - t * kRowChunks) * 16;
     };
     auto issue = [&](int buf, int base) {
         const uint32_t xl = lds_offset(s_x[buf]);
-        const uint32_t sl = lds_offset(s_sc[buf]);
         int32_t row[kDmaPer], off[kDmaPer];
 #pragma unroll
         for (int jj = 0; jj < kDmaPer; ++jj) {
@@ -344,21 +344,19 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
             dma_geo(min(wv + NW * jj, kDmaInsts - 1), t, off[jj]);
             row[jj] = max(row_at(base, t), 0);
         }
-        const int32_t srow = max(row_at(base, lane), 0);
         // Loads j = wv + NW jj; the last one exists only while j < 37.
 #pragma unroll
         for (int jj = 0; jj < kDmaPer - 1; ++jj)
-            lds_dma16(a.kv_code + (size_t)row[jj] * kRowBytes + off[jj], xl + (wv + NW * jj) * 1024);
+            lds_dma16(a.kv_cache + (size_t)row[jj] * kKvRow + off[jj], xl + (wv + NW * jj) * 1024);
         if (wv + NW * (kDmaPer - 1) < kDmaInsts)
-            lds_dma16(a.kv_code + (size_t)row[kDmaPer - 1] * kRowBytes + off[kDmaPer - 1],
+            lds_dma16(a.kv_cache + (size_t)row[kDmaPer - 1] * kKvRow + off[kDmaPer - 1],
                       xl + (wv + NW * (kDmaPer - 1)) * 1024);
-        if (wv == NW - 1) lds_dma4(a.kv_scale + srow, sl);
     };
     // Tiles with dead rows (past the split's end, or invalid entries) have
     // those rows zeroed, so no stale or garbage bytes reach the PV product.
     auto zero_dead = [&](uint8_t* xb, int base) {
-        for (int c = tid; c < kT * 36; c += NT) {
-            const int t = c / 36, part = c - t * 36;
+        for (int c = tid; c < kT * kRowChunks; c += NT) {
+            const int t = c / kRowChunks, part = c - t * kRowChunks;
             if (row_at(base, t) < 0) *reinterpret_cast<uint4*>(xb + t * kXStride + part * 16) = uint4{0u, 0u, 0u, 0u};
         }
     };
@@ -383,7 +381,6 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     // buffer freed by the previous tile, then QK, softmax and PV.
     for (int it = 0, buf = 0; it < n_tiles; ++it, buf = buf == NB - 1 ? 0 : buf + 1) {
         uint8_t* xb = s_x[buf];
-        const float* scb = s_sc[buf];
         const int tile = lo + it * kT;
         const int nt = min(kT, hi - tile);
         wait_tiles<NW>(wv, min(NB - 2, n_tiles - 1 - it));
@@ -417,8 +414,9 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         // Logits of this lane's tokens tk0 + i (tk0 = 16 tbk + 4g) for head
         // 16 hb + nn, and this wavefront's maximum.
         const int tk0 = 16 * tbk + 4 * g;
-        const float4 t4 = *reinterpret_cast<const float4*>(scb + tk0);
-        const float ts[4] = {t4.x, t4.y, t4.z, t4.w};
+        float ts[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ts[i] = *reinterpret_cast<const float*>(xb + (tk0 + i) * kXStride + kScaleAt);
         bool live[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) live[i] = tk0 + i < nt;

@@ -17,7 +17,7 @@ import os
 
 import torch
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN"}
@@ -38,7 +38,7 @@ _SIGS = {
                           _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
     "dsa_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
     "dsa_topk": ([_p, _i32, _p, _i32, _i32, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p], ctypes.c_int),
-    "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+    "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "dsa_lse_merge": ([_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
 }
@@ -175,13 +175,16 @@ def topk(scores, row_vis, top_k: int, n_splits: int = 1, workspace=None, topk_id
     return topk_idx, topk_count, status
 
 
-def sparse_mla_decode(q, kv_code, kv_scale, page_table, row_req, row_vis, topk_idx, topk_count,
+def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_count,
                       n_splits: int = 1, sm_scale: float = 1.0 / 24.0, part_o=None, part_lse=None,
                       out=None, out_lse=None, status=None, stream=None):
     """Split-K sparse MLA.  n_splits == 1 -> (out bf16 [R,H,512], out_lse f32 [R,H]);
-    otherwise -> (part_o f32 [R,H,S,512], part_lse f32 [R,H,S])."""
+    otherwise -> (part_o f32 [R,H,S,512], part_lse f32 [R,H,S]).  kv_cache is the
+    packed uint8 [NP, P, 640] MLA cache (codes, fp32 scale at byte 576, pad)."""
     r, h, dq = q.shape
-    n_pages, p, _ = kv_code.shape
+    n_pages, p, row_bytes = kv_cache.shape
+    if row_bytes != 640:
+        raise DsaError(f"kv_cache rows must be 640 bytes, got {row_bytes}")
     batch, max_pages = page_table.shape
     top_k = topk_idx.shape[1]
     dev = q.device
@@ -198,7 +201,7 @@ def sparse_mla_decode(q, kv_code, kv_scale, page_table, row_req, row_vis, topk_i
         if part_lse is None:
             part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
     _check(lib().dsa_sparse_mla_decode(
-        _ptr(q, _BF16, "q"), _ptr(kv_code, _FP8, "kv_code"), _ptr(kv_scale, torch.float32, "kv_scale"),
+        _ptr(q, _BF16, "q"), _ptr(kv_cache, torch.uint8, "kv_cache"),
         _ptr(page_table, torch.int32, "page_table"), _ptr(row_req, torch.int32, "row_req"),
         _ptr(row_vis, torch.int32, "row_vis"), _ptr(topk_idx, torch.int32, "topk_idx"),
         _ptr(topk_count, torch.int32, "topk_count"), r, batch, n_pages, max_pages, p, h, top_k,
@@ -269,11 +272,11 @@ class DecodeStep:
         topk(self.scores, i.row_vis, i.top_k, self.index_splits, workspace=self.workspace,
              topk_idx=self.topk_idx, topk_count=self.topk_count, status=self.status, stream=stream)
         if self.attn_splits == 1:
-            sparse_mla_decode(i.q_mla, i.kv_code, i.kv_scale, i.page_table, i.row_req, i.row_vis,
+            sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
                               self.topk_idx, self.topk_count, 1, i.sm_scale, out=self.out,
                               out_lse=self.out_lse, status=self.status, stream=stream)
         else:
-            sparse_mla_decode(i.q_mla, i.kv_code, i.kv_scale, i.page_table, i.row_req, i.row_vis,
+            sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
                               self.topk_idx, self.topk_count, self.attn_splits, i.sm_scale,
                               part_o=self.part_o, part_lse=self.part_lse, status=self.status,
                               stream=stream)

@@ -16,8 +16,11 @@ six-token MTP verify rows and long-prefix prefill rows.
 Layout of one page pool (NP pages of P tokens):
   k_code  uint8   [NP, P, 128]   indexer keys, E4M3FN codes
   k_scale float32 [NP, P]
-  kv_code uint8   [NP, P, 576]   MLA rows (512 latent, then 64 rope), E4M3FN
-  kv_scale float32 [NP, P]
+  kv_cache uint8  [NP, P, 640]   MLA rows: bytes 0..575 the E4M3FN codes (512
+                                 latent, then 64 rope), bytes 576..579 the
+                                 row's fp32 scale, bytes 580..639 unused
+                                 (filled with 0x7F, an E4M3FN NaN code)
+  (kv_code and kv_scale are views of kv_cache's codes and scales)
 Rows (query tokens) are request-major: row r belongs to request row_req[r]
 and sees the first row_vis[r] slots of that request.
 """
@@ -35,6 +38,18 @@ D_QK = 576
 D_V = 512
 TOP_K = 2048
 POISON_SCALE = 1.0e6
+KV_ROW_BYTES = 640      # 576 code bytes + 4 scale bytes, padded to five 128-byte lines
+PAD_CODE = 0x7F
+
+
+def kv_code_view(kv_cache: torch.Tensor) -> torch.Tensor:
+    """uint8 [NP, P, 576] view of the codes of a packed MLA cache."""
+    return kv_cache[..., :D_QK]
+
+
+def kv_scale_view(kv_cache: torch.Tensor) -> torch.Tensor:
+    """float32 [NP, P] view of the scales of a packed MLA cache."""
+    return kv_cache[..., D_QK:D_QK + 4].view(torch.float32).squeeze(-1)
 
 
 @dataclass(frozen=True)
@@ -90,14 +105,21 @@ class Inputs:
     q_mla: torch.Tensor       # bf16 [R, H, 576]
     k_code: torch.Tensor      # u8 [NP, P, 128]
     k_scale: torch.Tensor     # f32 [NP, P]
-    kv_code: torch.Tensor     # u8 [NP, P, 576]
-    kv_scale: torch.Tensor    # f32 [NP, P]
+    kv_cache: torch.Tensor    # u8 [NP, P, 640]: codes, fp32 scale, pad
     page_table: torch.Tensor  # i32 [B, max_pages], -1 past each span
     kv_lens: torch.Tensor     # i32 [B]
     row_req: torch.Tensor     # i32 [R]
     row_vis: torch.Tensor     # i32 [R]
     sm_scale: float = field(default=1.0 / math.sqrt(D_QK))
     planted_slots: torch.Tensor | None = None  # i64 [B, planted]
+
+    @property
+    def kv_code(self) -> torch.Tensor:
+        return kv_code_view(self.kv_cache)
+
+    @property
+    def kv_scale(self) -> torch.Tensor:
+        return kv_scale_view(self.kv_cache)
 
     @property
     def n_rows(self) -> int:
@@ -182,8 +204,9 @@ def make(name_or_cfg, seed: int | None = None, device="cpu", poison: bool = True
     # Caches, page by page in chunks to bound temporary memory.
     k_code = torch.empty((n_pool, p, IDX_DIM), dtype=torch.uint8, device=device)
     k_scale = torch.empty((n_pool, p), dtype=torch.float32, device=device)
-    kv_code = torch.empty((n_pool, p, D_QK), dtype=torch.uint8, device=device)
-    kv_scale = torch.empty((n_pool, p), dtype=torch.float32, device=device)
+    kv_cache = torch.full((n_pool, p, KV_ROW_BYTES), PAD_CODE, dtype=torch.uint8, device=device)
+    kv_code = kv_code_view(kv_cache)
+    kv_scale = kv_scale_view(kv_cache)
     for s in range(0, n_pool, chunk_pages):
         e = min(n_pool, s + chunk_pages)
         c, sc = _encode_fp8_rows(_normal((e - s, p, IDX_DIM), gen, device))
@@ -234,7 +257,7 @@ def make(name_or_cfg, seed: int | None = None, device="cpu", poison: bool = True
             kv_scale[pages, offs] *= cfg.planted_factor
 
     return Inputs(cfg=cfg, seed=seed, q_idx=q_idx, head_w=head_w, q_mla=q_mla,
-                  k_code=k_code, k_scale=k_scale, kv_code=kv_code, kv_scale=kv_scale,
+                  k_code=k_code, k_scale=k_scale, kv_cache=kv_cache,
                   page_table=page_table.to(device), kv_lens=kv.to(torch.int32).to(device),
                   row_req=torch.tensor(rows_req, dtype=torch.int32, device=device),
                   row_vis=torch.tensor(rows_vis, dtype=torch.int32, device=device),
@@ -244,7 +267,7 @@ def make(name_or_cfg, seed: int | None = None, device="cpu", poison: bool = True
 def to(inp: Inputs, device) -> Inputs:
     """Copy every tensor of ``inp`` to ``device``."""
     kw = {}
-    for f in ("q_idx", "head_w", "q_mla", "k_code", "k_scale", "kv_code", "kv_scale",
+    for f in ("q_idx", "head_w", "q_mla", "k_code", "k_scale", "kv_cache",
               "page_table", "kv_lens", "row_req", "row_vis"):
         kw[f] = getattr(inp, f).to(device)
     return replace(inp, **kw)
@@ -273,7 +296,7 @@ def subset(inp: Inputs, rows) -> Inputs:
         head_w=inp.head_w[rows.to(inp.head_w.device)].cpu(),
         q_mla=inp.q_mla[rows.to(inp.q_mla.device)].cpu(),
         k_code=inp.k_code[op].cpu(), k_scale=inp.k_scale[op].cpu(),
-        kv_code=inp.kv_code[op].cpu(), kv_scale=inp.kv_scale[op].cpu(),
+        kv_cache=inp.kv_cache[op].cpu(),
         page_table=new_pt, kv_lens=inp.kv_lens.cpu()[reqs],
         row_req=torch.tensor([new_req[int(r)] for r in row_req.tolist()], dtype=torch.int32),
         row_vis=inp.row_vis.cpu()[rows],
@@ -290,7 +313,8 @@ def as_numpy(inp: Inputs) -> dict:
         "q_idx": u16(inp.q_idx), "head_w": inp.head_w.cpu().numpy(),
         "q_mla": u16(inp.q_mla),
         "k_code": inp.k_code.cpu().numpy(), "k_scale": inp.k_scale.cpu().numpy(),
-        "kv_code": inp.kv_code.cpu().numpy(), "kv_scale": inp.kv_scale.cpu().numpy(),
+        "kv_code": inp.kv_code.cpu().contiguous().numpy(),
+        "kv_scale": inp.kv_scale.cpu().contiguous().numpy(),
         "page_table": inp.page_table.cpu().numpy(), "kv_lens": inp.kv_lens.cpu().numpy(),
         "row_req": inp.row_req.cpu().numpy(), "row_vis": inp.row_vis.cpu().numpy(),
         "page_size": inp.page_size, "top_k": inp.top_k, "sm_scale": inp.sm_scale,

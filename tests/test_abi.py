@@ -40,7 +40,9 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.dsa_abi_version() == dsa.ABI_VERSION == 1
+    assert L.dsa_abi_version() == dsa.ABI_VERSION
+    hdr = open(HEADER).read()
+    assert f"#define DSA_ABI_VERSION {dsa.ABI_VERSION}" in hdr
     for code in (OK, NULL, SHAPE, UNSUP, WS, -5):
         assert dsa.status_string(code).startswith("DSA_")
     assert dsa.status_string(12345) == "unknown"
@@ -94,7 +96,7 @@ def test_topk_validation_and_workspace(L):
 
 
 def _mla(L, **kw):
-    a = dict(q=P, kv_code=P, kv_scale=P, page_table=P, row_req=P, row_vis=P, topk_idx=P,
+    a = dict(q=P, kv_cache=P, page_table=P, row_req=P, row_vis=P, topk_idx=P,
              topk_count=P, n_rows=4, batch=4, num_pages=100, max_pages=20, page_size=256,
              n_heads=32, top_k=2048, n_splits=4, sm_scale=0.04, part_o=P, part_lse=P, out=None,
              out_lse=None, status=P, stream=None)

@@ -64,10 +64,10 @@ def mla_on_oracle_selection(sub, ref, n_splits):
     cnt = torch.from_numpy(ref["topk_count"].astype(np.int32)).cuda()
     st = dsa.new_status()
     if n_splits == 1:
-        out, lse, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_code, g.kv_scale, g.page_table, g.row_req,
+        out, lse, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_cache, g.page_table, g.row_req,
                                             g.row_vis, idx, cnt, 1, g.sm_scale, status=st)
     else:
-        po, pl, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_code, g.kv_scale, g.page_table, g.row_req,
+        po, pl, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_cache, g.page_table, g.row_req,
                                           g.row_vis, idx, cnt, n_splits, g.sm_scale, status=st)
         out, lse = dsa.lse_merge(po, pl)
     torch.cuda.synchronize()
@@ -206,8 +206,8 @@ def test_page_permutation_and_run_to_run_determinism():
     pt = inp.page_table.long()
     new_pt = torch.where(pt >= 0, perm[pt.clamp(min=0)], pt).to(torch.int32)
     from dataclasses import replace
-    p = replace(inp, k_code=inp.k_code[inv], k_scale=inp.k_scale[inv], kv_code=inp.kv_code[inv],
-                kv_scale=inp.kv_scale[inv], page_table=new_pt.contiguous())
+    p = replace(inp, k_code=inp.k_code[inv], k_scale=inp.k_scale[inv], kv_cache=inp.kv_cache[inv],
+                page_table=new_pt.contiguous())
     c = run_step(p)
     assert torch.equal(out_a, c.out) and torch.equal(a.topk_idx, c.topk_idx)
     assert torch.equal(a.scores, c.scores)

@@ -28,6 +28,18 @@ def test_c0_shapes_tables_and_determinism():
     assert not torch.any((a.kv_code & 0x7F) == 0x7F)
 
 
+def test_packed_mla_cache_layout():
+    a = W.make("c0")
+    assert a.kv_cache.shape == (256, 64, 640) and a.kv_cache.dtype == torch.uint8
+    # codes are bytes 0..575, the fp32 scale bytes 576..579 (little-endian), pad 0x7F
+    raw = a.kv_cache.numpy()
+    assert np.array_equal(a.kv_code.numpy(), raw[..., :576])
+    sc = raw[..., 576:580].copy().view("<f4")[..., 0]
+    assert np.array_equal(a.kv_scale.numpy(), sc)
+    assert np.all(raw[..., 580:] == 0x7F)
+    assert np.all(sc > 0) and np.all(np.isfinite(sc))
+
+
 def test_row_geometry_of_mtp_and_prefill():
     c3 = W.Config("t3", batch=3, kv_lens=(100, 300, 260), rows_per_req=6, causal="mtp",
                   page_size=64, mla_heads=16)
