@@ -14,9 +14,9 @@ pool, 64 x 128 fp8 indexer, 32 MLA heads over 576-wide fp8 rows, top-2048.
 
 Timing: W untimed steps, then K steps between two device synchronisations,
 replayed from a HIP graph of one step (``--eager`` launches the five kernels
-directly instead).  A second, eager pass of K steps brackets every kernel
-with HIP events on the stream it runs on, for per-kernel durations and the
-roofline of the dominant kernel.  The oracle (fp64, CPU) is timed on a bounded
+directly instead).  Then every kernel is replayed back to back from a graph
+of 20 launches between two HIP events on the stream it runs on, for
+per-kernel durations and the roofline of the dominant kernel.  The oracle (fp64, CPU) is timed on a bounded
 sample of the same workload as a reported baseline.
 """
 
@@ -163,39 +163,63 @@ def main():
     ms = elapsed * 1e3 / args.steps
     dsa.check_status(step.status)
 
-    # Per-kernel durations: HIP events around each launch on the launch stream.
-    names = ["quantize_q", "index_scores", "topk", "sparse_mla", "lse_merge"]
-    evs = {n: [] for n in names}
+    # Per-kernel durations: each kernel launched 20 times back to back from a
+    # HIP graph, the graph replayed K/4 times on the launch stream between
+    # two HIP events (every launch reads the same inputs and rewrites the
+    # same outputs), averaged per launch.
     i = inp
-    for _ in range(args.steps):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        marks[0].record(stream)
-        dsa.quantize_q(i.q_idx, step.q_code, step.q_scale)
-        marks[1].record(stream)
-        dsa.index_scores(step.q_code, step.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table,
-                         i.kv_lens, i.row_req, i.row_vis, group_rows=step.group_rows,
-                         score_stride=step.score_stride, scores=step.scores, status=step.status)
-        marks[2].record(stream)
-        dsa.topk(step.scores, i.row_vis, i.top_k, step.index_splits, workspace=step.workspace,
-                 topk_idx=step.topk_idx, topk_count=step.topk_count, status=step.status)
-        marks[3].record(stream)
-        if step.attn_splits == 1:
-            dsa.sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
-                                  step.topk_idx, step.topk_count, 1, i.sm_scale, out=step.out,
-                                  out_lse=step.out_lse, status=step.status)
-            marks[4].record(stream)
-        else:
-            dsa.sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
-                                  step.topk_idx, step.topk_count, step.attn_splits, i.sm_scale,
-                                  part_o=step.part_o, part_lse=step.part_lse, status=step.status)
-            marks[4].record(stream)
-            dsa.lse_merge(step.part_o, step.part_lse, out=step.out, out_lse=step.out_lse)
-        marks[5].record(stream)
-        for j, n in enumerate(names):
-            evs[n].append((marks[j], marks[j + 1]))
+    launches = {
+        "quantize_q": lambda: dsa.quantize_q(i.q_idx, step.q_code, step.q_scale),
+        "index_scores": lambda: dsa.index_scores(
+            step.q_code, step.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
+            i.row_req, i.row_vis, group_rows=step.group_rows, score_stride=step.score_stride,
+            scores=step.scores, status=step.status),
+        "topk": lambda: dsa.topk(step.scores, i.row_vis, i.top_k, step.index_splits,
+                                 workspace=step.workspace, topk_idx=step.topk_idx,
+                                 topk_count=step.topk_count, status=step.status),
+    }
+    if step.attn_splits == 1:
+        launches["sparse_mla"] = lambda: dsa.sparse_mla_decode(
+            i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis, step.topk_idx,
+            step.topk_count, 1, i.sm_scale, out=step.out, out_lse=step.out_lse, status=step.status)
+    else:
+        launches["sparse_mla"] = lambda: dsa.sparse_mla_decode(
+            i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis, step.topk_idx,
+            step.topk_count, step.attn_splits, i.sm_scale, part_o=step.part_o,
+            part_lse=step.part_lse, status=step.status)
+        launches["lse_merge"] = lambda: dsa.lse_merge(step.part_o, step.part_lse, out=step.out,
+                                                      out_lse=step.out_lse)
+    kern_us = {}
+    reps = 20
+    for n, fn in launches.items():
+        g = None
+        if not args.eager:
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                fn()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    fn()
+            torch.cuda.synchronize()
+        n_iter = max(1, args.steps // 4)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_iter):
+            if g is not None:
+                g.replay()
+            else:
+                for _ in range(reps):
+                    fn()
+        e1.record(stream)
+        e1.synchronize()
+        kern_us[n] = 1e3 * e0.elapsed_time(e1) / (n_iter * reps)
     torch.cuda.synchronize()
     dsa.check_status(step.status)
-    kern_us = {n: 1e3 * sum(a.elapsed_time(b) for a, b in evs[n]) / len(evs[n]) for n in names}
 
     ab = algorithmic_bytes(inp)
     idx_us = kern_us["index_scores"]
