@@ -22,8 +22,8 @@ context parallel (DCP) for GLM-5 / DeepSeek-V3.2" (sgl-project/sglang PR
 * Page "DeepSeek V4 DSpark Internals" (pypto.ai), kernel mapping: block tables
   hold -1 past each request's span.
 
-The pages never print the formulas.  The readings taken here (the design doc lists
-them) are the plainest ones consistent with the configurations: indexer score
+The pages never print the formulas.  The readings taken here are the plainest
+ones consistent with the configurations: indexer score
 ``s_t = sum_h w_h * relu(q_h . k_t)`` with one 128-wide key per token shared by
 all heads; absorbed MLA with keys = the 576-wide latent+rope row and values =
 its first 512 entries; logits scaled by ``sm_scale``; everything decoded from
