@@ -132,8 +132,11 @@ size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits);
  * Motivation: the top 2048 of the whole sequence; Modifications, indexer
  * decode: local top-k per shard merged into the exact global top-k).
  * Row r's slots [0, row_vis[r]) are cut into n_splits contiguous ranges of
- * ceil(row_vis/n_splits); each keeps its top-min(top_k, len) candidates and
- * one merge keeps the top-k of their union.  n_splits == 1 selects directly.
+ * ceil(row_vis/n_splits) rounded up to a multiple of 4 (the last ranges may
+ * be short or empty); each keeps its top-min(top_k, len) candidates and one
+ * merge keeps the top-k of their union.  n_splits == 1 selects directly.
+ * Score rows whose start is 16-byte aligned (score_stride a multiple of 4)
+ * are read in 16-byte loads.
  *   scores [n_rows, score_stride] f32 (only [0, row_vis) is read)
  *   topk_idx [n_rows, top_k] i32 out: selected slots in ascending order, then -1
  *   topk_count [n_rows] i32 out: min(top_k, row_vis)

@@ -25,8 +25,9 @@
 //      finds the rank k - (keys above) among them.
 // If the bracket misses or holds more keys than LDS has room for (heavy
 // ties), the same radix select runs over all keys instead.
-// Emission: per-thread counts and two workgroup scans give every selected
-// position its output rank, so the output comes out in list order.  Keys
+// Emission: per-thread counts and one workgroup scan give every selected
+// position its output rank; positions go to LDS at their ranks and out to
+// global memory in one coalesced pass, in list order.  Keys
 // above `thr` are taken; keys equal to `thr` are taken in list order until
 // the count is reached, which keeps the lowest slots among ties.
 #include "device_common.h"
@@ -49,7 +50,7 @@ struct TopkSmem {
         uint32_t stage[kTopkMaxList];
         struct {
             uint32_t hist[kBins0];
-            uint32_t cand_key[kCandCap];
+            uint32_t cand_key[kCandCap + kWave];   // + one dummy word per lane
         } sel;
     } u;
     uint32_t scan[kThreads / kWave + 1];
@@ -61,12 +62,18 @@ struct TopkSmem {
 
 __device__ __forceinline__ uint32_t bin0(uint32_t key) { return key >> 20; }
 
+// Keys per thread for a list of n: a multiple of 4 (whole 16-byte chunks),
+// at most kPer.
+__device__ __forceinline__ int keys_per_thread(int n) {
+    return ((n + 4 * kThreads - 1) / (4 * kThreads)) * 4;
+}
+
 // Digit d (of NB bins, scanned from the largest) whose bin holds the kk-th
 // largest counted key: s.sel_digit = d, s.sel_need = kk minus the keys in
 // larger bins.  Thread t owns the NB/kThreads bins just below
 // NB - t * (NB / kThreads).
 template <int NB>
-__device__ void find_digit(TopkSmem& s, uint32_t kk) {
+__device__ __forceinline__ uint32_t find_digit(TopkSmem& s, uint32_t kk) {
     constexpr int PER = NB / kThreads;
     const int tid = threadIdx.x;
     uint32_t c[PER];
@@ -87,9 +94,10 @@ __device__ void find_digit(TopkSmem& s, uint32_t kk) {
         above += c[j];
     }
     __syncthreads();
+    return total;
 }
 
-__device__ void clear_hist(TopkSmem& s, int nb) {
+__device__ __forceinline__ void clear_hist(TopkSmem& s, int nb) {
     for (int i = threadIdx.x; i < nb; i += kThreads) s.u.sel.hist[i] = 0;
     __syncthreads();
 }
@@ -98,7 +106,8 @@ __device__ void clear_hist(TopkSmem& s, int nb) {
 // among the keys get(i, &key) yields for i in [0, M) on each thread, by
 // three histogram passes of 12, 10 and 10 bits.
 template <int M, typename Get>
-__device__ void radix_select(TopkSmem& s, uint32_t kk, Get get, uint32_t* thr_out, uint32_t* need_out) {
+__device__ __forceinline__ void radix_select(TopkSmem& s, uint32_t kk, Get get, uint32_t* thr_out,
+                                             uint32_t* need_out) {
     clear_hist(s, kBins0);
 #pragma unroll
     for (int i = 0; i < M; ++i) {
@@ -108,8 +117,8 @@ __device__ void radix_select(TopkSmem& s, uint32_t kk, Get get, uint32_t* thr_ou
     __syncthreads();
     find_digit<kBins0>(s, kk);
     uint32_t prefix = s.sel_digit << 20;
-    uint32_t mask = 0xFFF00000u;
     kk = s.sel_need;
+    uint32_t mask = 0xFFF00000u;
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
         const int shift = pass == 0 ? 10 : 0;
@@ -133,10 +142,10 @@ __device__ void radix_select(TopkSmem& s, uint32_t kk, Get get, uint32_t* thr_ou
 
 // k-th largest (1 <= k < n) of the n keys, thread t holding `mine` of them
 // in key[0, mine).
-__device__ void select_kth(TopkSmem& s, const uint32_t (&key)[kPer], int mine, int n, int k,
+__device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kPer], int mine, int n, int k,
                            uint32_t* thr_out, uint32_t* need_out) {
     const int tid = threadIdx.x;
-    const int per = (n + kThreads - 1) / kThreads;
+    const int per = keys_per_thread(n);
     const int samples = (n + per - 1) / per;        // threads holding a key
     // 1. Sample histogram and the bracket of bins around rank k.
     clear_hist(s, kBins0);
@@ -157,27 +166,37 @@ __device__ void select_kth(TopkSmem& s, const uint32_t (&key)[kPer], int mine, i
         b_lo = s.sel_digit;
     }
     // 2. Count keys above the bracket; compact the keys inside it in order.
+    // Positions past a thread's share hold key 0 (bin 0); bin 0 is kept out
+    // of the bracket, so they are never counted, and a real key of bin 0 (a
+    // negative NaN pattern) only sends the selection to the fallback.
+    b_lo = max(b_lo, 1u);
     uint32_t above = 0, inside = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        if (i < mine) {
-            const uint32_t b = bin0(key[i]);
-            above += b > b_hi;
-            inside += (b >= b_lo && b <= b_hi);
-        }
+        const uint32_t b = bin0(key[i]);
+        above += b > b_hi;
+        inside += b >= b_lo && b <= b_hi;
     }
-    uint32_t tot_above, tot_inside;
-    block_exclusive_scan<kThreads>(above, s.scan, &tot_above);
-    uint32_t at = block_exclusive_scan<kThreads>(inside, s.scan, &tot_inside);
+    // One scan of (above, inside) in 16-bit halves (each total <= 32768).
+    uint32_t tot;
+    const uint32_t both = block_exclusive_scan<kThreads>((above << 16) | inside, s.scan, &tot);
+    const uint32_t tot_above = tot >> 16, tot_inside = tot & 0xFFFFu;
+    uint32_t at = both & 0xFFFFu;
     const bool fast = tot_above < (uint32_t)k && tot_above + tot_inside >= (uint32_t)k &&
                       tot_inside <= (uint32_t)kCandCap;
     if (fast) {
+        // Branch-free: a key outside the bracket goes to the lane's dummy word.
+        // The bounds are re-pinned so the compiler recomputes each key's test
+        // here instead of keeping 32 of them live across the scan.
+        pin(b_lo);
+        pin(b_hi);
+        const uint32_t dummy = (uint32_t)kCandCap + (threadIdx.x & (kWave - 1));
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            if (i < mine) {
-                const uint32_t b = bin0(key[i]);
-                if (b >= b_lo && b <= b_hi) s.u.sel.cand_key[at++] = key[i];
-            }
+            const uint32_t b = bin0(key[i]);
+            const bool in = b >= b_lo && b <= b_hi;
+            s.u.sel.cand_key[in ? at : dummy] = key[i];
+            at += in;
         }
         __syncthreads();
         // 3. Exact rank among the compacted keys (4 per thread).
@@ -203,34 +222,125 @@ __device__ void select_kth(TopkSmem& s, const uint32_t (&key)[kPer], int mine, i
         thr_out, need_out);
 }
 
-// Emit the selected keys in list order: emit(rank, i) for the thread's key i.
-template <typename Emit>
-__device__ void ordered_emit(TopkSmem& s, const uint32_t (&key)[kPer], int mine, uint32_t thr,
-                             uint32_t need_eq, Emit emit) {
+// LDS words of the emitted list positions and keys (each k + one dummy per
+// lane), inside the staging buffer, which is free once the keys are in
+// registers.
+constexpr int kEmitPos = 0;
+constexpr int kEmitKey = kTopkMaxK + kWave;
+static_assert(2 * (kTopkMaxK + kWave) <= kTopkMaxList, "emission buffers fit the staging buffer");
+
+// Selected keys in list order: a key is taken if it is above `thr`, or equal
+// to it and among the first need_eq equal keys.  After one packed scan each
+// thread's taken keys have consecutive ranks; their list positions (base +
+// i) and keys are written to LDS at those ranks without branches (a key not
+// taken goes to the lane's dummy word), for a coalesced copy out afterwards
+// (after a barrier, by the caller).
+__device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[kPer], int base,
+                                            uint32_t thr, uint32_t need_eq, int k) {
+    // Positions past the thread's share hold key 0, which is never above a
+    // threshold; equal keys are only counted for a nonzero threshold (a zero
+    // one means NaN scores, an error the caller is told about).
+    const uint32_t eq_key = thr != 0u ? thr : 0xFFFFFFFFu;
+    const bool eq_ok = thr != 0u;
     uint32_t eq = 0, gt = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        if (i < mine) {
-            eq += key[i] == thr;
-            gt += key[i] > thr;
-        }
+        eq += key[i] == eq_key && eq_ok;
+        gt += key[i] > thr;
     }
+    // One scan of (gt, eq) packed in 16-bit halves (each total <= 32768):
+    // the equal keys taken before this thread are min(eq_before, need_eq).
     uint32_t tot;
-    const uint32_t eq_before = block_exclusive_scan<kThreads>(eq, s.scan, &tot);
-    const uint32_t take_eq = min(eq, need_eq > eq_before ? need_eq - eq_before : 0u);
-    uint32_t rank = block_exclusive_scan<kThreads>(gt + take_eq, s.scan, &tot);
-    uint32_t eq_left = take_eq;
+    const uint32_t both = block_exclusive_scan<kThreads>((gt << 16) | eq, s.scan, &tot);
+    const uint32_t eq_before = both & 0xFFFFu;
+    uint32_t eq_left = min(eq, need_eq > eq_before ? need_eq - eq_before : 0u);
+    uint32_t rank = (both >> 16) + min(eq_before, need_eq);
+    const uint32_t dummy = (uint32_t)k + (threadIdx.x & (kWave - 1));
+    uint32_t thr2 = thr, eq_key2 = eq_key;   // recompute the per-key tests after the scan
+    pin(thr2);
+    pin(eq_key2);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        if (i < mine) {
-            bool take = key[i] > thr;
-            if (key[i] == thr && eq_left > 0) {
-                take = true;
-                --eq_left;
-            }
-            if (take) emit((int)rank++, i);
-        }
+        const bool is_eq = key[i] == eq_key2 && eq_ok;
+        const bool take = key[i] > thr2 || (is_eq && eq_left > 0);
+        eq_left -= (is_eq && take) ? 1u : 0u;
+        const uint32_t slot = take ? min(rank, (uint32_t)k - 1u) : dummy;
+        s.u.stage[kEmitPos + slot] = (uint32_t)(base + i);
+        s.u.stage[kEmitKey + slot] = key[i];
+        rank += take;
     }
+}
+
+// Direct emission (one split): the same selection as emit_to_lds, but each
+// thread walks only the set bits of its taken-key mask and writes the list
+// positions straight to `out` at their ranks.
+__device__ __forceinline__ void emit_direct(TopkSmem& s, const uint32_t (&key)[kPer], int base, uint32_t thr,
+                                            uint32_t need_eq, int k, int32_t* out, int lo) {
+    const uint32_t eq_key = thr != 0u ? thr : 0xFFFFFFFFu;
+    const bool eq_ok = thr != 0u;
+    uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        gtm |= (key[i] > thr ? 1u : 0u) << i;
+        eqm |= (key[i] == eq_key && eq_ok ? 1u : 0u) << i;
+    }
+    uint32_t tot;
+    const uint32_t both = block_exclusive_scan<kThreads>(((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm),
+                                                          s.scan, &tot);
+    const uint32_t eq_before = both & 0xFFFFu;
+    uint32_t take_eq = min((uint32_t)__popc(eqm), need_eq > eq_before ? need_eq - eq_before : 0u);
+    uint32_t tm = gtm;
+    for (uint32_t em = eqm; take_eq > 0; --take_eq) {   // the lowest take_eq equal keys
+        tm |= em & (0u - em);
+        em &= em - 1u;
+    }
+    uint32_t rank = (both >> 16) + min(eq_before, need_eq);
+    while (tm != 0u) {
+        const int i = __ffs(tm) - 1;
+        tm &= tm - 1u;
+        if (rank < (uint32_t)k) out[rank] = lo + base + i;
+        ++rank;
+    }
+}
+
+// Chunk swizzle of the vector staging buffer: chunk c (16 bytes) lives at
+// c ^ ((c / 32) % 8).  32 consecutive chunks (a coalesced write) keep 32
+// distinct 16-byte bank slots, and so do the chunks 8t + m (or 4t + m) that
+// 32 consecutive threads read for their own contiguous keys.
+__device__ __forceinline__ int chunk_swz(int c) { return c ^ ((c >> 5) & 7); }
+
+// Keys of list positions [base, base + mine) into registers from a 16-byte
+// aligned list of floats, in 16-byte loads (coalesced across lanes, all
+// issued before any use) and 16-byte LDS accesses.  Chunks past the list
+// reload its last chunk and are never read back; positions past n in the
+// last chunk are masked.  Sets `nan` if a listed score is NaN.
+__device__ __forceinline__ void load_list_vec(TopkSmem& s, const float* src, int n, int base, int mine,
+                                              uint32_t (&key)[kPer], bool& nan) {
+    constexpr int kChunks = kTopkMaxList / 4;
+    const int nch = (n + 3) >> 2;
+    float4 v[kPer / 4];
+#pragma unroll
+    for (int u = 0; u < kPer / 4; ++u)
+        v[u] = reinterpret_cast<const float4*>(src)[min(u * kThreads + (int)threadIdx.x, nch - 1)];
+    uint4* stage4 = reinterpret_cast<uint4*>(s.u.stage);
+#pragma unroll
+    for (int u = 0; u < kPer / 4; ++u) {
+        const int q = u * kThreads + (int)threadIdx.x;
+        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nan |= (f[j] != f[j]) && 4 * q + j < n;
+        stage4[chunk_swz(q)] = uint4{monotone_key(f[0]), monotone_key(f[1]), monotone_key(f[2]), monotone_key(f[3])};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kPer / 4; ++m) {
+        const uint4 x = stage4[chunk_swz(min((base >> 2) + m, kChunks - 1))];
+        key[4 * m + 0] = 4 * m + 0 < mine ? x.x : 0u;
+        key[4 * m + 1] = 4 * m + 1 < mine ? x.y : 0u;
+        key[4 * m + 2] = 4 * m + 2 < mine ? x.z : 0u;
+        key[4 * m + 3] = 4 * m + 3 < mine ? x.w : 0u;
+    }
+    __syncthreads();
 }
 
 // Word index in the staging buffer of list element i: 16-byte chunk c =
@@ -246,25 +356,27 @@ __device__ __forceinline__ int stage_index(int i) {
 // gives the key of list position i; it is called with consecutive i across
 // lanes (coalesced) and every load of a thread is issued before any use.
 template <typename Get>
-__device__ void load_list(TopkSmem& s, int n, int base, int mine, uint32_t (&key)[kPer], Get get) {
+__device__ __forceinline__ void load_list(TopkSmem& s, int n, int base, int mine, uint32_t (&key)[kPer], Get get) {
+    // Positions past n load position n - 1 again and are never read back;
+    // every index stays inside the 32768-word staging buffer.
     uint32_t v[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
         const int i = u * kThreads + (int)threadIdx.x;
-        v[u] = i < n ? get(i) : 0u;
+        v[u] = get(min(i, n - 1));
     }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-        const int i = u * kThreads + (int)threadIdx.x;
-        if (i < n) s.u.stage[stage_index(i)] = v[u];
-    }
+    for (int u = 0; u < kPer; ++u) s.u.stage[stage_index(u * kThreads + (int)threadIdx.x)] = v[u];
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) key[i] = i < mine ? s.u.stage[stage_index(base + i)] : 0u;
+    for (int i = 0; i < kPer; ++i) {
+        const uint32_t x = s.u.stage[stage_index(min(base + i, kTopkMaxList - 1))];
+        key[i] = i < mine ? x : 0u;
+    }
     __syncthreads();
 }
 
-__device__ int checked_vis(const TopkArgs& a, int r) {
+__device__ __forceinline__ int checked_vis(const TopkArgs& a, int r) {
     const int v = a.row_vis[r];
     if (v < 0 || v > a.score_stride) {
         if (threadIdx.x == 0) flag(a.status, DSA_DEV_ROW_RANGE);
@@ -273,7 +385,7 @@ __device__ int checked_vis(const TopkArgs& a, int r) {
     return v;
 }
 
-__device__ void pad_tail(int32_t* out, int from, int k) {
+__device__ __forceinline__ void pad_tail(int32_t* out, int from, int k) {
     for (int i = from + threadIdx.x; i < k; i += kThreads) out[i] = -1;
 }
 
@@ -283,7 +395,8 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
     const int r = blockIdx.y;
     const int j = blockIdx.x;
     const int v = checked_vis(a, r);
-    const int c = (v + a.n_splits - 1) / a.n_splits;
+    // Split length ceil(v / n_splits), rounded up to whole 16-byte chunks.
+    const int c = (((v + a.n_splits - 1) / a.n_splits) + 3) & ~3;
     const int lo = min(v, j * c);
     const int hi = min(v, lo + c);
     const int n = hi - lo;
@@ -315,32 +428,34 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
         }
         return;
     }
-    const int per = (n + kThreads - 1) / kThreads;
+    const int per = keys_per_thread(n);
     const int base = threadIdx.x * per;
     const int mine = max(0, min(per, n - base));
     uint32_t key[kPer];
     bool nan = false;
-    load_list(s, n, base, mine, key, [&](int i) {
-        const float f = src[i];
-        nan |= (f != f);
-        return monotone_key(f);
-    });
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+        load_list_vec(s, src, n, base, mine, key, nan);
+    } else {
+        load_list(s, n, base, mine, key, [&](int i) {
+            const float f = src[i];
+            nan |= (f != f);
+            return monotone_key(f);
+        });
+    }
     if (__ballot(nan) != 0ull && (threadIdx.x & 63) == 0) flag(a.status, DSA_DEV_NAN);
     uint32_t thr, need;
     select_kth(s, key, mine, n, k, &thr, &need);
-    // A right selection never produces rank >= k; the guard keeps a wrong
-    // one from writing past the row.
+    // A right selection takes exactly k keys; ranks are clamped below k so
+    // that a wrong one could not write past the buffers.
     if (direct) {
-        ordered_emit(s, key, mine, thr, need, [&](int rank, int i) {
-            if (rank < k) out_idx[rank] = lo + base + i;
-        });
+        emit_direct(s, key, base, thr, need, k, out_idx, lo);
     } else {
-        ordered_emit(s, key, mine, thr, need, [&](int rank, int i) {
-            if (rank < k) {
-                out_idx[rank] = lo + base + i;
-                out_key[rank] = key[i];
-            }
-        });
+        emit_to_lds(s, key, base, thr, need, k);
+        __syncthreads();
+        for (int i = threadIdx.x; i < k; i += kThreads) {
+            out_idx[i] = lo + (int)s.u.stage[kEmitPos + i];
+            out_key[i] = s.u.stage[kEmitKey + i];
+        }
     }
 }
 
@@ -379,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
         const int j = split_of(s, ns, pos);
         return (size_t)j * k + (pos - s.offs[j]);
     };
-    const int per = (n + kThreads - 1) / kThreads;
+    const int per = keys_per_thread(n);
     const int base = threadIdx.x * per;
     const int mine = max(0, min(per, n - base));
     if (n <= k) {
@@ -397,9 +512,9 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     load_list(s, n, base, mine, key, [&](int i) { return ckey[entry(i)]; });
     uint32_t thr, need;
     select_kth(s, key, mine, n, k, &thr, &need);
-    ordered_emit(s, key, mine, thr, need, [&](int rank, int i) {
-        if (rank < k) out_idx[rank] = cslot[entry(base + i)];
-    });
+    emit_to_lds(s, key, base, thr, need, k);
+    __syncthreads();
+    for (int i = threadIdx.x; i < k; i += kThreads) out_idx[i] = cslot[entry((int)s.u.stage[kEmitPos + i])];
 }
 
 }  // namespace

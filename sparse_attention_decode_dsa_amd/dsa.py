@@ -247,7 +247,8 @@ class DecodeStep:
         r = inp.n_rows
         h = inp.mla_heads
         k = inp.top_k
-        self.score_stride = score_stride or max(1, inp.max_vis())
+        # Rows start 16-byte aligned (the top-k then reads them in 16-byte loads).
+        self.score_stride = score_stride or max(64, (inp.max_vis() + 63) // 64 * 64)
         self.q_code = torch.empty((r, 64, 128), dtype=torch.uint8, device=dev)
         self.q_scale = torch.empty((r, 64), dtype=torch.float32, device=dev)
         self.scores = torch.empty((r, self.score_stride), dtype=torch.float32, device=dev)
