@@ -191,6 +191,48 @@ def test_bulk_decode_sampled_rows(name):
     mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
 
 
+# ------------------------------------------------------------------ long context, MTP verify, prefill
+
+def test_long_context_planted_sampled_rows():
+    """8 requests up to 131072 tokens, 16 index splits, 32 attention splits,
+    4 planted slots per request (both caches' scales x8)."""
+    inp = W.make("c2", device="cuda")
+    say(f"c2: B={inp.n_rows} vis={inp.row_vis.tolist()}")
+    step = run_step(inp)
+    idx = step.topk_idx.cpu().numpy()
+    hit = sum(len(set(inp.planted_slots[b].tolist()) & set(idx[b].tolist())) for b in range(inp.n_rows))
+    say(f"c2: {hit} of {inp.planted_slots.numel()} planted slots selected")
+    ref, sub, swapped = compare_step(inp, step, [0, 3, 6], max_swap_rows=1)
+    say(f"c2: swapped {swapped}")
+    mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
+
+
+def test_mtp_verify_grouped_rows():
+    """32 requests x 6 causal rows scored as groups of 6 against one key
+    stream; sampled requests 0 and 31 (12 rows)."""
+    inp = W.make("c3", device="cuda")
+    say(f"c3: R={inp.n_rows} group_rows={inp.cfg.group_rows}")
+    step = run_step(inp)
+    rows = list(range(0, 6)) + list(range(inp.n_rows - 6, inp.n_rows))
+    ref, sub, swapped = compare_step(inp, step, rows, max_swap_rows=2)
+    say(f"c3: swapped {swapped}")
+    mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
+
+
+def test_long_prefix_prefill_sampled_rows():
+    """4096 prefill rows after a 65536-token prefix, groups of 8 rows,
+    4 index splits, one attention split; sampled rows across the range."""
+    inp = W.make("c4", device="cuda")
+    say(f"c4: R={inp.n_rows} vis {int(inp.row_vis.min())}..{int(inp.row_vis.max())}")
+    step = run_step(inp)
+    cnt = step.topk_count.cpu().numpy()
+    assert np.all(cnt == np.minimum(inp.top_k, inp.row_vis.cpu().numpy()))
+    rows = [0, 1, 7, 8, 2047, 4095]
+    ref, sub, swapped = compare_step(inp, step, rows, max_swap_rows=1)
+    say(f"c4: swapped {swapped}")
+    mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
+
+
 # ------------------------------------------------------------------ properties
 
 def test_page_permutation_and_run_to_run_determinism():
