@@ -16,8 +16,11 @@
 // two 16-byte loads of a wavefront then reads one contiguous 64-byte half of
 // 16 consecutive 128-byte key rows.
 //
-// Work split: a workgroup (4 wavefronts) owns a chunk of kChunk tokens of a
+// Work split: a workgroup (4 wavefronts) owns a chunk of a.chunk tokens of a
 // group of G rows of one request; wavefronts take 64-token groups in turn.
+// The chunk (a multiple of 256, at most kMaxChunk) is picked at launch so that
+// the grid is about two workgroups per compute unit, all resident at once: a
+// second, partial round of workgroups would run with most of the chip idle.
 // With G > 1 (MTP verify, prefill) the keys of a 64-token group are loaded
 // once and reused for every row of the group, whose queries sit in LDS.
 //
@@ -31,10 +34,11 @@ namespace dsa {
 
 namespace {
 
-constexpr int kChunk = 2048;    // tokens per workgroup
+constexpr int kMaxChunk = 8192;  // most tokens per workgroup
+constexpr int kMinChunk = 1024;
 constexpr int kQStride = 144;   // LDS bytes per query head row (128 + 16 pad: conflict-free b128 reads)
 
-constexpr int kMaxChunkPages = kChunk / 16;  // pages of one chunk at the smallest page size
+constexpr int kMaxChunkPages = kMaxChunk / 16;  // pages of one chunk at the smallest page size
 
 __device__ __forceinline__ v8i load_q_operand(const uint8_t* head_row, int g) {
     const uint4 lo = *reinterpret_cast<const uint4*>(head_row + 16 * g);
@@ -46,26 +50,50 @@ __device__ __forceinline__ v8i load_q_operand(const uint8_t* head_row, int g) {
 }
 
 // The keys of one 64-token group in MFMA B layout: block j (tokens
-// 16j..16j+15) in b[j]; lane l holds the scale of token l of the group.
+// 16j..16j+15) in b[j]; lane l holds the scale of token l of the group and
+// whether that token is scored at all (inside the span, on a valid page).
 struct KeyGroup {
     v8i b[4];
     float scale;
+    bool ok;
 };
 
-// Score of this lane's token column (lane % 16) of one 16-token block for
-// one row: 4 MFMAs over the head blocks, ReLU-weighted head sum.
-__device__ __forceinline__ float block_dot(const v8i (&qa)[4], const float (&wq)[4][4], const v8i& kb) {
-    float part = 0.0f;
+// max(x, 0) as one integer max on the bit pattern: every negative float
+// (sign bit set) is a negative int32 and becomes +0, every other one is kept.
+// (fmaxf costs a second, NaN-quieting instruction.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Scores of one 64-token group for one row, before the key scale: lane l
+// gets the ReLU-weighted head sum of token l.  All 16 MFMAs (4 token blocks
+// x 4 head blocks) are issued before any result is used.  Lane (n, g) of
+// block j holds heads 16hb + 4g + i of token 16j + n; p[j] is its share of
+// the head sum, and a transpose-reduce over the four lane rows gives row g
+// the total of block g: two 32-lane swaps pair rows {0,2} and {1,3} of two
+// blocks at once, one 16-lane swap then folds rows 0 and 1.
+__device__ __forceinline__ float group_dot(const v8i (&qa)[4], const float (&wq)[4][4], const v8i (&kb)[4]) {
+    v4f acc[4][4];
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = mfma_fp8_16x16x128(qa[hb], kb, acc);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part += wq[hb][i] * fmaxf(acc[i], 0.0f);
+        for (int hb = 0; hb < 4; ++hb) acc[j][hb] = mfma_fp8_16x16x128(qa[hb], kb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float t = 0.0f;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t = fmaf(wq[hb][i], relu(acc[j][hb][i]), t);
+        p[j] = t;
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    return part;
+    // After the 32-lane swaps u (v) holds block 0 (1) in rows 0-1 and block
+    // 2 (3) in rows 2-3, each as the sum of two rows.
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+    const float u = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+    const float v = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+    const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+    return __uint_as_float(w[0]) + __uint_as_float(w[1]);
 }
 
 template <int G>
@@ -75,8 +103,8 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     const int n = lane & 15;
     const int g = lane >> 4;
     const int r0 = blockIdx.y * G;
-    const int t0 = blockIdx.x * kChunk;
-    const int t_end = min(t0 + kChunk, a.score_stride);
+    const int t0 = blockIdx.x * a.chunk;
+    const int t_end = min(t0 + a.chunk, a.score_stride);
 
     __shared__ int s_req[G];
     __shared__ int s_vis[G];
@@ -167,9 +195,9 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
 
     // Loads of the group starting at token tg, branch-free: a block past
     // vmax or on an invalid page reads row n of page 0 instead (always
-    // inside the cache) and is masked out of the scores later.  Keeping
-    // every path's loads identical lets the compiler wait for exactly the
-    // group it needs.
+    // inside the cache) and its tokens are masked out of the scores.
+    // Keeping every path's loads identical lets the compiler wait for
+    // exactly the group it needs.
     auto load_group = [&](int tg, KeyGroup& kg) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -180,43 +208,30 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
         }
         const int t = tg + lane;
         const int page = t < vmax ? s_page[(t >> a.log2_page) - p0] : -1;
+        kg.ok = page >= 0;
         kg.scale = a.k_scale[page >= 0 ? (size_t)page * a.page_size + (t & pmask) : 0];
     };
 
     // Scores of the group at tg for every row of the group.
     auto process = [&](const KeyGroup& kg, int tg) {
-        bool live[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int tb = tg + 16 * j;
-            live[j] = tb < vmax && s_page[(tb >> a.log2_page) - p0] >= 0;
-        }
-        // Scale of this lane's token column in block j is held by lane 16j+n.
-        float ks[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ks[j] = __shfl(kg.scale, 16 * j + n);
+        const int t = tg + lane;
 #pragma unroll 1
         for (int rr = 0; rr < G; ++rr) {
             const int r = r0 + rr;
             const int v = s_vis[rr];
-            if constexpr (G > 1) {
-#pragma unroll
-                for (int hb = 0; hb < 4; ++hb) {
-                    qa[hb] = load_q_operand(s_q + (rr * 64 + hb * 16 + n) * kQStride, g);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) wq[hb][i] = s_wq[rr * 64 + hb * 16 + 4 * g + i];
-                }
-            }
             float mine = -INFINITY;
+            if (tg < v) {
+                if constexpr (G > 1) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tb = tg + 16 * j;
-                if (live[j] && tb < v) {
-                    const float sc = block_dot(qa, wq, kg.b[j]) * ks[j];
-                    if (g == j && tb + n < v) mine = sc;
+                    for (int hb = 0; hb < 4; ++hb) {
+                        qa[hb] = load_q_operand(s_q + (rr * 64 + hb * 16 + n) * kQStride, g);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) wq[hb][i] = s_wq[rr * 64 + hb * 16 + 4 * g + i];
+                    }
                 }
+                const float sc = group_dot(qa, wq, kg.b) * kg.scale;
+                if (kg.ok && t < v) mine = sc;
             }
-            const int t = tg + lane;
             if (t < t_end) a.scores[(size_t)r * a.score_stride + t] = mine;
         }
     };
@@ -251,9 +266,18 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     }
 }
 
+// Target grid size: two workgroups per compute unit (256 units).  Registers
+// would allow three at G = 1, but two larger chunks each measure faster.
+constexpr int kResidentWgs = 512;
+
 template <int G>
-hipError_t launch_g(const IndexArgs& a, hipStream_t stream) {
-    dim3 grid((a.score_stride + kChunk - 1) / kChunk, a.n_rows / G);
+hipError_t launch_g(IndexArgs a, hipStream_t stream) {
+    const int groups = a.n_rows / G;
+    const int per_group = max(1, kResidentWgs / groups);
+    int chunk = (a.score_stride + per_group - 1) / per_group;
+    chunk = min(kMaxChunk, max(kMinChunk, (chunk + 255) & ~255));
+    a.chunk = chunk;
+    dim3 grid((a.score_stride + chunk - 1) / chunk, groups);
     index_scores_kernel<G><<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
 }

@@ -22,6 +22,7 @@ struct IndexArgs {
     float* scores;
     int32_t score_stride;
     int32_t* status;
+    int32_t chunk;   // tokens per workgroup, set by the launcher
 };
 
 struct TopkArgs {
