@@ -170,6 +170,7 @@ def main():
     i = inp
     launches = {
         "quantize_q": lambda: dsa.quantize_q(i.q_idx, step.q_code, step.q_scale),
+        "quantize_mla_q": lambda: dsa.quantize_mla_q(i.q_mla, step.q_terms, step.q_mla_scale),
         "index_scores": lambda: dsa.index_scores(
             step.q_code, step.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
             i.row_req, i.row_vis, group_rows=step.group_rows, score_stride=step.score_stride,
@@ -180,12 +181,12 @@ def main():
     }
     if step.attn_splits == 1:
         launches["sparse_mla"] = lambda: dsa.sparse_mla_decode(
-            i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis, step.topk_idx,
-            step.topk_count, 1, i.sm_scale, out=step.out, out_lse=step.out_lse, status=step.status)
+            step.q_terms, step.q_mla_scale, i.kv_cache, i.page_table, i.row_req, i.row_vis,
+            step.topk_idx, step.topk_count, 1, i.sm_scale, out=step.out, out_lse=step.out_lse, status=step.status)
     else:
         launches["sparse_mla"] = lambda: dsa.sparse_mla_decode(
-            i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis, step.topk_idx,
-            step.topk_count, step.attn_splits, i.sm_scale, part_o=step.part_o,
+            step.q_terms, step.q_mla_scale, i.kv_cache, i.page_table, i.row_req, i.row_vis,
+            step.topk_idx, step.topk_count, step.attn_splits, i.sm_scale, part_o=step.part_o,
             part_lse=step.part_lse, status=step.status)
         launches["lse_merge"] = lambda: dsa.lse_merge(step.part_o, step.part_lse, out=step.out,
                                                       out_lse=step.out_lse)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -94,6 +94,26 @@ const char* dsa_status_string(int status);
  */
 int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
                    uint8_t* q_code, float* q_scale, hipStream_t stream);
+
+/*
+ * dsa_quantize_mla_q -- input side of the sparse MLA (subject page,
+ * Modifications, sparse decode: the attention reads fp8 KV rows).  The bf16
+ * absorbed query of every (row, head) is split into two fp8 E4M3FN terms and
+ * one power-of-two scale, q = scale * (dec(hi) + dec(lo) / 16), with
+ * scale = 2^ceil(log2(amax / 448)) (1 for an all-zero head),
+ * hi = round-to-nearest-even(q / scale) and
+ * lo = round-to-nearest-even(16 * (q / scale - dec(hi))).
+ * Every bf16 element with |q / scale| >= 2^-6 is reproduced exactly (after
+ * scaling the head's largest magnitude is above 224, so these are all elements
+ * above about 2^-14 of it); smaller ones are off by at most 2^-14 * scale.
+ * dsa_sparse_mla_decode computes the logits from these terms.
+ *   q_bf16   [n_rows, n_heads, head_dim] bf16 bit patterns
+ *   q_terms  [n_rows, n_heads, 2, head_dim] uint8 out: hi codes, then lo codes
+ *   q_scale  [n_rows, n_heads] float32 out
+ * Supported: head_dim == 576, n_heads >= 1.  n_rows == 0 enqueues nothing.
+ */
+int dsa_quantize_mla_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
+                       uint8_t* q_terms, float* q_scale, hipStream_t stream);
 
 /*
  * dsa_index_scores -- fp8 lightning-indexer scores (subject page,
@@ -158,10 +178,11 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
  * top_k, so a split's range is known before the count is read; when
  * n < top_k the last splits may be empty):
  *   x_t   = dec(codes of row t) * scale of row t       (576 wide)
- *   l_t   = sm_scale * (q[r][h] . x_t)
+ *   l_t   = sm_scale * (q[r][h] . x_t),  q = q_scale * (dec(hi) + dec(lo) / 16)
  *   o_s   = sum_t e^{l_t - m} x_t[0:512] / sum_t e^{l_t - m},  lse_s = m + ln sum_t e^{l_t - m}
  * Empty split: o_s = 0, lse_s = -inf.
- *   q [n_rows, n_heads, 576] bf16 bit patterns
+ *   q_terms [n_rows, n_heads, 2, 576] uint8, q_scale [n_rows, n_heads] f32
+ *     (the query as dsa_quantize_mla_q prepares it)
  *   kv_cache [num_pages, page_size, 640] uint8 (layout above)
  *   page_table [batch, max_pages] i32, row_req / row_vis [n_rows] i32
  *   topk_idx [n_rows, top_k] i32, topk_count [n_rows] i32
@@ -173,7 +194,8 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
  * Supported: n_heads in {16, 32}, page_size a power of two in [16, 1024],
  * 1 <= n_splits <= 64, 1 <= top_k <= 8192.
  */
-int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
+int dsa_sparse_mla_decode(const uint8_t* q_terms, const float* q_scale, const uint8_t* kv_cache,
+                          const int32_t* page_table,
                           const int32_t* row_req, const int32_t* row_vis, const int32_t* topk_idx,
                           const int32_t* topk_count, int32_t n_rows,
                           int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,

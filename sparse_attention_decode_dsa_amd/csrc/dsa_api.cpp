@@ -66,6 +66,16 @@ int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int3
     return launch_status(dsa::launch_quantize_q(q_bf16, n_rows * n_heads, q_code, q_scale, stream));
 }
 
+int dsa_quantize_mla_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
+                       uint8_t* q_terms, float* q_scale, hipStream_t stream) {
+    if (n_rows < 0 || n_heads < 1 || head_dim < 1) return DSA_ERR_SHAPE;
+    if (head_dim != 576) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)n_rows * n_heads > INT32_MAX / 4) return DSA_ERR_SHAPE;
+    if (n_rows == 0) return DSA_OK;
+    if (!q_bf16 || !q_terms || !q_scale) return DSA_ERR_NULL;
+    return launch_status(dsa::launch_quantize_mla_q(q_bf16, n_rows * n_heads, q_terms, q_scale, stream));
+}
+
 int dsa_index_scores(const uint8_t* q_code, const float* q_scale, const float* head_w,
                      const uint8_t* k_code, const float* k_scale, const int32_t* page_table,
                      const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,
@@ -125,7 +135,8 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
     return launch_status(dsa::launch_topk(a, stream));
 }
 
-int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
+int dsa_sparse_mla_decode(const uint8_t* q_terms, const float* q_scale, const uint8_t* kv_cache,
+                          const int32_t* page_table,
                           const int32_t* row_req, const int32_t* row_vis, const int32_t* topk_idx,
                           const int32_t* topk_count, int32_t n_rows,
                           int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
@@ -139,13 +150,13 @@ int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int3
     if (n_heads != 16 && n_heads != 32) return DSA_ERR_UNSUPPORTED;
     int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
     if (rc != DSA_OK) return rc;
-    if (!q || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx ||
+    if (!q_terms || !q_scale || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx ||
         !topk_count || !status)
         return DSA_ERR_NULL;
     if (n_splits == 1 ? !out : (!part_o || !part_lse)) return DSA_ERR_NULL;
     if (n_rows == 0) return DSA_OK;
     dsa::MlaArgs a;
-    a.q = q; a.kv_cache = kv_cache; a.page_table = page_table;
+    a.q_terms = q_terms; a.q_scale = q_scale; a.kv_cache = kv_cache; a.page_table = page_table;
     a.row_req = row_req; a.row_vis = row_vis; a.topk_idx = topk_idx; a.topk_count = topk_count;
     a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
     a.page_size = page_size; a.log2_page = log2i(page_size); a.n_heads = n_heads;

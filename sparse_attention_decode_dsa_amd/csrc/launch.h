@@ -39,7 +39,8 @@ struct TopkArgs {
 };
 
 struct MlaArgs {
-    const uint16_t* q;
+    const uint8_t* q_terms;    // [n_rows, n_heads, 2, 576]: hi then lo fp8 codes
+    const float* q_scale;      // [n_rows, n_heads]
     const uint8_t* kv_cache;   // [num_pages, page_size, 640]: codes, fp32 scale, pad
     const int32_t* page_table;
     const int32_t* row_req;
@@ -70,6 +71,8 @@ constexpr int kMaxSplits = 64;
 
 hipError_t launch_quantize_q(const uint16_t* q, int32_t n_pairs, uint8_t* code, float* scale,
                              hipStream_t stream);
+hipError_t launch_quantize_mla_q(const uint16_t* q, int32_t n_pairs, uint8_t* terms, float* scale,
+                                 hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);

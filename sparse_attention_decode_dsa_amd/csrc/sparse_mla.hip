@@ -7,11 +7,12 @@
 //           LDS (rows padded to 592 bytes), with their fp32 scales;
 //   QK      on fp8 matrix cores: the tokens' fp8 bytes are the A operand as
 //           they are (M = tokens), the query the B operand (N = heads).  The
-//           bf16 query is split exactly into two fp8 terms per head,
-//           q = s_h (hi + lo / 16) with s_h a power of two (a bf16 value has
-//           8 significant bits, an E4M3 value 4), so two accumulator chains
-//           give the exact products without converting any key byte; both
-//           terms stay in registers for the whole split.  Wavefront w owns
+//           query arrives as two fp8 terms per head, q = s_h (hi + lo / 16)
+//           with s_h a power of two (the bf16 query split once per row, see
+//           quantize_q.hip), so two accumulator chains give the products
+//           without converting any key byte; both terms are gathered into
+//           the last tile buffer at the start and stay in registers for the
+//           whole split.  Wavefront w owns
 //           head block w % HB and 16 HB tokens; K steps of 128 use
 //           v_mfma_f32_16x16x128_f8f6f4, the last 64 bytes
 //           v_mfma_f32_16x16x32_fp8_fp8;
@@ -27,10 +28,12 @@
 // The value rows are the first 512 entries of the same rows (absorbed MLA),
 // so a tile is read from HBM once for both products.
 //
-// Latency hiding: a split's range of the selected list depends only on top_k,
-// so its entries are loaded together with the row's metadata; the block
-// table is then walked once for the whole split (slot -> page -> physical
-// row, kept in LDS).  Tiles are gathered by LDS-direct loads
+// Latency hiding: the query terms go out first, as LDS-direct loads into the
+// last tile buffer (free until the first tile's barrier); a split's range of
+// the selected list depends only on top_k, so its entries are loaded
+// together with the row's metadata; the block table is then walked once for
+// the whole split (slot -> page -> physical row, kept in LDS) and the first
+// gathers go out right after it.  Tiles are gathered by LDS-direct loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at the wavefront's LDS
 // base + 16 * lane), which need no registers: with four tile buffers, three
 // tiles are in flight while the fourth is computed.  Each wavefront waits
@@ -136,19 +139,16 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     // Tile buffers; the loads into them are issued as inline assembly and
     // waited for with explicit counts, so the compiler never waits for them.
     __shared__ __attribute__((aligned(16))) uint8_t s_x[NB][kTileBytes];
-    __shared__ float s_qsc[H];                                            // per-head power-of-two scale
     __shared__ __attribute__((aligned(16))) uint8_t s_p[8 * kPGroup];
     __shared__ int32_t s_rows[kRowsCap];
     __shared__ __attribute__((aligned(16))) float s_red[H][4];           // per-head values of the wavefronts
     __shared__ __attribute__((aligned(16))) float s_alpha[H];
     __shared__ __attribute__((aligned(16))) float s_m[H];
     __shared__ int s_moved[HB];
-    __shared__ int s_bad;
-    // The query terms are staged in the last tile buffer, which the first
-    // gathers leave free until the first tile's barrier.
-    uint8_t* const s_qh = s_x[NB - 1];
-    uint8_t* const s_ql = s_qh + H * kXStride;
-    static_assert(2 * H * kXStride <= kTileBytes, "query terms fit one tile buffer");
+    __shared__ int s_bad[NW];   // per wavefront: an entry of the split is invalid
+    // The query terms of the row land in the last tile buffer: term row
+    // 2h + t (t = 0 hi, 1 lo) of head h at kXStride-byte pitch, like a tile.
+    static_assert(2 * H <= kT, "query terms fit one tile buffer");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -160,6 +160,22 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     const int r = blockIdx.y;
     const int sp = blockIdx.x;
     const int ns = gridDim.x;
+
+    // Query terms: 2H rows of 576 bytes, contiguous in q_terms, gathered
+    // like a tile's rows (chunk 36, the pad, rereads chunk 0 of its row).
+    // They are the oldest loads of every wavefront, so the waits for any
+    // later load cover them.
+    {
+        const uint8_t* qrow = a.q_terms + (size_t)r * H * (2 * kRowBytes);
+        const uint32_t xl = lds_offset(s_x[NB - 1]);
+        constexpr int kQInsts = (2 * H * kRowChunks + kWave - 1) / kWave;
+#pragma unroll
+        for (int j = wv; j < kQInsts; j += NW) {
+            const int c = min(64 * j + lane, 2 * H * kRowChunks - 1);
+            const int t = c / kRowChunks, part = c - t * kRowChunks;
+            lds_dma16(qrow + (size_t)t * kRowBytes + (part < 36 ? part * 16 : 0), xl + j * 1024);
+        }
+    }
 
     // Row metadata (uniform loads) and the split's range of the selected
     // list.  The range depends only on top_k, so the list entries can be
@@ -183,68 +199,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     };
     load_slots(lo);
 
-    // Query -> two fp8 terms per head, staged in LDS rows of 592 bytes.
-    // Wavefront wv takes heads wv, wv+NW, ...; lane l holds 16-byte chunk l
-    // (and 64 + l for l < 8) of the 1152-byte bf16 row.  With
-    // s = 2^ceil(log2(max|q| / 448)) (1 for a zero head): hi = RNE_E4M3(q / s),
-    // lo = RNE_E4M3(16 (q / s - hi)); q / s - hi is exact, and so is lo
-    // wherever 16 (q / s - hi) is an E4M3 value.
-    constexpr int kQH = H / NW;   // heads per wavefront
-    uint4 qc0[kQH], qc1[kQH];
-#pragma unroll
-    for (int j = 0; j < kQH; ++j) {   // all loads first, then the arithmetic
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q + ((size_t)r * H + wv + NW * j) * kRowBytes);
-        qc0[j] = *reinterpret_cast<const uint4*>(src + 16 * lane);
-        qc1[j] = uint4{0u, 0u, 0u, 0u};
-        if (lane < 8) qc1[j] = *reinterpret_cast<const uint4*>(src + 16 * (64 + lane));
-    }
-#pragma unroll
-    for (int j = 0; j < kQH; ++j) {
-        const int hq = wv + NW * j;
-        const uint4 c0 = qc0[j], c1 = qc1[j];
-        float v[16];
-        const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        float amax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            v[2 * k] = __uint_as_float(w[k] << 16);
-            v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-            amax = fmaxf(amax, fmaxf(fabsf(v[2 * k]), fabsf(v[2 * k + 1])));
-        }
-        amax = wave_max(amax);
-        float s = 1.0f;
-        if (amax > 0.0f) {
-            int e;
-            const float m = frexpf(amax / 448.0f, &e);   // amax / 448 = m 2^e, m in [0.5, 1)
-            s = ldexpf(1.0f, m == 0.5f ? e - 1 : e);      // smallest power of two >= amax / 448
-        }
-        const float inv = 1.0f / s;                        // exact: s is a power of two
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float l4[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float x = v[4 * k + u] * inv;
-                const uint32_t hbyte = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xFFu;
-                l4[u] = 16.0f * (x - __builtin_amdgcn_cvt_f32_fp8(hbyte, 0));
-            }
-            int hp = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k] * inv, v[4 * k + 1] * inv, 0, false);
-            hp = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k + 2] * inv, v[4 * k + 3] * inv, hp, true);
-            int lp = __builtin_amdgcn_cvt_pk_fp8_f32(l4[0], l4[1], 0, false);
-            lp = __builtin_amdgcn_cvt_pk_fp8_f32(l4[2], l4[3], lp, true);
-            hw[k] = (uint32_t)hp;
-            lw[k] = (uint32_t)lp;
-        }
-        // chunk l covers bf16 elements [8l, 8l+8): fp8 bytes [8l, 8l+8)
-        *reinterpret_cast<uint2*>(s_qh + hq * kXStride + 8 * lane) = uint2{hw[0], hw[1]};
-        *reinterpret_cast<uint2*>(s_ql + hq * kXStride + 8 * lane) = uint2{lw[0], lw[1]};
-        if (lane < 8) {
-            *reinterpret_cast<uint2*>(s_qh + hq * kXStride + 8 * (64 + lane)) = uint2{hw[2], hw[3]};
-            *reinterpret_cast<uint2*>(s_ql + hq * kXStride + 8 * (64 + lane)) = uint2{lw[2], lw[3]};
-        }
-        if (lane == 0) s_qsc[hq] = s;
-    }
+    const float cq = a.sm_scale * a.q_scale[(size_t)r * H + 16 * hb + nn];
 
     bool ok = b_raw >= 0 && b_raw < a.batch && v_raw >= 0 && v_raw <= a.max_pages * a.page_size;
     if (!ok && tid == 0) flag(a.status, DSA_DEV_ROW_RANGE);
@@ -257,31 +212,12 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     const int n_tiles = hi > lo ? (hi - lo + kT - 1) / kT : 0;
     const int32_t* pt = a.page_table + (size_t)(ok ? b_raw : 0) * a.max_pages;
     const int pmask = a.page_size - 1;
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-
-    // The query operand of this lane (head 16 hb + nn, lane group g) for the
-    // whole split: 9 chunks per term, in the QK K order.
-    v4i qh[9], ql[9];
-    {
-        const int qo = (16 * hb + nn) * kXStride;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                qh[2 * p + h] = *reinterpret_cast<const v4i*>(s_qh + qo + 16 * qk_chunk(p, h, g));
-                ql[2 * p + h] = *reinterpret_cast<const v4i*>(s_ql + qo + 16 * qk_chunk(p, h, g));
-            }
-        qh[8] = *reinterpret_cast<const v4i*>(s_qh + qo + 16 * (32 + g));
-        ql[8] = *reinterpret_cast<const v4i*>(s_ql + qo + 16 * (32 + g));
-    }
-    const float cq = a.sm_scale * s_qsc[16 * hb + nn];
-
     // Block-table walk for the whole split, once: selected slot -> page ->
     // physical row, kept in LDS (-1 for invalid entries, which are reported).
     // All page-table loads of a batch go out before any result is used;
     // their indexes are clamped into the table so that they need no branch,
     // and validity is decided afterwards.
+    bool bad = false;
     auto walk = [&](int base) {
         int page[8];
 #pragma unroll
@@ -299,7 +235,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
                 } else {
                     row = page[u] * a.page_size + (slot[u] & pmask);
                 }
-                if (row < 0) s_bad = 1;
+                bad |= row < 0;
                 s_rows[e - lo] = row;
             }
         }
@@ -312,8 +248,33 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         }
     }
     static_assert(MlaGeom<4>::kRowsCap <= 2048, "a four-buffer split is one batch (kBatch >= 2048)");
+    const bool wave_bad = __ballot(bad) != 0ull;
+    if (lane == 0) s_bad[wv] = wave_bad;
+    // Every load of the wavefronts done (the query terms included, which the
+    // compiler does not track), so the terms are in LDS after the barrier and
+    // no load the compiler tracks is outstanding once the gathers go out.
+    wait_vm<0>();
     __syncthreads();
-    const bool any_bad = s_bad != 0;
+    bool any_bad = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any_bad |= s_bad[w] != 0;
+
+    // The query operand of this lane (head 16 hb + nn, lane group g) for the
+    // whole split: 9 chunks per term, in the QK K order.
+    v4i qh[9], ql[9];
+    {
+        const uint8_t* qh_row = s_x[NB - 1] + (2 * (16 * hb + nn)) * kXStride;
+        const uint8_t* ql_row = qh_row + kXStride;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                qh[2 * p + h] = *reinterpret_cast<const v4i*>(qh_row + 16 * qk_chunk(p, h, g));
+                ql[2 * p + h] = *reinterpret_cast<const v4i*>(ql_row + 16 * qk_chunk(p, h, g));
+            }
+        qh[8] = *reinterpret_cast<const v4i*>(qh_row + 16 * (32 + g));
+        ql[8] = *reinterpret_cast<const v4i*>(ql_row + 16 * (32 + g));
+    }
 
     // Row of tile-local token t of the tile starting at split entry `base`.
     // The read is clamped into the array and its value discarded past the end,
@@ -361,8 +322,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         }
     };
 
-    // Prologue: the first NB-1 tiles in flight (into buffers other than the
-    // query staging buffer).
+    // Prologue: the first NB-1 tiles in flight.
 #pragma unroll
     for (int j = 0; j < NB - 1; ++j)
         if (j < n_tiles) issue(j, lo + j * kT);

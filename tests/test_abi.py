@@ -31,7 +31,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_index_scores",
+    assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_quantize_mla_q", "dsa_index_scores",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_merge"} <= set(names)
     raw = ctypes.CDLL(dsa.lib_path())
     for n in names:
@@ -96,7 +96,7 @@ def test_topk_validation_and_workspace(L):
 
 
 def _mla(L, **kw):
-    a = dict(q=P, kv_cache=P, page_table=P, row_req=P, row_vis=P, topk_idx=P,
+    a = dict(q_terms=P, q_scale=P, kv_cache=P, page_table=P, row_req=P, row_vis=P, topk_idx=P,
              topk_count=P, n_rows=4, batch=4, num_pages=100, max_pages=20, page_size=256,
              n_heads=32, top_k=2048, n_splits=4, sm_scale=0.04, part_o=P, part_lse=P, out=None,
              out_lse=None, status=P, stream=None)
@@ -114,6 +114,8 @@ def test_sparse_mla_validation(L):
     assert _mla(L, part_o=None) == NULL                      # split path needs partials
     assert _mla(L, n_splits=1, out=None) == NULL             # lone split needs out
     assert _mla(L, page_size=48) == UNSUP
+    assert _mla(L, q_terms=None) == NULL
+    assert _mla(L, q_scale=None) == NULL
     assert _mla(L, n_rows=0) == OK
 
 
@@ -130,3 +132,9 @@ def test_lse_merge_and_quantize_validation(L):
     assert q(P, -1, 64, 128, P, P, None) == SHAPE
     assert q(None, 4, 64, 128, P, P, None) == NULL
     assert q(P, 0, 64, 128, P, P, None) == OK
+    qm = L.dsa_quantize_mla_q
+    assert qm(P, 4, 32, 512, P, P, None) == UNSUP
+    assert qm(P, -1, 32, 576, P, P, None) == SHAPE
+    assert qm(P, 4, 0, 576, P, P, None) == SHAPE
+    assert qm(P, 4, 32, 576, P, None, None) == NULL
+    assert qm(P, 0, 32, 576, P, P, None) == OK

@@ -63,11 +63,12 @@ def mla_on_oracle_selection(sub, ref, n_splits):
     idx = torch.from_numpy(ref["topk_idx"].astype(np.int32)).cuda()
     cnt = torch.from_numpy(ref["topk_count"].astype(np.int32)).cuda()
     st = dsa.new_status()
+    qt, qs = dsa.quantize_mla_q(g.q_mla)
     if n_splits == 1:
-        out, lse, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_cache, g.page_table, g.row_req,
+        out, lse, _ = dsa.sparse_mla_decode(qt, qs, g.kv_cache, g.page_table, g.row_req,
                                             g.row_vis, idx, cnt, 1, g.sm_scale, status=st)
     else:
-        po, pl, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_cache, g.page_table, g.row_req,
+        po, pl, _ = dsa.sparse_mla_decode(qt, qs, g.kv_cache, g.page_table, g.row_req,
                                           g.row_vis, idx, cnt, n_splits, g.sm_scale, status=st)
         out, lse = dsa.lse_merge(po, pl)
     torch.cuda.synchronize()
@@ -92,6 +93,35 @@ def test_quantize_q_bit_exact():
     rc, rs = O.quantize_q(qb.view(torch.int16).numpy().view(np.uint16))
     np.testing.assert_array_equal(scale.cpu().double().numpy(), rs)
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_mla_q_terms():
+    """The prepared MLA query: a power-of-two scale per head, 2^ceil(log2(amax/448))
+    (1 for a zero head), and q = scale * (hi + lo / 16) exactly for every element
+    with |q / scale| >= 2^-6, within 2^-14 * scale below that."""
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(9, 32, 576, generator=g) * torch.exp(torch.randn(9, 32, 1, generator=g) * 4)
+    q[0, 0] = 0.0                      # all-zero head
+    q[0, 1, :] = 0.0
+    q[0, 1, 7] = -448.0                # amax exactly 448
+    q[0, 2, ::3] *= 1e-6               # elements far below the head's maximum
+    q[1, 5] *= 1e-30                   # tiny head
+    q[2, 7] *= 1e30                    # huge head
+    qb = q.to(torch.bfloat16)
+    terms, scale = dsa.quantize_mla_q(qb.cuda())
+    torch.cuda.synchronize()
+    terms, scale = terms.cpu(), scale.cpu().double()
+    x = qb.double()
+    amax = x.abs().amax(dim=2)
+    expect = torch.where(amax > 0, torch.exp2(torch.ceil(torch.log2(amax / 448.0))), torch.ones_like(amax))
+    assert torch.equal(scale, expect)
+    hi = terms[:, :, 0].view(torch.float8_e4m3fn).double()
+    lo = terms[:, :, 1].view(torch.float8_e4m3fn).double()
+    rec = scale[..., None] * (hi + lo / 16.0)
+    y = (x / scale[..., None]).abs()
+    exact = y >= 2.0 ** -6
+    assert torch.equal(rec[exact], x[exact])
+    assert ((rec - x).abs()[~exact] <= 2.0 ** -14 * scale[..., None].expand_as(x)[~exact]).all()
 
 
 # ------------------------------------------------------------------ top-k alone
