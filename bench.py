@@ -2,10 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1_l32k]
 
-A step is the whole hot path for one batch: bf16 indexer query -> fp8 codes,
-fp8 indexer scores over every cached token, exact top-2048 (per split, then
-merged), split-K sparse absorbed-MLA attention over the selected paged fp8
-rows, and the LSE merge.  Inputs are seeded synthetic tensors already resident
+A step is the whole hot path for one batch: bf16 queries -> fp8 (indexer
+codes, the MLA query's two terms), fp8 indexer scores over every cached token,
+exact top-2048 (per split, then merged), split-K sparse absorbed-MLA attention
+over the selected paged fp8 rows, and the LSE merge.  Inputs are seeded synthetic tensors already resident
 in HBM.  Prints ONE JSON line (rank 0).
 
 The default workload is bulk decode at the metric's point: 64 requests, one
@@ -13,7 +13,7 @@ query row each, 32768 cached tokens each, 256-token pages shuffled in the
 pool, 64 x 128 fp8 indexer, 32 MLA heads over 576-wide fp8 rows, top-2048.
 
 Timing: W untimed steps, then K steps between two device synchronisations,
-replayed from a HIP graph of one step (``--eager`` launches the five kernels
+replayed from a HIP graph of one step (``--eager`` launches the kernels
 directly instead).  Then every kernel is replayed back to back from a graph
 of 20 launches between two HIP events on the stream it runs on, for
 per-kernel durations and the roofline of the dominant kernel.  The oracle (fp64, CPU) is timed on a bounded
@@ -169,8 +169,8 @@ def main():
     # same outputs), averaged per launch.
     i = inp
     launches = {
-        "quantize_q": lambda: dsa.quantize_q(i.q_idx, step.q_code, step.q_scale),
-        "quantize_mla_q": lambda: dsa.quantize_mla_q(i.q_mla, step.q_terms, step.q_mla_scale),
+        "prepare_queries": lambda: dsa.prepare_queries(i.q_idx, i.q_mla, step.q_code, step.q_scale,
+                                                       step.q_terms, step.q_mla_scale),
         "index_scores": lambda: dsa.index_scores(
             step.q_code, step.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
             i.row_req, i.row_vis, group_rows=step.group_rows, score_stride=step.score_stride,

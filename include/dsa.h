@@ -5,6 +5,8 @@
  * DeepSeek-V3.2", sgl-project/sglang PR #42618, sections Motivation and
  * Modifications):
  *   1. dsa_quantize_q        bf16 indexer queries -> fp8 E4M3FN codes + scales
+ *      dsa_quantize_mla_q    bf16 MLA queries -> two fp8 E4M3FN terms + scales
+ *      (dsa_prepare_queries does both in one launch)
  *   2. dsa_index_scores      fp8 indexer score of every visible cached token
  *   3. dsa_topk              exact top-k per row: per-split local top-k, then an
  *                            exact merge of the candidates
@@ -114,6 +116,18 @@ int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int3
  */
 int dsa_quantize_mla_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
                        uint8_t* q_terms, float* q_scale, hipStream_t stream);
+
+/*
+ * dsa_prepare_queries -- both query preparations of a decode step in one
+ * launch: the same outputs as dsa_quantize_q(q_idx, n_rows, idx_heads,
+ * idx_dim, q_code, q_scale) followed by dsa_quantize_mla_q(q_mla, n_rows,
+ * mla_heads, mla_dim, q_terms, q_mla_scale), with the same layouts.
+ * Supported: idx_dim == 128, mla_dim == 576, idx_heads >= 1, mla_heads >= 1.
+ * n_rows == 0 enqueues nothing.
+ */
+int dsa_prepare_queries(const uint16_t* q_idx, int32_t n_rows, int32_t idx_heads, int32_t idx_dim,
+                        uint8_t* q_code, float* q_scale, const uint16_t* q_mla, int32_t mla_heads,
+                        int32_t mla_dim, uint8_t* q_terms, float* q_mla_scale, hipStream_t stream);
 
 /*
  * dsa_index_scores -- fp8 lightning-indexer scores (subject page,

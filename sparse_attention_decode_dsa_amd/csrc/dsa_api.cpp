@@ -76,6 +76,18 @@ int dsa_quantize_mla_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, 
     return launch_status(dsa::launch_quantize_mla_q(q_bf16, n_rows * n_heads, q_terms, q_scale, stream));
 }
 
+int dsa_prepare_queries(const uint16_t* q_idx, int32_t n_rows, int32_t idx_heads, int32_t idx_dim,
+                        uint8_t* q_code, float* q_scale, const uint16_t* q_mla, int32_t mla_heads,
+                        int32_t mla_dim, uint8_t* q_terms, float* q_mla_scale, hipStream_t stream) {
+    if (n_rows < 0 || idx_heads < 1 || idx_dim < 1 || mla_heads < 1 || mla_dim < 1) return DSA_ERR_SHAPE;
+    if (idx_dim != 128 || mla_dim != 576) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)n_rows * (idx_heads + mla_heads) > INT32_MAX / 4) return DSA_ERR_SHAPE;
+    if (n_rows == 0) return DSA_OK;
+    if (!q_idx || !q_code || !q_scale || !q_mla || !q_terms || !q_mla_scale) return DSA_ERR_NULL;
+    return launch_status(dsa::launch_prepare_queries(q_idx, n_rows * idx_heads, q_code, q_scale, q_mla,
+                                                     n_rows * mla_heads, q_terms, q_mla_scale, stream));
+}
+
 int dsa_index_scores(const uint8_t* q_code, const float* q_scale, const float* head_w,
                      const uint8_t* k_code, const float* k_scale, const int32_t* page_table,
                      const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,

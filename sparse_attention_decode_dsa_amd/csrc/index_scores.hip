@@ -111,6 +111,10 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     __shared__ int s_page[kMaxChunkPages];
     __shared__ __attribute__((aligned(16))) uint8_t s_q[G > 1 ? G * 64 * kQStride : 16];
     __shared__ __attribute__((aligned(16))) float s_wq[G > 1 ? G * 64 : 4];
+    // One row (decode): the chunk's scores collect here and go out in one
+    // burst after the chunk's keys are read (HBM reads slow down markedly
+    // when writes are mixed in).  Several rows write as they go.
+    __shared__ __attribute__((aligned(16))) float s_sc[G == 1 ? kMaxChunk : 4];
 
     // Row geometry, checked once per row.
     if (threadIdx.x < G) {
@@ -213,7 +217,12 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     };
 
     // Scores of the group at tg for every row of the group.
-    auto process = [&](const KeyGroup& kg, int tg) {
+    auto process = [&](KeyGroup& kg, int tg) {
+        // Every path consumes the group's loads here, so none is left
+        // pending across the loop's back edge when a path skips the rows.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pin(kg.b[j]);
+        pin(kg.scale);
         const int t = tg + lane;
 #pragma unroll 1
         for (int rr = 0; rr < G; ++rr) {
@@ -232,13 +241,17 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
                 const float sc = group_dot(qa, wq, kg.b) * kg.scale;
                 if (kg.ok && t < v) mine = sc;
             }
-            if (t < t_end) a.scores[(size_t)r * a.score_stride + t] = mine;
+            if constexpr (G == 1) {
+                if (t < t_end) s_sc[t - t0] = mine;
+            } else {
+                if (t < t_end) a.scores[(size_t)r * a.score_stride + t] = mine;
+            }
         }
     };
 
     // Two key buffers in turn: the loads of the next group are in flight
     // while the current one is computed, and no register copy forces a wait
-    // on them (or on the score stores) before the next loads go out.
+    // on them before the next loads go out.
     // The last prefetch of a wavefront re-reads its current group (an L2
     // hit) rather than branching around the loads.
     KeyGroup ka, kb;
@@ -259,10 +272,26 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
         }
     }
 
-    // -inf for the part of the chunk past every row's span.
-    for (int rr = 0; rr < G; ++rr) {
-        float* srow = a.scores + (size_t)(r0 + rr) * a.score_stride;
-        for (int t = t_comp + threadIdx.x; t < t_end; t += 256) srow[t] = -INFINITY;
+    if constexpr (G == 1) {
+        // -inf past the span, then the whole chunk out: 16-byte stores where
+        // the row's chunk is 16-byte aligned, else one float per lane.
+        for (int t = t_comp + threadIdx.x; t < t_end; t += 256) s_sc[t - t0] = -INFINITY;
+        __syncthreads();
+        float* dst = a.scores + (size_t)r0 * a.score_stride + t0;
+        const int n = t_end - t0;
+        if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+            for (int i = 4 * threadIdx.x; i + 3 < n; i += 1024)
+                *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&s_sc[i]);
+            for (int i = (n & ~3) + threadIdx.x; i < n; i += 256) dst[i] = s_sc[i];
+        } else {
+            for (int i = threadIdx.x; i < n; i += 256) dst[i] = s_sc[i];
+        }
+    } else {
+        // -inf for the part of the chunk past every row's span.
+        for (int rr = 0; rr < G; ++rr) {
+            float* srow = a.scores + (size_t)(r0 + rr) * a.score_stride;
+            for (int t = t_comp + threadIdx.x; t < t_end; t += 256) srow[t] = -INFINITY;
+        }
     }
 }
 

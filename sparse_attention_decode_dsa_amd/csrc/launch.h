@@ -73,6 +73,9 @@ hipError_t launch_quantize_q(const uint16_t* q, int32_t n_pairs, uint8_t* code, 
                              hipStream_t stream);
 hipError_t launch_quantize_mla_q(const uint16_t* q, int32_t n_pairs, uint8_t* terms, float* scale,
                                  hipStream_t stream);
+hipError_t launch_prepare_queries(const uint16_t* q_idx, int32_t n_idx, uint8_t* code, float* scale,
+                                  const uint16_t* q_mla, int32_t n_mla, uint8_t* terms, float* mla_scale,
+                                  hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);

@@ -3,17 +3,16 @@
 //   - MLA queries (576 bf16) -> two fp8 E4M3FN terms and one power-of-two
 //     scale s, q = s (hi + lo / 16), read by the sparse MLA kernel's fp8
 //     QK products.
+// Each has a kernel of its own; a third does both in one launch (the
+// indexer pairs first, then the MLA pairs), which is what a decode step
+// uses.
 #include "device_common.h"
 #include "launch.h"
 
 namespace dsa {
 
-__global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* __restrict__ q, int32_t n_pairs,
-                                                         uint8_t* __restrict__ code,
-                                                         float* __restrict__ scale) {
-    const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pair >= n_pairs) return;  // whole wavefront leaves together
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void quantize_idx_pair(const uint16_t* __restrict__ q, int pair, int lane,
+                                                  uint8_t* __restrict__ code, float* __restrict__ scale) {
     const uint32_t w = reinterpret_cast<const uint32_t*>(q + (size_t)pair * 128)[lane];
     const float x0 = __uint_as_float(w << 16);
     const float x1 = __uint_as_float(w & 0xFFFF0000u);
@@ -38,19 +37,23 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* __restr
     if (lane == 0) scale[pair] = ldexpf(1.0f, e);
 }
 
+__global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* __restrict__ q, int32_t n_pairs,
+                                                         uint8_t* __restrict__ code,
+                                                         float* __restrict__ scale) {
+    const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= n_pairs) return;  // whole wavefront leaves together
+    quantize_idx_pair(q, pair, threadIdx.x & 63, code, scale);
+}
+
 // MLA query of one (row, head): s = 2^ceil(log2(max|q| / 448)) (1 for a zero
 // head), hi = RNE_E4M3(q / s), lo = RNE_E4M3(16 (q / s - hi)).  q / s - hi is
 // exact in fp32; a bf16 value has 8 significant bits and hi carries the top
 // 4, so lo is exact too wherever 16 (q / s - hi) is an E4M3 value (always,
 // unless q / s is below E4M3's normal range).  Lane l converts elements
 // [8l, 8l + 8) and, for l < 8, [512 + 8l, 512 + 8l + 8).
-__global__ __launch_bounds__(256) void quantize_mla_q_kernel(const uint16_t* __restrict__ q, int32_t n_pairs,
-                                                             uint8_t* __restrict__ terms,
-                                                             float* __restrict__ scale) {
+__device__ __forceinline__ void quantize_mla_pair(const uint16_t* __restrict__ q, int pair, int lane,
+                                                  uint8_t* __restrict__ terms, float* __restrict__ scale) {
     constexpr int kD = 576;
-    const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pair >= n_pairs) return;  // whole wavefront leaves together
-    const int lane = threadIdx.x & 63;
     const uint8_t* src = reinterpret_cast<const uint8_t*>(q + (size_t)pair * kD);
     const uint4 c0 = *reinterpret_cast<const uint4*>(src + 16 * lane);
     uint4 c1 = uint4{0u, 0u, 0u, 0u};
@@ -98,6 +101,37 @@ __global__ __launch_bounds__(256) void quantize_mla_q_kernel(const uint16_t* __r
         *reinterpret_cast<uint2*>(lo + 8 * (64 + lane)) = uint2{lw[2], lw[3]};
     }
     if (lane == 0) scale[pair] = s;
+}
+
+__global__ __launch_bounds__(256) void quantize_mla_q_kernel(const uint16_t* __restrict__ q, int32_t n_pairs,
+                                                             uint8_t* __restrict__ terms,
+                                                             float* __restrict__ scale) {
+    const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= n_pairs) return;  // whole wavefront leaves together
+    quantize_mla_pair(q, pair, threadIdx.x & 63, terms, scale);
+}
+
+// Wavefront w < n_idx prepares indexer pair w, the next n_mla wavefronts the
+// MLA pairs.
+__global__ __launch_bounds__(256) void prepare_queries_kernel(const uint16_t* __restrict__ q_idx, int32_t n_idx,
+                                                              uint8_t* __restrict__ code, float* __restrict__ scale,
+                                                              const uint16_t* __restrict__ q_mla, int32_t n_mla,
+                                                              uint8_t* __restrict__ terms,
+                                                              float* __restrict__ mla_scale) {
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < n_idx) quantize_idx_pair(q_idx, w, lane, code, scale);
+    else if (w - n_idx < n_mla) quantize_mla_pair(q_mla, w - n_idx, lane, terms, mla_scale);
+}
+
+hipError_t launch_prepare_queries(const uint16_t* q_idx, int32_t n_idx, uint8_t* code, float* scale,
+                                  const uint16_t* q_mla, int32_t n_mla, uint8_t* terms, float* mla_scale,
+                                  hipStream_t stream) {
+    const int64_t waves = (int64_t)n_idx + n_mla;
+    if (waves == 0) return hipSuccess;
+    prepare_queries_kernel<<<(int)((waves + 3) / 4), 256, 0, stream>>>(q_idx, n_idx, code, scale, q_mla, n_mla,
+                                                                       terms, mla_scale);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_mla_q(const uint16_t* q, int32_t n_pairs, uint8_t* terms, float* scale,

@@ -35,6 +35,7 @@ _SIGS = {
     "dsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dsa_quantize_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_quantize_mla_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
+    "dsa_prepare_queries": ([_p, _i32, _i32, _i32, _p, _p, _p, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_index_scores": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
     "dsa_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
@@ -135,6 +136,31 @@ def quantize_mla_q(q_bf16, q_terms=None, q_scale=None, stream=None):
                                     _ptr(q_terms, _FP8, "q_terms"), _ptr(q_scale, torch.float32, "q_scale"),
                                     _stream(stream)), "dsa_quantize_mla_q")
     return q_terms, q_scale
+
+
+def prepare_queries(q_idx, q_mla, q_code=None, q_scale=None, q_terms=None, q_mla_scale=None,
+                    stream=None):
+    """quantize_q(q_idx) and quantize_mla_q(q_mla) in one launch ->
+    (q_code, q_scale, q_terms, q_mla_scale)."""
+    r, hi, di = q_idx.shape
+    rm, hm, dm = q_mla.shape
+    if rm != r:
+        raise DsaError(f"q_idx has {r} rows, q_mla {rm}")
+    dev = q_idx.device
+    if q_code is None:
+        q_code = torch.empty((r, hi, di), dtype=torch.uint8, device=dev)
+    if q_scale is None:
+        q_scale = torch.empty((r, hi), dtype=torch.float32, device=dev)
+    if q_terms is None:
+        q_terms = torch.empty((r, hm, 2, dm), dtype=torch.uint8, device=dev)
+    if q_mla_scale is None:
+        q_mla_scale = torch.empty((r, hm), dtype=torch.float32, device=dev)
+    _check(lib().dsa_prepare_queries(
+        _ptr(q_idx, _BF16, "q_idx"), r, hi, di, _ptr(q_code, _FP8, "q_code"),
+        _ptr(q_scale, torch.float32, "q_scale"), _ptr(q_mla, _BF16, "q_mla"), hm, dm,
+        _ptr(q_terms, _FP8, "q_terms"), _ptr(q_mla_scale, torch.float32, "q_mla_scale"),
+        _stream(stream)), "dsa_prepare_queries")
+    return q_code, q_scale, q_terms, q_mla_scale
 
 
 def index_scores(q_code, q_scale, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis,
@@ -287,8 +313,8 @@ class DecodeStep:
 
     def run(self, stream=None):
         i = self.inp
-        quantize_q(i.q_idx, self.q_code, self.q_scale, stream=stream)
-        quantize_mla_q(i.q_mla, self.q_terms, self.q_mla_scale, stream=stream)
+        prepare_queries(i.q_idx, i.q_mla, self.q_code, self.q_scale, self.q_terms, self.q_mla_scale,
+                        stream=stream)
         index_scores(self.q_code, self.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table,
                      i.kv_lens, i.row_req, i.row_vis, group_rows=self.group_rows,
                      score_stride=self.score_stride, scores=self.scores, status=self.status,

@@ -31,7 +31,8 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_quantize_mla_q", "dsa_index_scores",
+    assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_quantize_mla_q",
+            "dsa_prepare_queries", "dsa_index_scores",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_merge"} <= set(names)
     raw = ctypes.CDLL(dsa.lib_path())
     for n in names:
@@ -138,3 +139,10 @@ def test_lse_merge_and_quantize_validation(L):
     assert qm(P, 4, 0, 576, P, P, None) == SHAPE
     assert qm(P, 4, 32, 576, P, None, None) == NULL
     assert qm(P, 0, 32, 576, P, P, None) == OK
+    pq = L.dsa_prepare_queries
+    assert pq(P, 4, 64, 64, P, P, P, 32, 576, P, P, None) == UNSUP
+    assert pq(P, 4, 64, 128, P, P, P, 32, 512, P, P, None) == UNSUP
+    assert pq(P, -1, 64, 128, P, P, P, 32, 576, P, P, None) == SHAPE
+    assert pq(P, 4, 64, 128, P, P, P, 0, 576, P, P, None) == SHAPE
+    assert pq(P, 4, 64, 128, P, P, None, 32, 576, P, P, None) == NULL
+    assert pq(P, 0, 64, 128, P, P, P, 32, 576, P, P, None) == OK

@@ -124,6 +124,19 @@ def test_quantize_mla_q_terms():
     assert ((rec - x).abs()[~exact] <= 2.0 ** -14 * scale[..., None].expand_as(x)[~exact]).all()
 
 
+def test_prepare_queries_equals_separate_calls():
+    """The one-launch preparation writes exactly what the two separate calls do."""
+    g = torch.Generator().manual_seed(12)
+    qi = (torch.randn(7, 64, 128, generator=g) * 3).to(torch.bfloat16).cuda()
+    qm = (torch.randn(7, 16, 576, generator=g) * 5).to(torch.bfloat16).cuda()
+    code, sc, terms, msc = dsa.prepare_queries(qi, qm)
+    code2, sc2 = dsa.quantize_q(qi)
+    terms2, msc2 = dsa.quantize_mla_q(qm)
+    torch.cuda.synchronize()
+    assert torch.equal(code, code2) and torch.equal(sc, sc2)
+    assert torch.equal(terms, terms2) and torch.equal(msc, msc2)
+
+
 # ------------------------------------------------------------------ top-k alone
 
 def _synthetic_scores(rng, r, stride, vis, tie_frac=0.3):
