@@ -13,11 +13,15 @@ query row each, 32768 cached tokens each, 256-token pages shuffled in the
 pool, 64 x 128 fp8 indexer, 32 MLA heads over 576-wide fp8 rows, top-2048.
 
 Timing: W untimed steps, then K steps between two device synchronisations,
-replayed from a HIP graph of one step (``--eager`` launches the kernels
-directly instead).  Then every kernel is replayed back to back from a graph
-of 20 launches between two HIP events on the stream it runs on, for
-per-kernel durations and the roofline of the dominant kernel.  The oracle (fp64, CPU) is timed on a bounded
-sample of the same workload as a reported baseline.
+replayed from HIP graphs (``--eager`` launches the kernels directly instead).
+Consecutive steps cycle through ``--rotate`` independent input sets (default
+3), so that no step re-reads bytes the one before left in the chip's 256 MB
+memory-side cache: every step reads its inputs from HBM, as the layers of a
+real decode step do.  Then every kernel is replayed back to back from a graph
+of 20 launches (cycling through the input sets) between two HIP events on the
+stream it runs on, for per-kernel durations and the roofline of the dominant
+kernel.  The oracle (fp64, CPU) is timed on a bounded sample of the same
+workload as a reported baseline.
 """
 
 from __future__ import annotations
@@ -51,6 +55,9 @@ def parse():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="independent input sets that consecutive steps and launches cycle through, "
+                         "so that no launch re-reads what the one before left in the memory-side cache")
     return ap.parse_args()
 
 
@@ -114,14 +121,19 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = W.make(args.config, seed=args.seed, device=dev)
-    step = dsa.DecodeStep(inp, args.index_splits, args.attn_splits)
+    n_sets = max(1, args.rotate)
+    base_seed = args.seed if args.seed is not None else sum(map(ord, args.config))
+    inps = [W.make(args.config, seed=base_seed + k, device=dev) for k in range(n_sets)]
+    steps = [dsa.DecodeStep(x, args.index_splits, args.attn_splits) for x in inps]
+    inp, step = inps[0], steps[0]
     stream = torch.cuda.current_stream()
 
-    # Correctness gate before timing: one eager step, no device faults.
-    step.run()
+    # Correctness gate before timing: one eager step per input set, no device faults.
+    for st in steps:
+        st.run()
     torch.cuda.synchronize()
-    dsa.check_status(step.status)
+    for st in steps:
+        dsa.check_status(st.status)
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
@@ -132,79 +144,98 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    graph = None
+    # A graph of one step per input set (a round), and one graph per single
+    # step for the remainder, so that exactly K steps run.
+    round_graph, single = None, []
     if not args.eager:
         s = torch.cuda.Stream()
         s.wait_stream(stream)
         with torch.cuda.stream(s):
             for _ in range(2):
-                step.run()
+                for st in steps:
+                    st.run()
         stream.wait_stream(s)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step.run()
+        round_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(round_graph):
+            for st in steps:
+                st.run()
+        for st in steps:
+            g1 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1):
+                st.run()
+            single.append(g1)
         torch.cuda.synchronize()
 
-    def one():
-        if graph is not None:
-            graph.replay()
+    def run_steps(k):
+        if round_graph is not None:
+            for _ in range(k // n_sets):
+                round_graph.replay()
+            for j in range(k % n_sets):
+                single[j].replay()
         else:
-            step.run()
+            for j in range(k):
+                steps[j % n_sets].run()
 
-    for _ in range(args.warmup):
-        one()
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one()
+    run_steps(args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed * 1e3 / args.steps
-    dsa.check_status(step.status)
+    for st in steps:
+        dsa.check_status(st.status)
 
     # Per-kernel durations: each kernel launched 20 times back to back from a
-    # HIP graph, the graph replayed K/4 times on the launch stream between
-    # two HIP events (every launch reads the same inputs and rewrites the
-    # same outputs), averaged per launch.
-    i = inp
-    launches = {
-        "prepare_queries": lambda: dsa.prepare_queries(i.q_idx, i.q_mla, step.q_code, step.q_scale,
-                                                       step.q_terms, step.q_mla_scale),
-        "index_scores": lambda: dsa.index_scores(
-            step.q_code, step.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
-            i.row_req, i.row_vis, group_rows=step.group_rows, score_stride=step.score_stride,
-            scores=step.scores, status=step.status),
-        "topk": lambda: dsa.topk(step.scores, i.row_vis, i.top_k, step.index_splits,
-                                 workspace=step.workspace, topk_idx=step.topk_idx,
-                                 topk_count=step.topk_count, status=step.status),
-    }
-    if step.attn_splits == 1:
-        launches["sparse_mla"] = lambda: dsa.sparse_mla_decode(
-            step.q_terms, step.q_mla_scale, i.kv_cache, i.page_table, i.row_req, i.row_vis,
-            step.topk_idx, step.topk_count, 1, i.sm_scale, out=step.out, out_lse=step.out_lse, status=step.status)
-    else:
-        launches["sparse_mla"] = lambda: dsa.sparse_mla_decode(
-            step.q_terms, step.q_mla_scale, i.kv_cache, i.page_table, i.row_req, i.row_vis,
-            step.topk_idx, step.topk_count, step.attn_splits, i.sm_scale, part_o=step.part_o,
-            part_lse=step.part_lse, status=step.status)
-        launches["lse_merge"] = lambda: dsa.lse_merge(step.part_o, step.part_lse, out=step.out,
-                                                      out_lse=step.out_lse)
+    # HIP graph, the launches cycling through the input sets (each set's
+    # launch reads that set's inputs and rewrites its outputs), the graph
+    # replayed K/4 times on the launch stream between two HIP events,
+    # averaged per launch.
+    def kernel_launches(i, st):
+        fns = {
+            "prepare_queries": lambda: dsa.prepare_queries(i.q_idx, i.q_mla, st.q_code, st.q_scale,
+                                                           st.q_terms, st.q_mla_scale),
+            "index_scores": lambda: dsa.index_scores(
+                st.q_code, st.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
+                i.row_req, i.row_vis, group_rows=st.group_rows, score_stride=st.score_stride,
+                scores=st.scores, status=st.status),
+            "topk": lambda: dsa.topk(st.scores, i.row_vis, i.top_k, st.index_splits,
+                                     workspace=st.workspace, topk_idx=st.topk_idx,
+                                     topk_count=st.topk_count, status=st.status),
+        }
+        if st.attn_splits == 1:
+            fns["sparse_mla"] = lambda: dsa.sparse_mla_decode(
+                st.q_terms, st.q_mla_scale, i.kv_cache, i.page_table, i.row_req, i.row_vis,
+                st.topk_idx, st.topk_count, 1, i.sm_scale, out=st.out, out_lse=st.out_lse,
+                status=st.status)
+        else:
+            fns["sparse_mla"] = lambda: dsa.sparse_mla_decode(
+                st.q_terms, st.q_mla_scale, i.kv_cache, i.page_table, i.row_req, i.row_vis,
+                st.topk_idx, st.topk_count, st.attn_splits, i.sm_scale, part_o=st.part_o,
+                part_lse=st.part_lse, status=st.status)
+            fns["lse_merge"] = lambda: dsa.lse_merge(st.part_o, st.part_lse, out=st.out,
+                                                     out_lse=st.out_lse)
+        return fns
+
+    per_set = [kernel_launches(x, st) for x, st in zip(inps, steps)]
     kern_us = {}
     reps = 20
-    for n, fn in launches.items():
+    for n in per_set[0]:
+        fns = [d[n] for d in per_set]
         g = None
         if not args.eager:
             side = torch.cuda.Stream()
             side.wait_stream(stream)
             with torch.cuda.stream(side):
-                fn()
+                for fn in fns:
+                    fn()
             stream.wait_stream(side)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _ in range(reps):
-                    fn()
+                for j in range(reps):
+                    fns[j % n_sets]()
             torch.cuda.synchronize()
         n_iter = max(1, args.steps // 4)
         e0 = torch.cuda.Event(enable_timing=True)
@@ -214,13 +245,14 @@ def main():
             if g is not None:
                 g.replay()
             else:
-                for _ in range(reps):
-                    fn()
+                for j in range(reps):
+                    fns[j % n_sets]()
         e1.record(stream)
         e1.synchronize()
         kern_us[n] = 1e3 * e0.elapsed_time(e1) / (n_iter * reps)
     torch.cuda.synchronize()
-    dsa.check_status(step.status)
+    for st in steps:
+        dsa.check_status(st.status)
 
     ab = algorithmic_bytes(inp)
     idx_us = kern_us["index_scores"]
@@ -253,7 +285,8 @@ def main():
             "batch": inp.n_rows, "kv_len_max": int(inp.row_vis.max()), "top_k": inp.top_k,
             "page_size": inp.page_size, "mla_heads": inp.mla_heads,
             "index_splits": step.index_splits, "attn_splits": step.attn_splits,
-            "launch": "eager" if graph is None else "hipgraph",
+            "launch": "eager" if round_graph is None else "hipgraph",
+            "input_sets": n_sets,
         },
         "roofline": {
             "kernel": "index_scores",
