@@ -4,16 +4,17 @@
  * The step (page "[ROCm] Support decode context parallel (DCP) for GLM-5 /
  * DeepSeek-V3.2", sgl-project/sglang PR #42618, sections Motivation and
  * Modifications):
- *   1. dsa_quantize_q        bf16 indexer queries -> fp8 E4M3FN codes + scales
- *      dsa_quantize_mla_q    bf16 MLA queries -> two fp8 E4M3FN terms + scales
- *      (dsa_prepare_queries does both in one launch)
- *   2. dsa_index_scores      fp8 indexer score of every visible cached token
- *   3. dsa_topk              exact top-k per row: per-split local top-k, then an
+ *   1. dsa_index_scores      fp8 indexer score of every visible cached token
+ *                            (the bf16 queries quantized as dsa_quantize_q does)
+ *   2. dsa_topk              exact top-k per row: per-split local top-k, then an
  *                            exact merge of the candidates
- *   4. dsa_sparse_mla_decode absorbed-MLA attention over the selected paged fp8
- *                            rows, split along the selected list into
+ *   3. dsa_sparse_mla_decode absorbed-MLA attention over the selected paged fp8
+ *                            rows (the bf16 query split as dsa_quantize_mla_q
+ *                            does), split along the selected list into
  *                            (partial output, natural-log LSE) pairs
- *   5. dsa_lse_merge         merge of the split partials by their LSE
+ *   4. dsa_lse_merge         merge of the split partials by their LSE
+ * dsa_quantize_q and dsa_quantize_mla_q expose the query quantization of
+ * steps 1 and 3 on their own.
  *
  * Conventions shared by every entry point:
  *  - Every array pointer is DEVICE memory owned by the caller.  The library
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -88,7 +89,8 @@ const char* dsa_status_string(int status);
  * The subject page's indexer scores fp8 keys; the query arrives as bf16, so it
  * is brought to fp8 E4M3FN with one power-of-two scale per (row, head):
  * scale = 2^ceil(log2(amax / 448)) (scale 1 for an all-zero head) and
- * code = round-to-nearest-even(q / scale).
+ * code = round-to-nearest-even(q / scale).  dsa_index_scores quantizes its
+ * queries the same way, bit for bit.
  *   q_bf16   [n_rows, n_heads, head_dim] bf16 bit patterns
  *   q_code   [n_rows, n_heads, head_dim] uint8 out
  *   q_scale  [n_rows, n_heads] float32 out
@@ -108,7 +110,8 @@ int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int3
  * Every bf16 element with |q / scale| >= 2^-6 is reproduced exactly (after
  * scaling the head's largest magnitude is above 224, so these are all elements
  * above about 2^-14 of it); smaller ones are off by at most 2^-14 * scale.
- * dsa_sparse_mla_decode computes the logits from these terms.
+ * dsa_sparse_mla_decode splits its query the same way, bit for bit, and
+ * computes the logits from the terms.
  *   q_bf16   [n_rows, n_heads, head_dim] bf16 bit patterns
  *   q_terms  [n_rows, n_heads, 2, head_dim] uint8 out: hi codes, then lo codes
  *   q_scale  [n_rows, n_heads] float32 out
@@ -118,25 +121,14 @@ int dsa_quantize_mla_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, 
                        uint8_t* q_terms, float* q_scale, hipStream_t stream);
 
 /*
- * dsa_prepare_queries -- both query preparations of a decode step in one
- * launch: the same outputs as dsa_quantize_q(q_idx, n_rows, idx_heads,
- * idx_dim, q_code, q_scale) followed by dsa_quantize_mla_q(q_mla, n_rows,
- * mla_heads, mla_dim, q_terms, q_mla_scale), with the same layouts.
- * Supported: idx_dim == 128, mla_dim == 576, idx_heads >= 1, mla_heads >= 1.
- * n_rows == 0 enqueues nothing.
- */
-int dsa_prepare_queries(const uint16_t* q_idx, int32_t n_rows, int32_t idx_heads, int32_t idx_dim,
-                        uint8_t* q_code, float* q_scale, const uint16_t* q_mla, int32_t mla_heads,
-                        int32_t mla_dim, uint8_t* q_terms, float* q_mla_scale, hipStream_t stream);
-
-/*
  * dsa_index_scores -- fp8 lightning-indexer scores (subject page,
  * Modifications, indexer decode: the index-K cache is scored per token).
  *   scores[r][t] = k_scale[t] * sum_h (head_w[r][h] * q_scale[r][h])
  *                  * relu( dec(q_code[r][h]) . dec(k_code[t]) )     for t < row_vis[r]
+ * with (q_code, q_scale) = dsa_quantize_q of q,
  *   scores[r][t] = -inf                      for row_vis[r] <= t < score_stride
  * which equals sum_h w_h * relu(q_h . k_t) for positive scales.
- *   q_code [n_rows, 64, 128] uint8, q_scale [n_rows, 64] f32, head_w [n_rows, 64] f32
+ *   q [n_rows, 64, 128] bf16 bit patterns, head_w [n_rows, 64] f32
  *   k_code [num_pages, page_size, 128] uint8, k_scale [num_pages, page_size] f32
  *   page_table [batch, max_pages] i32, kv_lens [batch] i32
  *   row_req [n_rows] i32, row_vis [n_rows] i32
@@ -147,7 +139,7 @@ int dsa_prepare_queries(const uint16_t* q_idx, int32_t n_rows, int32_t idx_heads
  * Supported: n_heads == 64, head_dim == 128, page_size a power of two in
  * [16, 1024].  All scales must be finite and > 0.
  */
-int dsa_index_scores(const uint8_t* q_code, const float* q_scale, const float* head_w,
+int dsa_index_scores(const uint16_t* q, const float* head_w,
                      const uint8_t* k_code, const float* k_scale, const int32_t* page_table,
                      const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,
                      int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
@@ -192,11 +184,12 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
  * top_k, so a split's range is known before the count is read; when
  * n < top_k the last splits may be empty):
  *   x_t   = dec(codes of row t) * scale of row t       (576 wide)
- *   l_t   = sm_scale * (q[r][h] . x_t),  q = q_scale * (dec(hi) + dec(lo) / 16)
+ *   l_t   = sm_scale * (q'[r][h] . x_t),  q' = scale * (dec(hi) + dec(lo) / 16)
+ * where (hi, lo, scale) is dsa_quantize_mla_q's split of q (q' = q for every
+ * element above about 2^-14 of its head's largest),
  *   o_s   = sum_t e^{l_t - m} x_t[0:512] / sum_t e^{l_t - m},  lse_s = m + ln sum_t e^{l_t - m}
  * Empty split: o_s = 0, lse_s = -inf.
- *   q_terms [n_rows, n_heads, 2, 576] uint8, q_scale [n_rows, n_heads] f32
- *     (the query as dsa_quantize_mla_q prepares it)
+ *   q [n_rows, n_heads, 576] bf16 bit patterns
  *   kv_cache [num_pages, page_size, 640] uint8 (layout above)
  *   page_table [batch, max_pages] i32, row_req / row_vis [n_rows] i32
  *   topk_idx [n_rows, top_k] i32, topk_count [n_rows] i32
@@ -208,8 +201,7 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
  * Supported: n_heads in {16, 32}, page_size a power of two in [16, 1024],
  * 1 <= n_splits <= 64, 1 <= top_k <= 8192.
  */
-int dsa_sparse_mla_decode(const uint8_t* q_terms, const float* q_scale, const uint8_t* kv_cache,
-                          const int32_t* page_table,
+int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
                           const int32_t* row_req, const int32_t* row_vis, const int32_t* topk_idx,
                           const int32_t* topk_count, int32_t n_rows,
                           int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,

@@ -76,19 +76,7 @@ int dsa_quantize_mla_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, 
     return launch_status(dsa::launch_quantize_mla_q(q_bf16, n_rows * n_heads, q_terms, q_scale, stream));
 }
 
-int dsa_prepare_queries(const uint16_t* q_idx, int32_t n_rows, int32_t idx_heads, int32_t idx_dim,
-                        uint8_t* q_code, float* q_scale, const uint16_t* q_mla, int32_t mla_heads,
-                        int32_t mla_dim, uint8_t* q_terms, float* q_mla_scale, hipStream_t stream) {
-    if (n_rows < 0 || idx_heads < 1 || idx_dim < 1 || mla_heads < 1 || mla_dim < 1) return DSA_ERR_SHAPE;
-    if (idx_dim != 128 || mla_dim != 576) return DSA_ERR_UNSUPPORTED;
-    if ((int64_t)n_rows * (idx_heads + mla_heads) > INT32_MAX / 4) return DSA_ERR_SHAPE;
-    if (n_rows == 0) return DSA_OK;
-    if (!q_idx || !q_code || !q_scale || !q_mla || !q_terms || !q_mla_scale) return DSA_ERR_NULL;
-    return launch_status(dsa::launch_prepare_queries(q_idx, n_rows * idx_heads, q_code, q_scale, q_mla,
-                                                     n_rows * mla_heads, q_terms, q_mla_scale, stream));
-}
-
-int dsa_index_scores(const uint8_t* q_code, const float* q_scale, const float* head_w,
+int dsa_index_scores(const uint16_t* q, const float* head_w,
                      const uint8_t* k_code, const float* k_scale, const int32_t* page_table,
                      const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,
                      int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
@@ -101,12 +89,12 @@ int dsa_index_scores(const uint8_t* q_code, const float* q_scale, const float* h
     if (rc != DSA_OK) return rc;
     if (group_rows < 1 || group_rows > 8) return DSA_ERR_SHAPE;
     if (n_rows % group_rows != 0) return DSA_ERR_SHAPE;
-    if (!q_code || !q_scale || !head_w || !k_code || !k_scale || !page_table || !kv_lens ||
+    if (!q || !head_w || !k_code || !k_scale || !page_table || !kv_lens ||
         !row_req || !row_vis || !scores || !status)
         return DSA_ERR_NULL;
     if (n_rows == 0) return DSA_OK;
     dsa::IndexArgs a;
-    a.q_code = q_code; a.q_scale = q_scale; a.head_w = head_w;
+    a.q = q; a.head_w = head_w;
     a.k_code = k_code; a.k_scale = k_scale; a.page_table = page_table; a.kv_lens = kv_lens;
     a.row_req = row_req; a.row_vis = row_vis;
     a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
@@ -147,8 +135,7 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
     return launch_status(dsa::launch_topk(a, stream));
 }
 
-int dsa_sparse_mla_decode(const uint8_t* q_terms, const float* q_scale, const uint8_t* kv_cache,
-                          const int32_t* page_table,
+int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
                           const int32_t* row_req, const int32_t* row_vis, const int32_t* topk_idx,
                           const int32_t* topk_count, int32_t n_rows,
                           int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
@@ -162,13 +149,13 @@ int dsa_sparse_mla_decode(const uint8_t* q_terms, const float* q_scale, const ui
     if (n_heads != 16 && n_heads != 32) return DSA_ERR_UNSUPPORTED;
     int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
     if (rc != DSA_OK) return rc;
-    if (!q_terms || !q_scale || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx ||
+    if (!q || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx ||
         !topk_count || !status)
         return DSA_ERR_NULL;
     if (n_splits == 1 ? !out : (!part_o || !part_lse)) return DSA_ERR_NULL;
     if (n_rows == 0) return DSA_OK;
     dsa::MlaArgs a;
-    a.q_terms = q_terms; a.q_scale = q_scale; a.kv_cache = kv_cache; a.page_table = page_table;
+    a.q = q; a.kv_cache = kv_cache; a.page_table = page_table;
     a.row_req = row_req; a.row_vis = row_vis; a.topk_idx = topk_idx; a.topk_count = topk_count;
     a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
     a.page_size = page_size; a.log2_page = log2i(page_size); a.n_heads = n_heads;

@@ -29,6 +29,7 @@
 // loads of its next 64-token group before computing the current one.
 #include "device_common.h"
 #include "launch.h"
+#include "query_quant.h"
 
 namespace dsa {
 
@@ -109,8 +110,8 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     __shared__ int s_req[G];
     __shared__ int s_vis[G];
     __shared__ int s_page[kMaxChunkPages];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[G > 1 ? G * 64 * kQStride : 16];
-    __shared__ __attribute__((aligned(16))) float s_wq[G > 1 ? G * 64 : 4];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[G * 64 * kQStride];   // fp8 query codes
+    __shared__ __attribute__((aligned(16))) float s_wq[G * 64];              // head weight * query scale
     // One row (decode): the chunk's scores collect here and go out in one
     // burst after the chunk's keys are read (HBM reads slow down markedly
     // when writes are mixed in).  Several rows write as they go.
@@ -137,18 +138,17 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
         s_req[threadIdx.x] = ok ? b : 0;
         s_vis[threadIdx.x] = v;
     }
-    if constexpr (G > 1) {
-        // Queries of the group into LDS (rows padded to kQStride bytes).
-        for (int c = threadIdx.x; c < G * 64 * 8; c += 256) {
-            const int hr = c >> 3, part = c & 7;   // head row (g*64+h), 16-byte part
-            const uint4 v = *reinterpret_cast<const uint4*>(a.q_code + (size_t)(r0 * 64 + hr) * 128 + part * 16);
-            *reinterpret_cast<uint4*>(s_q + hr * kQStride + part * 16) = v;
-        }
-        for (int c = threadIdx.x; c < G * 64; c += 256) {
-            const size_t i = (size_t)r0 * 64 + c;
-            s_wq[c] = a.head_w[i] * a.q_scale[i];
-        }
-    }
+    // The group's bf16 queries, loaded now and quantized once the first keys
+    // are in flight: four threads per head (head row p * 64 + threadIdx / 4
+    // of pass p), elements [32 c, 32 c + 32) each, c = threadIdx % 4.
+    const int qc = threadIdx.x & 3;
+    const int qh = threadIdx.x >> 2;
+    uint4 qraw[G][4];
+#pragma unroll
+    for (int p = 0; p < G; ++p)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            qraw[p][k] = reinterpret_cast<const uint4*>(a.q + ((size_t)r0 * 64 + p * 64 + qh) * 128 + 32 * qc)[k];
     __syncthreads();
 
     const int b = s_req[0];
@@ -183,19 +183,6 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
 
     v8i qa[4];
     float wq[4][4];
-    if constexpr (G == 1) {
-        const int r = r0;
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-            qa[hb] = load_q_operand(a.q_code + ((size_t)r * 64 + hb * 16 + n) * 128, g);
-            pin(qa[hb]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const size_t hi = (size_t)r * 64 + hb * 16 + 4 * g + i;
-                wq[hb][i] = a.head_w[hi] * a.q_scale[hi];
-            }
-        }
-    }
 
     // Loads of the group starting at token tg, branch-free: a block past
     // vmax or on an invalid page reads row n of page 0 instead (always
@@ -256,8 +243,50 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     // hit) rather than branching around the loads.
     KeyGroup ka, kb;
     int tg = t0 + wv * 64;
+    if (tg < t_comp) load_group(tg, ka);
+
+    // Query quantization (the same arithmetic as dsa_quantize_q) into LDS
+    // while the first keys load: the head's amax over its four threads, one
+    // power-of-two scale, fp8 codes.
+#pragma unroll
+    for (int p = 0; p < G; ++p) {
+        float v[32];
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float x[8];
+            bf16x8_to_f32(qraw[p][k], x);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                v[8 * k + u] = x[u];
+                amax = fmaxf(amax, fabsf(x[u]));
+            }
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        const int e = idx_q_exponent(amax);
+        const IdxQFactors f = idx_q_factors(e);
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            w[k] = idx_q_code2(v[4 * k], v[4 * k + 1], f) | (idx_q_code2(v[4 * k + 2], v[4 * k + 3], f) << 16);
+        const int hr = p * 64 + qh;
+        uint4* dst = reinterpret_cast<uint4*>(s_q + hr * kQStride + 32 * qc);
+        dst[0] = uint4{w[0], w[1], w[2], w[3]};
+        dst[1] = uint4{w[4], w[5], w[6], w[7]};
+        if (qc == 0) s_wq[hr] = a.head_w[(size_t)r0 * 64 + hr] * ldexpf(1.0f, e);
+    }
+    lds_sync();
+    if constexpr (G == 1) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            qa[hb] = load_q_operand(s_q + (hb * 16 + n) * kQStride, g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wq[hb][i] = s_wq[hb * 16 + 4 * g + i];
+        }
+    }
+
     if (tg < t_comp) {
-        load_group(tg, ka);
         while (true) {
             const bool m1 = tg + 256 < t_comp;
             load_group(m1 ? tg + 256 : tg, kb);

@@ -9,8 +9,7 @@
 namespace dsa {
 
 struct IndexArgs {
-    const uint8_t* q_code;
-    const float* q_scale;
+    const uint16_t* q;        // [n_rows, 64, 128] bf16
     const float* head_w;
     const uint8_t* k_code;
     const float* k_scale;
@@ -39,8 +38,7 @@ struct TopkArgs {
 };
 
 struct MlaArgs {
-    const uint8_t* q_terms;    // [n_rows, n_heads, 2, 576]: hi then lo fp8 codes
-    const float* q_scale;      // [n_rows, n_heads]
+    const uint16_t* q;         // [n_rows, n_heads, 576] bf16
     const uint8_t* kv_cache;   // [num_pages, page_size, 640]: codes, fp32 scale, pad
     const int32_t* page_table;
     const int32_t* row_req;
@@ -73,9 +71,6 @@ hipError_t launch_quantize_q(const uint16_t* q, int32_t n_pairs, uint8_t* code, 
                              hipStream_t stream);
 hipError_t launch_quantize_mla_q(const uint16_t* q, int32_t n_pairs, uint8_t* terms, float* scale,
                                  hipStream_t stream);
-hipError_t launch_prepare_queries(const uint16_t* q_idx, int32_t n_idx, uint8_t* code, float* scale,
-                                  const uint16_t* q_mla, int32_t n_mla, uint8_t* terms, float* mla_scale,
-                                  hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);

@@ -7,12 +7,11 @@
 //           LDS (rows padded to 592 bytes), with their fp32 scales;
 //   QK      on fp8 matrix cores: the tokens' fp8 bytes are the A operand as
 //           they are (M = tokens), the query the B operand (N = heads).  The
-//           query arrives as two fp8 terms per head, q = s_h (hi + lo / 16)
-//           with s_h a power of two (the bf16 query split once per row, see
-//           quantize_q.hip), so two accumulator chains give the products
-//           without converting any key byte; both terms are gathered into
-//           the last tile buffer at the start and stay in registers for the
-//           whole split.  Wavefront w owns
+//           bf16 query is split exactly into two fp8 terms per head,
+//           q = s_h (hi + lo / 16) with s_h a power of two (query_quant.h),
+//           so two accumulator chains give the products without converting
+//           any key byte; the split is done while the first gathers are in
+//           flight and both terms stay in registers for the whole split.  Wavefront w owns
 //           head block w % HB and 16 HB tokens; K steps of 128 use
 //           v_mfma_f32_16x16x128_f8f6f4, the last 64 bytes
 //           v_mfma_f32_16x16x32_fp8_fp8;
@@ -28,12 +27,12 @@
 // The value rows are the first 512 entries of the same rows (absorbed MLA),
 // so a tile is read from HBM once for both products.
 //
-// Latency hiding: the query terms go out first, as LDS-direct loads into the
-// last tile buffer (free until the first tile's barrier); a split's range of
-// the selected list depends only on top_k, so its entries are loaded
-// together with the row's metadata; the block table is then walked once for
-// the whole split (slot -> page -> physical row, kept in LDS) and the first
-// gathers go out right after it.  Tiles are gathered by LDS-direct loads
+// Latency hiding: a split's range of the selected list depends only on
+// top_k, so its entries are loaded together with the row's metadata and the
+// bf16 query; the block table is then walked once for the whole split
+// (slot -> page -> physical row, kept in LDS), the first gathers go out right
+// after it, and the query is split into its fp8 terms (staged in the last
+// tile buffer, free until the first tile's barrier) while they load.  Tiles are gathered by LDS-direct loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at the wavefront's LDS
 // base + 16 * lane), which need no registers: with four tile buffers, three
 // tiles are in flight while the fourth is computed.  Each wavefront waits
@@ -55,6 +54,7 @@
 // conflict-free as it is.
 #include "device_common.h"
 #include "launch.h"
+#include "query_quant.h"
 
 namespace dsa {
 
@@ -146,9 +146,12 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) float s_m[H];
     __shared__ int s_moved[HB];
     __shared__ int s_bad[NW];   // per wavefront: an entry of the split is invalid
-    // The query terms of the row land in the last tile buffer: term row
-    // 2h + t (t = 0 hi, 1 lo) of head h at kXStride-byte pitch, like a tile.
-    static_assert(2 * H <= kT, "query terms fit one tile buffer");
+    __shared__ float s_qsc[H];  // per-head power-of-two query scale
+    // The query terms are staged in the last tile buffer: hi of head h at
+    // row h, lo at row H + h (kXStride-byte pitch).
+    uint8_t* const s_qh = s_x[NB - 1];
+    uint8_t* const s_ql = s_qh + H * kXStride;
+    static_assert(2 * H * kXStride <= kTileBytes, "query terms fit one tile buffer");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -160,22 +163,6 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     const int r = blockIdx.y;
     const int sp = blockIdx.x;
     const int ns = gridDim.x;
-
-    // Query terms: 2H rows of 576 bytes, contiguous in q_terms, gathered
-    // like a tile's rows (chunk 36, the pad, rereads chunk 0 of its row).
-    // They are the oldest loads of every wavefront, so the waits for any
-    // later load cover them.
-    {
-        const uint8_t* qrow = a.q_terms + (size_t)r * H * (2 * kRowBytes);
-        const uint32_t xl = lds_offset(s_x[NB - 1]);
-        constexpr int kQInsts = (2 * H * kRowChunks + kWave - 1) / kWave;
-#pragma unroll
-        for (int j = wv; j < kQInsts; j += NW) {
-            const int c = min(64 * j + lane, 2 * H * kRowChunks - 1);
-            const int t = c / kRowChunks, part = c - t * kRowChunks;
-            lds_dma16(qrow + (size_t)t * kRowBytes + (part < 36 ? part * 16 : 0), xl + j * 1024);
-        }
-    }
 
     // Row metadata (uniform loads) and the split's range of the selected
     // list.  The range depends only on top_k, so the list entries can be
@@ -199,7 +186,17 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     };
     load_slots(lo);
 
-    const float cq = a.sm_scale * a.q_scale[(size_t)r * H + 16 * hb + nn];
+    // The bf16 query: wavefront wv holds heads wv, wv+NW, ...; lane l has
+    // 16-byte chunk l (and 64 + l for l < 8) of the 1152-byte row.
+    constexpr int kQH = H / NW;   // heads per wavefront
+    uint4 qc0[kQH], qc1[kQH];
+#pragma unroll
+    for (int j = 0; j < kQH; ++j) {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q + ((size_t)r * H + wv + NW * j) * kRowBytes);
+        qc0[j] = *reinterpret_cast<const uint4*>(src + 16 * lane);
+        qc1[j] = uint4{0u, 0u, 0u, 0u};
+        if (lane < 8) qc1[j] = *reinterpret_cast<const uint4*>(src + 16 * (64 + lane));
+    }
 
     bool ok = b_raw >= 0 && b_raw < a.batch && v_raw >= 0 && v_raw <= a.max_pages * a.page_size;
     if (!ok && tid == 0) flag(a.status, DSA_DEV_ROW_RANGE);
@@ -250,31 +247,18 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     static_assert(MlaGeom<4>::kRowsCap <= 2048, "a four-buffer split is one batch (kBatch >= 2048)");
     const bool wave_bad = __ballot(bad) != 0ull;
     if (lane == 0) s_bad[wv] = wave_bad;
-    // Every load of the wavefronts done (the query terms included, which the
-    // compiler does not track), so the terms are in LDS after the barrier and
-    // no load the compiler tracks is outstanding once the gathers go out.
+    // Every load of the wavefronts done (the bf16 query included), so no
+    // load the compiler tracks is outstanding once the gathers go out.
     wait_vm<0>();
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kQH; ++j) {
+        pin(qc0[j].x); pin(qc0[j].y); pin(qc0[j].z); pin(qc0[j].w);
+        pin(qc1[j].x); pin(qc1[j].y); pin(qc1[j].z); pin(qc1[j].w);
+    }
     bool any_bad = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) any_bad |= s_bad[w] != 0;
-
-    // The query operand of this lane (head 16 hb + nn, lane group g) for the
-    // whole split: 9 chunks per term, in the QK K order.
-    v4i qh[9], ql[9];
-    {
-        const uint8_t* qh_row = s_x[NB - 1] + (2 * (16 * hb + nn)) * kXStride;
-        const uint8_t* ql_row = qh_row + kXStride;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                qh[2 * p + h] = *reinterpret_cast<const v4i*>(qh_row + 16 * qk_chunk(p, h, g));
-                ql[2 * p + h] = *reinterpret_cast<const v4i*>(ql_row + 16 * qk_chunk(p, h, g));
-            }
-        qh[8] = *reinterpret_cast<const v4i*>(qh_row + 16 * (32 + g));
-        ql[8] = *reinterpret_cast<const v4i*>(ql_row + 16 * (32 + g));
-    }
 
     // Row of tile-local token t of the tile starting at split entry `base`.
     // The read is clamped into the array and its value discarded past the end,
@@ -326,6 +310,53 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
     for (int j = 0; j < NB - 1; ++j)
         if (j < n_tiles) issue(j, lo + j * kT);
+
+    // Query -> two fp8 terms per head (query_quant.h) while they load.
+#pragma unroll
+    for (int j = 0; j < kQH; ++j) {
+        const int hq = wv + NW * j;
+        float v0[8], v1[8];
+        bf16x8_to_f32(qc0[j], v0);
+        bf16x8_to_f32(qc1[j], v1);
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fmaxf(fabsf(v0[k]), fabsf(v1[k])));
+        const float sq = mla_q_scale(wave_max(amax));
+        const float inv = 1.0f / sq;                       // exact: sq is a power of two
+        uint32_t hw[4], lw[4];
+        mla_q_split4(v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv, hw[0], lw[0]);
+        mla_q_split4(v0[4] * inv, v0[5] * inv, v0[6] * inv, v0[7] * inv, hw[1], lw[1]);
+        mla_q_split4(v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv, hw[2], lw[2]);
+        mla_q_split4(v1[4] * inv, v1[5] * inv, v1[6] * inv, v1[7] * inv, hw[3], lw[3]);
+        // chunk l covers bf16 elements [8l, 8l+8): fp8 bytes [8l, 8l+8)
+        *reinterpret_cast<uint2*>(s_qh + hq * kXStride + 8 * lane) = uint2{hw[0], hw[1]};
+        *reinterpret_cast<uint2*>(s_ql + hq * kXStride + 8 * lane) = uint2{lw[0], lw[1]};
+        if (lane < 8) {
+            *reinterpret_cast<uint2*>(s_qh + hq * kXStride + 8 * (64 + lane)) = uint2{hw[2], hw[3]};
+            *reinterpret_cast<uint2*>(s_ql + hq * kXStride + 8 * (64 + lane)) = uint2{lw[2], lw[3]};
+        }
+        if (lane == 0) s_qsc[hq] = sq;
+    }
+    lds_sync();
+
+    // The query operand of this lane (head 16 hb + nn, lane group g) for the
+    // whole split: 9 chunks per term, in the QK K order.
+    v4i qh[9], ql[9];
+    {
+        const uint8_t* qh_row = s_qh + (16 * hb + nn) * kXStride;
+        const uint8_t* ql_row = s_ql + (16 * hb + nn) * kXStride;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                qh[2 * p + h] = *reinterpret_cast<const v4i*>(qh_row + 16 * qk_chunk(p, h, g));
+                ql[2 * p + h] = *reinterpret_cast<const v4i*>(ql_row + 16 * qk_chunk(p, h, g));
+            }
+        qh[8] = *reinterpret_cast<const v4i*>(qh_row + 16 * (32 + g));
+        ql[8] = *reinterpret_cast<const v4i*>(ql_row + 16 * (32 + g));
+    }
+
+    const float cq = a.sm_scale * s_qsc[16 * hb + nn];
 
     // Softmax state: in the QK layout a lane owns head 16 hb + nn (m_run,
     // and l_run: this wavefront's share of the denominator); in the PV

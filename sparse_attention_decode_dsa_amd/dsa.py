@@ -17,7 +17,7 @@ import os
 
 import torch
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN"}
@@ -35,12 +35,11 @@ _SIGS = {
     "dsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dsa_quantize_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_quantize_mla_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
-    "dsa_prepare_queries": ([_p, _i32, _i32, _i32, _p, _p, _p, _i32, _i32, _p, _p, _p], ctypes.c_int),
-    "dsa_index_scores": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+    "dsa_index_scores": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
     "dsa_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
     "dsa_topk": ([_p, _i32, _p, _i32, _i32, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p], ctypes.c_int),
-    "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+    "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "dsa_lse_merge": ([_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
 }
@@ -138,47 +137,22 @@ def quantize_mla_q(q_bf16, q_terms=None, q_scale=None, stream=None):
     return q_terms, q_scale
 
 
-def prepare_queries(q_idx, q_mla, q_code=None, q_scale=None, q_terms=None, q_mla_scale=None,
-                    stream=None):
-    """quantize_q(q_idx) and quantize_mla_q(q_mla) in one launch ->
-    (q_code, q_scale, q_terms, q_mla_scale)."""
-    r, hi, di = q_idx.shape
-    rm, hm, dm = q_mla.shape
-    if rm != r:
-        raise DsaError(f"q_idx has {r} rows, q_mla {rm}")
-    dev = q_idx.device
-    if q_code is None:
-        q_code = torch.empty((r, hi, di), dtype=torch.uint8, device=dev)
-    if q_scale is None:
-        q_scale = torch.empty((r, hi), dtype=torch.float32, device=dev)
-    if q_terms is None:
-        q_terms = torch.empty((r, hm, 2, dm), dtype=torch.uint8, device=dev)
-    if q_mla_scale is None:
-        q_mla_scale = torch.empty((r, hm), dtype=torch.float32, device=dev)
-    _check(lib().dsa_prepare_queries(
-        _ptr(q_idx, _BF16, "q_idx"), r, hi, di, _ptr(q_code, _FP8, "q_code"),
-        _ptr(q_scale, torch.float32, "q_scale"), _ptr(q_mla, _BF16, "q_mla"), hm, dm,
-        _ptr(q_terms, _FP8, "q_terms"), _ptr(q_mla_scale, torch.float32, "q_mla_scale"),
-        _stream(stream)), "dsa_prepare_queries")
-    return q_code, q_scale, q_terms, q_mla_scale
-
-
-def index_scores(q_code, q_scale, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis,
+def index_scores(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis,
                  group_rows: int = 1, score_stride: int | None = None, scores=None, status=None,
                  stream=None):
-    """fp8 indexer scores [R, score_stride] f32 (-inf past each row's span)."""
-    r, h, d = q_code.shape
+    """fp8 indexer scores [R, score_stride] f32 (-inf past each row's span) of
+    the bf16 queries q [R, 64, 128] (quantized in the kernel as quantize_q does)."""
+    r, h, d = q.shape
     n_pages, p, dk = k_code.shape
     batch, max_pages = page_table.shape
     if score_stride is None:
         score_stride = scores.shape[1] if scores is not None else max_pages * p
     if scores is None:
-        scores = torch.empty((r, score_stride), dtype=torch.float32, device=q_code.device)
+        scores = torch.empty((r, score_stride), dtype=torch.float32, device=q.device)
     if status is None:
-        status = new_status(q_code.device)
+        status = new_status(q.device)
     _check(lib().dsa_index_scores(
-        _ptr(q_code, _FP8, "q_code"), _ptr(q_scale, torch.float32, "q_scale"),
-        _ptr(head_w, torch.float32, "head_w"), _ptr(k_code, _FP8, "k_code"),
+        _ptr(q, _BF16, "q"), _ptr(head_w, torch.float32, "head_w"), _ptr(k_code, _FP8, "k_code"),
         _ptr(k_scale, torch.float32, "k_scale"), _ptr(page_table, torch.int32, "page_table"),
         _ptr(kv_lens, torch.int32, "kv_lens"), _ptr(row_req, torch.int32, "row_req"),
         _ptr(row_vis, torch.int32, "row_vis"), r, batch, n_pages, max_pages, p, h, d, group_rows,
@@ -215,23 +189,21 @@ def topk(scores, row_vis, top_k: int, n_splits: int = 1, workspace=None, topk_id
     return topk_idx, topk_count, status
 
 
-def sparse_mla_decode(q_terms, q_scale, kv_cache, page_table, row_req, row_vis, topk_idx, topk_count,
+def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_count,
                       n_splits: int = 1, sm_scale: float = 1.0 / 24.0, part_o=None, part_lse=None,
                       out=None, out_lse=None, status=None, stream=None):
-    """Split-K sparse MLA.  n_splits == 1 -> (out bf16 [R,H,512], out_lse f32 [R,H]);
-    otherwise -> (part_o f32 [R,H,S,512], part_lse f32 [R,H,S]).  The query is
-    given as ``quantize_mla_q`` prepares it; kv_cache is the packed uint8
-    [NP, P, 640] MLA cache (codes, fp32 scale at byte 576, pad)."""
-    r, h, two, dq = q_terms.shape
-    if two != 2 or dq != 576 or tuple(q_scale.shape) != (r, h):
-        raise DsaError(f"q_terms must be [R, H, 2, 576] with q_scale [R, H], got {tuple(q_terms.shape)}, "
-                       f"{tuple(q_scale.shape)}")
+    """Split-K sparse MLA of the bf16 query q [R, H, 576] (split in the kernel
+    as quantize_mla_q does).  n_splits == 1 -> (out bf16 [R,H,512], out_lse f32
+    [R,H]); otherwise -> (part_o f32 [R,H,S,512], part_lse f32 [R,H,S]).
+    kv_cache is the packed uint8 [NP, P, 640] MLA cache (codes, fp32 scale at
+    byte 576, pad)."""
+    r, h, dq = q.shape
     n_pages, p, row_bytes = kv_cache.shape
     if row_bytes != 640:
         raise DsaError(f"kv_cache rows must be 640 bytes, got {row_bytes}")
     batch, max_pages = page_table.shape
     top_k = topk_idx.shape[1]
-    dev = q_terms.device
+    dev = q.device
     if status is None:
         status = new_status(dev)
     if n_splits == 1:
@@ -245,8 +217,7 @@ def sparse_mla_decode(q_terms, q_scale, kv_cache, page_table, row_req, row_vis, 
         if part_lse is None:
             part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
     _check(lib().dsa_sparse_mla_decode(
-        _ptr(q_terms, _FP8, "q_terms"), _ptr(q_scale, torch.float32, "q_scale"),
-        _ptr(kv_cache, torch.uint8, "kv_cache"),
+        _ptr(q, _BF16, "q"), _ptr(kv_cache, torch.uint8, "kv_cache"),
         _ptr(page_table, torch.int32, "page_table"), _ptr(row_req, torch.int32, "row_req"),
         _ptr(row_vis, torch.int32, "row_vis"), _ptr(topk_idx, torch.int32, "topk_idx"),
         _ptr(topk_count, torch.int32, "topk_count"), r, batch, n_pages, max_pages, p, h, top_k,
@@ -278,9 +249,8 @@ def lse_merge(part_o, part_lse, out=None, out_lse=None, stream=None):
 
 class DecodeStep:
     """All buffers of one DSA decode step for fixed inputs, allocated once;
-    ``run()`` enqueues query preparation -> scores -> top-k -> sparse MLA ->
-    merge on the given (else the current) stream without allocating or
-    synchronising."""
+    ``run()`` enqueues scores -> top-k -> sparse MLA -> merge on the given
+    (else the current) stream without allocating or synchronising."""
 
     def __init__(self, inp, index_splits: int | None = None, attn_splits: int | None = None,
                  group_rows: int | None = None, score_stride: int | None = None):
@@ -295,10 +265,6 @@ class DecodeStep:
         k = inp.top_k
         # Rows start 16-byte aligned (the top-k then reads them in 16-byte loads).
         self.score_stride = score_stride or max(64, (inp.max_vis() + 63) // 64 * 64)
-        self.q_code = torch.empty((r, 64, 128), dtype=torch.uint8, device=dev)
-        self.q_scale = torch.empty((r, 64), dtype=torch.float32, device=dev)
-        self.q_terms = torch.empty((r, h, 2, 576), dtype=torch.uint8, device=dev)
-        self.q_mla_scale = torch.empty((r, h), dtype=torch.float32, device=dev)
         self.scores = torch.empty((r, self.score_stride), dtype=torch.float32, device=dev)
         need = topk_workspace_size(r, k, self.index_splits)
         self.workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
@@ -313,20 +279,18 @@ class DecodeStep:
 
     def run(self, stream=None):
         i = self.inp
-        prepare_queries(i.q_idx, i.q_mla, self.q_code, self.q_scale, self.q_terms, self.q_mla_scale,
-                        stream=stream)
-        index_scores(self.q_code, self.q_scale, i.head_w, i.k_code, i.k_scale, i.page_table,
+        index_scores(i.q_idx, i.head_w, i.k_code, i.k_scale, i.page_table,
                      i.kv_lens, i.row_req, i.row_vis, group_rows=self.group_rows,
                      score_stride=self.score_stride, scores=self.scores, status=self.status,
                      stream=stream)
         topk(self.scores, i.row_vis, i.top_k, self.index_splits, workspace=self.workspace,
              topk_idx=self.topk_idx, topk_count=self.topk_count, status=self.status, stream=stream)
         if self.attn_splits == 1:
-            sparse_mla_decode(self.q_terms, self.q_mla_scale, i.kv_cache, i.page_table, i.row_req,
+            sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req,
                               i.row_vis, self.topk_idx, self.topk_count, 1, i.sm_scale, out=self.out,
                               out_lse=self.out_lse, status=self.status, stream=stream)
         else:
-            sparse_mla_decode(self.q_terms, self.q_mla_scale, i.kv_cache, i.page_table, i.row_req,
+            sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req,
                               i.row_vis, self.topk_idx, self.topk_count, self.attn_splits, i.sm_scale,
                               part_o=self.part_o, part_lse=self.part_lse, status=self.status,
                               stream=stream)

@@ -32,7 +32,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_quantize_mla_q",
-            "dsa_prepare_queries", "dsa_index_scores",
+            "dsa_index_scores",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_merge"} <= set(names)
     raw = ctypes.CDLL(dsa.lib_path())
     for n in names:
@@ -50,7 +50,7 @@ def test_abi_version_and_status_strings(L):
 
 
 def _idx(L, **kw):
-    a = dict(q_code=P, q_scale=P, head_w=P, k_code=P, k_scale=P, page_table=P, kv_lens=P,
+    a = dict(q=P, head_w=P, k_code=P, k_scale=P, page_table=P, kv_lens=P,
              row_req=P, row_vis=P, n_rows=4, batch=2, num_pages=10, max_pages=5, page_size=256,
              n_heads=64, head_dim=128, group_rows=1, scores=P, score_stride=1280, status=P,
              stream=None)
@@ -69,7 +69,7 @@ def test_index_scores_validation(L):
     assert _idx(L, group_rows=3) == SHAPE      # 4 rows not divisible by 3
     assert _idx(L, group_rows=9, n_rows=9) == SHAPE
     assert _idx(L, score_stride=0) == SHAPE
-    assert _idx(L, q_code=None) == NULL
+    assert _idx(L, q=None) == NULL
     assert _idx(L, status=None) == NULL
     assert _idx(L, n_rows=0) == OK             # nothing to enqueue
 
@@ -97,7 +97,7 @@ def test_topk_validation_and_workspace(L):
 
 
 def _mla(L, **kw):
-    a = dict(q_terms=P, q_scale=P, kv_cache=P, page_table=P, row_req=P, row_vis=P, topk_idx=P,
+    a = dict(q=P, kv_cache=P, page_table=P, row_req=P, row_vis=P, topk_idx=P,
              topk_count=P, n_rows=4, batch=4, num_pages=100, max_pages=20, page_size=256,
              n_heads=32, top_k=2048, n_splits=4, sm_scale=0.04, part_o=P, part_lse=P, out=None,
              out_lse=None, status=P, stream=None)
@@ -115,8 +115,7 @@ def test_sparse_mla_validation(L):
     assert _mla(L, part_o=None) == NULL                      # split path needs partials
     assert _mla(L, n_splits=1, out=None) == NULL             # lone split needs out
     assert _mla(L, page_size=48) == UNSUP
-    assert _mla(L, q_terms=None) == NULL
-    assert _mla(L, q_scale=None) == NULL
+    assert _mla(L, q=None) == NULL
     assert _mla(L, n_rows=0) == OK
 
 
@@ -139,10 +138,3 @@ def test_lse_merge_and_quantize_validation(L):
     assert qm(P, 4, 0, 576, P, P, None) == SHAPE
     assert qm(P, 4, 32, 576, P, None, None) == NULL
     assert qm(P, 0, 32, 576, P, P, None) == OK
-    pq = L.dsa_prepare_queries
-    assert pq(P, 4, 64, 64, P, P, P, 32, 576, P, P, None) == UNSUP
-    assert pq(P, 4, 64, 128, P, P, P, 32, 512, P, P, None) == UNSUP
-    assert pq(P, -1, 64, 128, P, P, P, 32, 576, P, P, None) == SHAPE
-    assert pq(P, 4, 64, 128, P, P, P, 0, 576, P, P, None) == SHAPE
-    assert pq(P, 4, 64, 128, P, P, None, 32, 576, P, P, None) == NULL
-    assert pq(P, 0, 64, 128, P, P, P, 32, 576, P, P, None) == OK

@@ -33,8 +33,11 @@ def compare_step(inp, step, rows, max_swap_rows=None):
     rows = list(rows)
     sub = W.subset(inp, rows)
     ref = O.decode_step(W.as_numpy(sub), step.index_splits, step.attn_splits)
-    np.testing.assert_array_equal(step.q_code[rows].cpu().numpy(), ref["q_code"])
-    np.testing.assert_array_equal(step.q_scale[rows].cpu().double().numpy(), ref["q_scale"])
+    # The indexer quantizes its queries in the kernel with the helpers that
+    # quantize_q runs on its own: the codes of this workload's queries.
+    q_code, q_scale = dsa.quantize_q(inp.q_idx[rows].contiguous())
+    np.testing.assert_array_equal(q_code.cpu().numpy(), ref["q_code"])
+    np.testing.assert_array_equal(q_scale.cpu().double().numpy(), ref["q_scale"])
     vis = sub.row_vis.numpy()
     g_scores = step.scores[rows].cpu().double().numpy()
     r_scores = np.full_like(g_scores, -np.inf)
@@ -63,12 +66,11 @@ def mla_on_oracle_selection(sub, ref, n_splits):
     idx = torch.from_numpy(ref["topk_idx"].astype(np.int32)).cuda()
     cnt = torch.from_numpy(ref["topk_count"].astype(np.int32)).cuda()
     st = dsa.new_status()
-    qt, qs = dsa.quantize_mla_q(g.q_mla)
     if n_splits == 1:
-        out, lse, _ = dsa.sparse_mla_decode(qt, qs, g.kv_cache, g.page_table, g.row_req,
+        out, lse, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_cache, g.page_table, g.row_req,
                                             g.row_vis, idx, cnt, 1, g.sm_scale, status=st)
     else:
-        po, pl, _ = dsa.sparse_mla_decode(qt, qs, g.kv_cache, g.page_table, g.row_req,
+        po, pl, _ = dsa.sparse_mla_decode(g.q_mla, g.kv_cache, g.page_table, g.row_req,
                                           g.row_vis, idx, cnt, n_splits, g.sm_scale, status=st)
         out, lse = dsa.lse_merge(po, pl)
     torch.cuda.synchronize()
@@ -122,19 +124,6 @@ def test_quantize_mla_q_terms():
     exact = y >= 2.0 ** -6
     assert torch.equal(rec[exact], x[exact])
     assert ((rec - x).abs()[~exact] <= 2.0 ** -14 * scale[..., None].expand_as(x)[~exact]).all()
-
-
-def test_prepare_queries_equals_separate_calls():
-    """The one-launch preparation writes exactly what the two separate calls do."""
-    g = torch.Generator().manual_seed(12)
-    qi = (torch.randn(7, 64, 128, generator=g) * 3).to(torch.bfloat16).cuda()
-    qm = (torch.randn(7, 16, 576, generator=g) * 5).to(torch.bfloat16).cuda()
-    code, sc, terms, msc = dsa.prepare_queries(qi, qm)
-    code2, sc2 = dsa.quantize_q(qi)
-    terms2, msc2 = dsa.quantize_mla_q(qm)
-    torch.cuda.synchronize()
-    assert torch.equal(code, code2) and torch.equal(sc, sc2)
-    assert torch.equal(terms, terms2) and torch.equal(msc, msc2)
 
 
 # ------------------------------------------------------------------ top-k alone
