@@ -31,6 +31,8 @@
 #include "launch.h"
 #include "query_quant.h"
 
+#include <climits>
+
 namespace dsa {
 
 namespace {
@@ -97,73 +99,97 @@ __device__ __forceinline__ float group_dot(const v8i (&qa)[4], const float (&wq)
     return __uint_as_float(w[0]) + __uint_as_float(w[1]);
 }
 
+// Row-groups a balanced launch can schedule (their tile counts live in LDS;
+// fewer at eight rows a group, whose query codes take most of the LDS).
 template <int G>
-__global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
+constexpr int max_balanced_groups() { return G > 4 ? 512 : 1024; }
+
+template <int G>
+struct IndexSmem {
+    int req[G];
+    int vis[G];   // spans checked against the launch's bounds (-1: reported invalid)
+    int vok[G];   // spans also checked against kv_len (0 for an invalid row)
+    int page[kMaxChunkPages];
+    __attribute__((aligned(16))) uint8_t q[G * 64 * kQStride];   // fp8 query codes
+    __attribute__((aligned(16))) float wq[G * 64];              // head weight * query scale
+    // One row (decode): a range's scores collect here and go out in one
+    // burst after its keys are read (HBM reads slow down markedly when
+    // writes are mixed in).  Several rows write as they go.
+    __attribute__((aligned(16))) float sc[G == 1 ? kMaxChunk : 4];
+    int pre[max_balanced_groups<G>() + 1];   // balanced launch: first tile of each group
+    uint32_t scan[256 / kWave + 1];
+};
+
+// Scores of rows [r0, r0 + G) at tokens [t0, t_end) (t0 a multiple of 64,
+// t_end - t0 <= kMaxChunk; -inf where a row's span ends) and -inf over
+// [fill_lo, fill_hi).  `report`: this call reports the rows' geometry errors
+// (one call per row does).  `quantize`: the group's queries are not in LDS
+// yet (the previous call, if any, was for another group).
+template <int G>
+__device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G>& s, int r0, int t0, int t_end,
+                                            int fill_lo, int fill_hi, bool report, bool quantize) {
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
-    const int r0 = blockIdx.y * G;
-    const int t0 = blockIdx.x * a.chunk;
-    const int t_end = min(t0 + a.chunk, a.score_stride);
+    __syncthreads();   // the previous range is done with the shared arrays
 
-    __shared__ int s_req[G];
-    __shared__ int s_vis[G];
-    __shared__ int s_page[kMaxChunkPages];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[G * 64 * kQStride];   // fp8 query codes
-    __shared__ __attribute__((aligned(16))) float s_wq[G * 64];              // head weight * query scale
-    // One row (decode): the chunk's scores collect here and go out in one
-    // burst after the chunk's keys are read (HBM reads slow down markedly
-    // when writes are mixed in).  Several rows write as they go.
-    __shared__ __attribute__((aligned(16))) float s_sc[G == 1 ? kMaxChunk : 4];
-
-    // Row geometry, checked once per row.
+    // Row geometry, in two steps so that the block-table loads need not
+    // wait for kv_lens: the request and span are checked against the
+    // launch's bounds now; the span against the request's kv_len below,
+    // alongside the block-table loads.
     if (threadIdx.x < G) {
         const int r = r0 + threadIdx.x;
         const int b = a.row_req[r];
         int v = a.row_vis[r];
         const int b0 = a.row_req[r0];
-        bool ok = b >= 0 && b < a.batch;
-        if (ok) {
-            const int kv = a.kv_lens[b];
-            ok = v >= 0 && v <= kv && kv <= a.max_pages * a.page_size && v <= a.score_stride;
-        }
+        const bool ok = b >= 0 && b < a.batch && v >= 0 && v <= a.score_stride &&
+                        v <= a.max_pages * a.page_size;
         if (!ok) {
-            if (blockIdx.x == 0) flag(a.status, DSA_DEV_ROW_RANGE);
-            v = 0;
+            if (report) flag(a.status, DSA_DEV_ROW_RANGE);
+            v = -1;   // reported; no second report below
         } else if (b != b0) {
-            if (blockIdx.x == 0) flag(a.status, DSA_DEV_GROUP);
-            v = 0;
+            if (report) flag(a.status, DSA_DEV_GROUP);
+            v = -1;
         }
-        s_req[threadIdx.x] = ok ? b : 0;
-        s_vis[threadIdx.x] = v;
+        s.req[threadIdx.x] = ok ? b : 0;
+        s.vis[threadIdx.x] = v;
     }
-    // The group's bf16 queries, loaded now and quantized once the first keys
-    // are in flight: four threads per head (head row p * 64 + threadIdx / 4
-    // of pass p), elements [32 c, 32 c + 32) each, c = threadIdx % 4.
+    // The group's bf16 queries and head weights, loaded now (before any key,
+    // so that no wait for them also waits for keys) and quantized once the
+    // first keys are in flight: four threads per head (head row
+    // p * 64 + threadIdx / 4 of pass p), elements [32 c, 32 c + 32) each,
+    // c = threadIdx % 4.
     const int qc = threadIdx.x & 3;
     const int qh = threadIdx.x >> 2;
     uint4 qraw[G][4];
+    float hw[G];   // head weight of this thread's head in each pass (used by qc == 0)
+    if (quantize) {
 #pragma unroll
-    for (int p = 0; p < G; ++p)
+        for (int p = 0; p < G; ++p) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            qraw[p][k] = reinterpret_cast<const uint4*>(a.q + ((size_t)r0 * 64 + p * 64 + qh) * 128 + 32 * qc)[k];
+            for (int k = 0; k < 4; ++k)
+                qraw[p][k] = reinterpret_cast<const uint4*>(a.q + ((size_t)r0 * 64 + p * 64 + qh) * 128 + 32 * qc)[k];
+            hw[p] = a.head_w[(size_t)r0 * 64 + p * 64 + qh];
+        }
+    }
     __syncthreads();
 
-    const int b = s_req[0];
-    int vmax = 0;
+    const int b = s.req[0];
+    int vmax = 0;   // longest span before the kv_len check (a superset)
 #pragma unroll
-    for (int j = 0; j < G; ++j) vmax = max(vmax, s_vis[j]);
+    for (int j = 0; j < G; ++j) vmax = max(vmax, s.vis[j]);
     const int pmask = a.page_size - 1;
     // Tokens [t0, t_comp) are computed in 64-token groups; the rest of the
-    // chunk only needs -inf.
+    // range only needs -inf.
     const int t_comp = min(t_end, t0 + ((max(vmax - t0, 0) + 63) & ~63));
 
-    // Block table of the chunk, once: page ids of the pages [t0, t_comp)
-    // touches (-1 for invalid ones, which are reported).
+    // Block table of the range, once: page ids of the pages [t0, t_comp)
+    // touches (-1 for invalid ones), and the spans against kv_len.  An
+    // invalid page is reported only if it lies inside a checked span.
+    const int p0 = t0 >> a.log2_page;
+    int bad_from = INT_MAX;   // first token of an invalid page this thread saw
     {
-        const int p0 = t0 >> a.log2_page;
         const int np = t_comp > t0 ? ((t_comp - 1) >> a.log2_page) - p0 + 1 : 0;
         const int* pt = a.page_table + (size_t)b * a.max_pages;
         for (int i = threadIdx.x; i < np; i += 256) {
@@ -171,15 +197,31 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
             if (((p0 + i) << a.log2_page) < vmax) {
                 page = pt[p0 + i];
                 if (page < 0 || page >= a.num_pages) {
-                    flag(a.status, DSA_DEV_PAGE_OOB);
+                    bad_from = min(bad_from, (p0 + i) << a.log2_page);
                     page = -1;
                 }
             }
-            s_page[i] = page;
+            s.page[i] = page;
         }
     }
+    if (threadIdx.x < G) {
+        int v = s.vis[threadIdx.x];
+        if (v >= 0) {
+            const int kv = a.kv_lens[s.req[threadIdx.x]];
+            if (v > kv || kv > a.max_pages * a.page_size) {
+                if (report) flag(a.status, DSA_DEV_ROW_RANGE);
+                v = 0;
+            }
+        }
+        s.vok[threadIdx.x] = max(v, 0);
+    }
     __syncthreads();
-    const int p0 = t0 >> a.log2_page;
+    {
+        int vchk = 0;
+#pragma unroll
+        for (int j = 0; j < G; ++j) vchk = max(vchk, s.vok[j]);
+        if (bad_from < vchk) flag(a.status, DSA_DEV_PAGE_OOB);
+    }
 
     v8i qa[4];
     float wq[4][4];
@@ -193,12 +235,12 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int tb = tg + 16 * j;
-            const int page = tb < vmax ? s_page[(tb >> a.log2_page) - p0] : -1;
+            const int page = tb < vmax ? s.page[(tb >> a.log2_page) - p0] : -1;
             const size_t row = page >= 0 ? (size_t)page * a.page_size + (tb & pmask) + n : (size_t)n;
             kg.b[j] = load_q_operand(a.k_code + row * 128, g);
         }
         const int t = tg + lane;
-        const int page = t < vmax ? s_page[(t >> a.log2_page) - p0] : -1;
+        const int page = t < vmax ? s.page[(t >> a.log2_page) - p0] : -1;
         kg.ok = page >= 0;
         kg.scale = a.k_scale[page >= 0 ? (size_t)page * a.page_size + (t & pmask) : 0];
     };
@@ -214,78 +256,93 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
 #pragma unroll 1
         for (int rr = 0; rr < G; ++rr) {
             const int r = r0 + rr;
-            const int v = s_vis[rr];
+            const int v = s.vok[rr];
             float mine = -INFINITY;
             if (tg < v) {
                 if constexpr (G > 1) {
 #pragma unroll
                     for (int hb = 0; hb < 4; ++hb) {
-                        qa[hb] = load_q_operand(s_q + (rr * 64 + hb * 16 + n) * kQStride, g);
+                        qa[hb] = load_q_operand(s.q + (rr * 64 + hb * 16 + n) * kQStride, g);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) wq[hb][i] = s_wq[rr * 64 + hb * 16 + 4 * g + i];
+                        for (int i = 0; i < 4; ++i) wq[hb][i] = s.wq[rr * 64 + hb * 16 + 4 * g + i];
                     }
                 }
                 const float sc = group_dot(qa, wq, kg.b) * kg.scale;
                 if (kg.ok && t < v) mine = sc;
             }
             if constexpr (G == 1) {
-                if (t < t_end) s_sc[t - t0] = mine;
+                if (t < t_end) s.sc[t - t0] = mine;
             } else {
                 if (t < t_end) a.scores[(size_t)r * a.score_stride + t] = mine;
             }
         }
     };
 
-    // Two key buffers in turn: the loads of the next group are in flight
-    // while the current one is computed, and no register copy forces a wait
-    // on them before the next loads go out.
-    // The last prefetch of a wavefront re-reads its current group (an L2
-    // hit) rather than branching around the loads.
     KeyGroup ka, kb;
     int tg = t0 + wv * 64;
+    if (quantize) {
+        // The query loads are long done; consuming them here, before any key
+        // load goes out, keeps the compiler from waiting for keys as well
+        // when the quantization below first reads them.
+#pragma unroll
+        for (int p = 0; p < G; ++p) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                pin(qraw[p][k].x); pin(qraw[p][k].y); pin(qraw[p][k].z); pin(qraw[p][k].w);
+            }
+            pin(hw[p]);
+        }
+    }
     if (tg < t_comp) load_group(tg, ka);
 
-    // Query quantization (the same arithmetic as dsa_quantize_q) into LDS
-    // while the first keys load: the head's amax over its four threads, one
-    // power-of-two scale, fp8 codes.
+    if (quantize) {
+        // Query quantization (the same arithmetic as dsa_quantize_q) into LDS
+        // while the first keys load: the head's amax over its four threads,
+        // one power-of-two scale, fp8 codes.
 #pragma unroll
-    for (int p = 0; p < G; ++p) {
-        float v[32];
-        float amax = 0.0f;
+        for (int p = 0; p < G; ++p) {
+            float v[32];
+            float amax = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float x[8];
-            bf16x8_to_f32(qraw[p][k], x);
+            for (int k = 0; k < 4; ++k) {
+                float x[8];
+                bf16x8_to_f32(qraw[p][k], x);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                v[8 * k + u] = x[u];
-                amax = fmaxf(amax, fabsf(x[u]));
+                for (int u = 0; u < 8; ++u) {
+                    v[8 * k + u] = x[u];
+                    amax = fmaxf(amax, fabsf(x[u]));
+                }
             }
-        }
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        const int e = idx_q_exponent(amax);
-        const IdxQFactors f = idx_q_factors(e);
-        uint32_t w[8];
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            const int e = idx_q_exponent(amax);
+            const IdxQFactors f = idx_q_factors(e);
+            uint32_t w[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            w[k] = idx_q_code2(v[4 * k], v[4 * k + 1], f) | (idx_q_code2(v[4 * k + 2], v[4 * k + 3], f) << 16);
-        const int hr = p * 64 + qh;
-        uint4* dst = reinterpret_cast<uint4*>(s_q + hr * kQStride + 32 * qc);
-        dst[0] = uint4{w[0], w[1], w[2], w[3]};
-        dst[1] = uint4{w[4], w[5], w[6], w[7]};
-        if (qc == 0) s_wq[hr] = a.head_w[(size_t)r0 * 64 + hr] * ldexpf(1.0f, e);
+            for (int k = 0; k < 8; ++k)
+                w[k] = idx_q_code2(v[4 * k], v[4 * k + 1], f) | (idx_q_code2(v[4 * k + 2], v[4 * k + 3], f) << 16);
+            const int hr = p * 64 + qh;
+            uint4* dst = reinterpret_cast<uint4*>(s.q + hr * kQStride + 32 * qc);
+            dst[0] = uint4{w[0], w[1], w[2], w[3]};
+            dst[1] = uint4{w[4], w[5], w[6], w[7]};
+            if (qc == 0) s.wq[hr] = hw[p] * ldexpf(1.0f, e);
+        }
+        lds_sync();
     }
-    lds_sync();
     if constexpr (G == 1) {
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
-            qa[hb] = load_q_operand(s_q + (hb * 16 + n) * kQStride, g);
+            qa[hb] = load_q_operand(s.q + (hb * 16 + n) * kQStride, g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wq[hb][i] = s_wq[hb * 16 + 4 * g + i];
+            for (int i = 0; i < 4; ++i) wq[hb][i] = s.wq[hb * 16 + 4 * g + i];
         }
     }
 
+    // Two key buffers in turn: the loads of the next group are in flight
+    // while the current one is computed, and no register copy forces a wait
+    // on them before the next loads go out.  The last prefetch of a
+    // wavefront re-reads its current group (an L2 hit) rather than
+    // branching around the loads.
     if (tg < t_comp) {
         while (true) {
             const bool m1 = tg + 256 < t_comp;
@@ -302,24 +359,104 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     }
 
     if constexpr (G == 1) {
-        // -inf past the span, then the whole chunk out: 16-byte stores where
-        // the row's chunk is 16-byte aligned, else one float per lane.
-        for (int t = t_comp + threadIdx.x; t < t_end; t += 256) s_sc[t - t0] = -INFINITY;
+        // -inf past the span, then the whole range out: 16-byte stores where
+        // the row's range is 16-byte aligned, else one float per lane.
+        for (int t = t_comp + threadIdx.x; t < t_end; t += 256) s.sc[t - t0] = -INFINITY;
         __syncthreads();
         float* dst = a.scores + (size_t)r0 * a.score_stride + t0;
-        const int n = t_end - t0;
+        const int cnt = t_end - t0;
         if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-            for (int i = 4 * threadIdx.x; i + 3 < n; i += 1024)
-                *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&s_sc[i]);
-            for (int i = (n & ~3) + threadIdx.x; i < n; i += 256) dst[i] = s_sc[i];
+            for (int i = 4 * threadIdx.x; i + 3 < cnt; i += 1024)
+                *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&s.sc[i]);
+            for (int i = (cnt & ~3) + threadIdx.x; i < cnt; i += 256) dst[i] = s.sc[i];
         } else {
-            for (int i = threadIdx.x; i < n; i += 256) dst[i] = s_sc[i];
+            for (int i = threadIdx.x; i < cnt; i += 256) dst[i] = s.sc[i];
         }
     } else {
-        // -inf for the part of the chunk past every row's span.
+        // -inf for the part of the range past every row's span.
         for (int rr = 0; rr < G; ++rr) {
             float* srow = a.scores + (size_t)(r0 + rr) * a.score_stride;
             for (int t = t_comp + threadIdx.x; t < t_end; t += 256) srow[t] = -INFINITY;
+        }
+    }
+    // This range's share of the rows' tail past their tiles.
+    for (int rr = 0; rr < G; ++rr) {
+        float* srow = a.scores + (size_t)(r0 + rr) * a.score_stride;
+        for (int t = fill_lo + threadIdx.x; t < fill_hi; t += 256) srow[t] = -INFINITY;
+    }
+}
+
+// Two launch shapes:
+//   chunked:  grid (chunks, groups); a workgroup scores one chunk of a.chunk
+//             tokens of one group of G rows;
+//   balanced: a 1-D grid; every workgroup counts the live 64-token tiles of
+//             every group (max(1, ceil(vmax / 64)), vmax the group's longest
+//             row, so that a dead group still owns one tile), and takes an
+//             equal share of the concatenated tiles, group by group, in
+//             ranges of at most kMaxChunk tokens.  A group's tail past its
+//             tiles, [64 T, score_stride), is cut in proportion to the tiles,
+//             so every position of every row is written exactly once.  Rows
+//             of very different lengths then cost each workgroup the same.
+// Groups of several rows (MTP verify, prefill) use the balanced shape; one
+// row per group (decode) the chunked one, whose workgroups start sooner
+// (measured faster for decode batches, ragged ones included).
+template <int G>
+__global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
+    __shared__ IndexSmem<G> s;
+    if (!a.balanced) {
+        const int t0 = blockIdx.x * a.chunk;
+        score_range<G>(a, s, blockIdx.y * G, t0, min(t0 + a.chunk, a.score_stride), 0, 0, blockIdx.x == 0, true);
+        return;
+    }
+    constexpr int kPer = max_balanced_groups<G>() / 256;   // groups per thread in the scan
+    const int ng = a.n_rows / G;
+    const int cap = min(a.score_stride, a.max_pages * a.page_size);
+    int cnt[kPer];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int gi = kPer * (int)threadIdx.x + k;
+        int vm = 0;
+        if (gi < ng) {
+            for (int j = 0; j < G; ++j) vm = max(vm, min(max(a.row_vis[gi * G + j], 0), cap));
+        }
+        cnt[k] = gi < ng ? max(1, (vm + 63) >> 6) : 0;
+        sum += cnt[k];
+    }
+    uint32_t total;
+    int ex = (int)block_exclusive_scan<256>((uint32_t)sum, s.scan, &total);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int gi = kPer * (int)threadIdx.x + k;
+        if (gi < ng) s.pre[gi] = ex;
+        ex += cnt[k];
+    }
+    if (threadIdx.x == 0) s.pre[ng] = (int)total;
+    __syncthreads();
+    const int T = s.pre[ng];
+    const int A = (int)((int64_t)blockIdx.x * T / gridDim.x);
+    const int B = (int)((int64_t)(blockIdx.x + 1) * T / gridDim.x);
+    if (A >= B) return;
+    // First group: the last one starting at or before tile A.
+    int lo = 0, hi = ng - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s.pre[mid] <= A) lo = mid;
+        else hi = mid - 1;
+    }
+    constexpr int kMaxTiles = kMaxChunk / 64;
+    int last = -1;
+    for (int gi = lo; gi < ng && s.pre[gi] < B; ++gi) {
+        const int base = s.pre[gi];
+        const int tiles = s.pre[gi + 1] - base;
+        const int j0 = max(A, base) - base, j1 = min(B, base + tiles) - base;
+        const int tail = max(0, a.score_stride - 64 * tiles);
+        for (int js = j0; js < j1; js += kMaxTiles) {
+            const int je = min(j1, js + kMaxTiles);
+            const int f_lo = 64 * tiles + (int)((int64_t)tail * js / tiles);
+            const int f_hi = 64 * tiles + (int)((int64_t)tail * je / tiles);
+            score_range<G>(a, s, gi * G, 64 * js, min(64 * je, a.score_stride), f_lo, f_hi, js == 0, gi != last);
+            last = gi;
         }
     }
 }
@@ -331,9 +468,16 @@ constexpr int kResidentWgs = 512;
 template <int G>
 hipError_t launch_g(IndexArgs a, hipStream_t stream) {
     const int groups = a.n_rows / G;
+    if (G > 1 && groups <= max_balanced_groups<G>()) {
+        a.balanced = 1;
+        a.chunk = 0;
+        index_scores_kernel<G><<<kResidentWgs, 256, 0, stream>>>(a);
+        return hipGetLastError();
+    }
     const int per_group = max(1, kResidentWgs / groups);
     int chunk = (a.score_stride + per_group - 1) / per_group;
     chunk = min(kMaxChunk, max(kMinChunk, (chunk + 255) & ~255));
+    a.balanced = 0;
     a.chunk = chunk;
     dim3 grid((a.score_stride + chunk - 1) / chunk, groups);
     index_scores_kernel<G><<<grid, 256, 0, stream>>>(a);

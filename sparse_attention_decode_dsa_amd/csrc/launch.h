@@ -21,7 +21,8 @@ struct IndexArgs {
     float* scores;
     int32_t score_stride;
     int32_t* status;
-    int32_t chunk;   // tokens per workgroup, set by the launcher
+    int32_t chunk;     // chunked launch: tokens per workgroup (set by the launcher)
+    int32_t balanced;  // 1: balanced launch (set by the launcher)
 };
 
 struct TopkArgs {
