@@ -9,12 +9,10 @@
  *   2. dsa_topk              exact top-k per row: per-split local top-k, then an
  *                            exact merge of the candidates
  *   3. dsa_sparse_mla_decode absorbed-MLA attention over the selected paged fp8
- *                            rows (the bf16 query split as dsa_quantize_mla_q
- *                            does), split along the selected list into
+ *                            rows, split along the selected list into
  *                            (partial output, natural-log LSE) pairs
  *   4. dsa_lse_merge         merge of the split partials by their LSE
- * dsa_quantize_q and dsa_quantize_mla_q expose the query quantization of
- * steps 1 and 3 on their own.
+ * dsa_quantize_q exposes the query quantization of step 1 on its own.
  *
  * Conventions shared by every entry point:
  *  - Every array pointer is DEVICE memory owned by the caller.  The library
@@ -56,7 +54,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 4
+#define DSA_ABI_VERSION 5
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -98,27 +96,6 @@ const char* dsa_status_string(int status);
  */
 int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
                    uint8_t* q_code, float* q_scale, hipStream_t stream);
-
-/*
- * dsa_quantize_mla_q -- input side of the sparse MLA (subject page,
- * Modifications, sparse decode: the attention reads fp8 KV rows).  The bf16
- * absorbed query of every (row, head) is split into two fp8 E4M3FN terms and
- * one power-of-two scale, q = scale * (dec(hi) + dec(lo) / 16), with
- * scale = 2^ceil(log2(amax / 448)) (1 for an all-zero head),
- * hi = round-to-nearest-even(q / scale) and
- * lo = round-to-nearest-even(16 * (q / scale - dec(hi))).
- * Every bf16 element with |q / scale| >= 2^-6 is reproduced exactly (after
- * scaling the head's largest magnitude is above 224, so these are all elements
- * above about 2^-14 of it); smaller ones are off by at most 2^-14 * scale.
- * dsa_sparse_mla_decode splits its query the same way, bit for bit, and
- * computes the logits from the terms.
- *   q_bf16   [n_rows, n_heads, head_dim] bf16 bit patterns
- *   q_terms  [n_rows, n_heads, 2, head_dim] uint8 out: hi codes, then lo codes
- *   q_scale  [n_rows, n_heads] float32 out
- * Supported: head_dim == 576, n_heads >= 1.  n_rows == 0 enqueues nothing.
- */
-int dsa_quantize_mla_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
-                       uint8_t* q_terms, float* q_scale, hipStream_t stream);
 
 /*
  * dsa_index_scores -- fp8 lightning-indexer scores (subject page,
@@ -184,9 +161,7 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
  * top_k, so a split's range is known before the count is read; when
  * n < top_k the last splits may be empty):
  *   x_t   = dec(codes of row t) * scale of row t       (576 wide)
- *   l_t   = sm_scale * (q'[r][h] . x_t),  q' = scale * (dec(hi) + dec(lo) / 16)
- * where (hi, lo, scale) is dsa_quantize_mla_q's split of q (q' = q for every
- * element above about 2^-14 of its head's largest),
+ *   l_t   = sm_scale * (q[r][h] . x_t)     (q the exact bf16 values)
  *   o_s   = sum_t e^{l_t - m} x_t[0:512] / sum_t e^{l_t - m},  lse_s = m + ln sum_t e^{l_t - m}
  * Empty split: o_s = 0, lse_s = -inf.
  *   q [n_rows, n_heads, 576] bf16 bit patterns

@@ -66,16 +66,6 @@ int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int3
     return launch_status(dsa::launch_quantize_q(q_bf16, n_rows * n_heads, q_code, q_scale, stream));
 }
 
-int dsa_quantize_mla_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int32_t head_dim,
-                       uint8_t* q_terms, float* q_scale, hipStream_t stream) {
-    if (n_rows < 0 || n_heads < 1 || head_dim < 1) return DSA_ERR_SHAPE;
-    if (head_dim != 576) return DSA_ERR_UNSUPPORTED;
-    if ((int64_t)n_rows * n_heads > INT32_MAX / 4) return DSA_ERR_SHAPE;
-    if (n_rows == 0) return DSA_OK;
-    if (!q_bf16 || !q_terms || !q_scale) return DSA_ERR_NULL;
-    return launch_status(dsa::launch_quantize_mla_q(q_bf16, n_rows * n_heads, q_terms, q_scale, stream));
-}
-
 int dsa_index_scores(const uint16_t* q, const float* head_w,
                      const uint8_t* k_code, const float* k_scale, const int32_t* page_table,
                      const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,

@@ -70,8 +70,6 @@ constexpr int kMaxSplits = 64;
 
 hipError_t launch_quantize_q(const uint16_t* q, int32_t n_pairs, uint8_t* code, float* scale,
                              hipStream_t stream);
-hipError_t launch_quantize_mla_q(const uint16_t* q, int32_t n_pairs, uint8_t* terms, float* scale,
-                                 hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);

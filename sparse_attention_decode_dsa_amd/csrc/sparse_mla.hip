@@ -5,16 +5,12 @@
 // softmax.  Per tile:
 //   gather  the 64 selected 576-byte fp8 rows through the block table into
 //           LDS (rows padded to 592 bytes), with their fp32 scales;
-//   QK      on fp8 matrix cores: the tokens' fp8 bytes are the A operand as
-//           they are (M = tokens), the query the B operand (N = heads).  The
-//           bf16 query is split exactly into two fp8 terms per head,
-//           q = s_h (hi + lo / 16) with s_h a power of two (query_quant.h),
-//           so two accumulator chains give the products without converting
-//           any key byte; the split is done while the first gathers are in
-//           flight and both terms stay in registers for the whole split.  Wavefront w owns
-//           head block w % HB and 16 HB tokens; K steps of 128 use
-//           v_mfma_f32_16x16x128_f8f6f4, the last 64 bytes
-//           v_mfma_f32_16x16x32_fp8_fp8;
+//   QK      on bf16 matrix cores: the tokens' fp8 bytes, converted to bf16
+//           (exact), are the A operand (M = tokens), the bf16 query as it
+//           is the B operand (N = heads), v_mfma_f32_16x16x32_bf16 over the
+//           576 dimensions in 18 steps on two accumulator chains.  The query
+//           stays in registers for the whole split.  Wavefront w owns head
+//           block w % HB and 16 HB tokens;
 //   softmax a lane holds 4 tokens of one head per token block, so the
 //           per-head maximum and sum reduce in-lane and then across the four
 //           16-lane rows with two permlane swaps; the tile maximum per head
@@ -27,12 +23,12 @@
 // The value rows are the first 512 entries of the same rows (absorbed MLA),
 // so a tile is read from HBM once for both products.
 //
-// Latency hiding: a split's range of the selected list depends only on
-// top_k, so its entries are loaded together with the row's metadata and the
-// bf16 query; the block table is then walked once for the whole split
-// (slot -> page -> physical row, kept in LDS), the first gathers go out right
-// after it, and the query is split into its fp8 terms (staged in the last
-// tile buffer, free until the first tile's barrier) while they load.  Tiles are gathered by LDS-direct loads
+// Latency hiding: the bf16 query goes out first, as LDS-direct loads into
+// the last tile buffer (free until the first tile's barrier); a split's
+// range of the selected list depends only on top_k, so its entries are
+// loaded together with the row's metadata; the block table is then walked
+// once for the whole split (slot -> page -> physical row, kept in LDS) and
+// the first gathers go out right after it.  Tiles are gathered by LDS-direct loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at the wavefront's LDS
 // base + 16 * lane), which need no registers: with four tile buffers, three
 // tiles are in flight while the fourth is computed.  Each wavefront waits
@@ -45,16 +41,16 @@
 // multiples of 16 bytes and the next 16 rows on the other half.  QK's K
 // order therefore gives lane groups g = 0..3 the 16-byte chunks
 // c + {0, 16, 8, 24} of a row: the two groups served together differ by
-// 256 bytes and never collide.  For the 128-wide step p the chunks are
-// c = 2p and 2p + 1; the rope tail is chunk 32 + g.  Both operands use the
-// same byte positions, so the sums are the plain dot products.  P' is laid
+// 256 bytes and never collide.  Lane group g reads chunks
+// {2p + h + 16 (g & 1) + 8 (g >> 1) : p < 4, h < 2} and 32 + g, each as two
+// 8-byte K steps; the query takes the same element positions, so the sums
+// are the plain dot products.  P' is laid
 // out as [token group of 8][head][8 tokens] with 768 bytes per token group,
 // which makes both its 8-byte stores and its 16-byte A-operand reads
 // conflict-free.  ds_read_b64_tr_b8 over 32 rows of 592 bytes is
 // conflict-free as it is.
 #include "device_common.h"
 #include "launch.h"
-#include "query_quant.h"
 
 namespace dsa {
 
@@ -146,12 +142,11 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) float s_m[H];
     __shared__ int s_moved[HB];
     __shared__ int s_bad[NW];   // per wavefront: an entry of the split is invalid
-    __shared__ float s_qsc[H];  // per-head power-of-two query scale
-    // The query terms are staged in the last tile buffer: hi of head h at
-    // row h, lo at row H + h (kXStride-byte pitch).
-    uint8_t* const s_qh = s_x[NB - 1];
-    uint8_t* const s_ql = s_qh + H * kXStride;
-    static_assert(2 * H * kXStride <= kTileBytes, "query terms fit one tile buffer");
+    // The bf16 query is staged in the last tile buffer: head h at row h,
+    // kQRow bytes apart (72 chunks of 16 bytes and a pad chunk).
+    constexpr int kQRow = 2 * kRowBytes + 16;
+    constexpr int kQChunks = kQRow / 16;
+    static_assert(H * kQRow <= kTileBytes, "the query fits one tile buffer");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -163,6 +158,21 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     const int r = blockIdx.y;
     const int sp = blockIdx.x;
     const int ns = gridDim.x;
+
+    // The bf16 query of the row, gathered like a tile (lane i of load j
+    // fills chunk 64 j + i of the staging rows; the pad chunk rereads chunk
+    // 0 of its row).  These are the oldest loads of every wavefront, so the
+    // waits for any later load cover them.
+    {
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q + (size_t)r * H * kRowBytes);
+        const uint32_t xl = lds_offset(s_x[NB - 1]);
+        constexpr int kQInsts = (H * kQChunks + kWave - 1) / kWave;
+        for (int j = wv; j < kQInsts; j += NW) {
+            const int c = min(64 * j + lane, H * kQChunks - 1);
+            const int t = c / kQChunks, part = c - t * kQChunks;
+            lds_dma16(qrow + (size_t)t * (2 * kRowBytes) + (part < kQChunks - 1 ? part * 16 : 0), xl + j * 1024);
+        }
+    }
 
     // Row metadata (uniform loads) and the split's range of the selected
     // list.  The range depends only on top_k, so the list entries can be
@@ -185,18 +195,6 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
             if (base + NT * u < hi_list) slot[u] = sel[min(base + NT * u + tid, hi_list - 1)];
     };
     load_slots(lo);
-
-    // The bf16 query: wavefront wv holds heads wv, wv+NW, ...; lane l has
-    // 16-byte chunk l (and 64 + l for l < 8) of the 1152-byte row.
-    constexpr int kQH = H / NW;   // heads per wavefront
-    uint4 qc0[kQH], qc1[kQH];
-#pragma unroll
-    for (int j = 0; j < kQH; ++j) {
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q + ((size_t)r * H + wv + NW * j) * kRowBytes);
-        qc0[j] = *reinterpret_cast<const uint4*>(src + 16 * lane);
-        qc1[j] = uint4{0u, 0u, 0u, 0u};
-        if (lane < 8) qc1[j] = *reinterpret_cast<const uint4*>(src + 16 * (64 + lane));
-    }
 
     bool ok = b_raw >= 0 && b_raw < a.batch && v_raw >= 0 && v_raw <= a.max_pages * a.page_size;
     if (!ok && tid == 0) flag(a.status, DSA_DEV_ROW_RANGE);
@@ -247,18 +245,29 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     static_assert(MlaGeom<4>::kRowsCap <= 2048, "a four-buffer split is one batch (kBatch >= 2048)");
     const bool wave_bad = __ballot(bad) != 0ull;
     if (lane == 0) s_bad[wv] = wave_bad;
-    // Every load of the wavefronts done (the bf16 query included), so no
-    // load the compiler tracks is outstanding once the gathers go out.
+    // Every load of the wavefronts done (the query included, which the
+    // compiler does not track), so the query is in LDS after the barrier and
+    // no load the compiler tracks is outstanding once the gathers go out.
     wait_vm<0>();
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kQH; ++j) {
-        pin(qc0[j].x); pin(qc0[j].y); pin(qc0[j].z); pin(qc0[j].w);
-        pin(qc1[j].x); pin(qc1[j].y); pin(qc1[j].z); pin(qc1[j].w);
-    }
     bool any_bad = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) any_bad |= s_bad[w] != 0;
+
+    // The query operand of this lane (head 16 hb + nn, lane group g) for the
+    // whole split: for the i-th key chunk of lane group g (chunk ch), the
+    // query elements [16 ch, 16 ch + 16) as two 8-element K steps.
+    v8bf qb[18];
+    {
+        const uint8_t* qr = s_x[NB - 1] + (16 * hb + nn) * kQRow;
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            const int ch = i < 8 ? qk_chunk(i >> 1, i & 1, g) : 32 + g;
+            qb[2 * i] = *reinterpret_cast<const v8bf*>(qr + 32 * ch);
+            qb[2 * i + 1] = *reinterpret_cast<const v8bf*>(qr + 32 * ch + 16);
+        }
+    }
+    const float cq = a.sm_scale;
 
     // Row of tile-local token t of the tile starting at split entry `base`.
     // The read is clamped into the array and its value discarded past the end,
@@ -311,53 +320,6 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     for (int j = 0; j < NB - 1; ++j)
         if (j < n_tiles) issue(j, lo + j * kT);
 
-    // Query -> two fp8 terms per head (query_quant.h) while they load.
-#pragma unroll
-    for (int j = 0; j < kQH; ++j) {
-        const int hq = wv + NW * j;
-        float v0[8], v1[8];
-        bf16x8_to_f32(qc0[j], v0);
-        bf16x8_to_f32(qc1[j], v1);
-        float amax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fmaxf(fabsf(v0[k]), fabsf(v1[k])));
-        const float sq = mla_q_scale(wave_max(amax));
-        const float inv = 1.0f / sq;                       // exact: sq is a power of two
-        uint32_t hw[4], lw[4];
-        mla_q_split4(v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv, hw[0], lw[0]);
-        mla_q_split4(v0[4] * inv, v0[5] * inv, v0[6] * inv, v0[7] * inv, hw[1], lw[1]);
-        mla_q_split4(v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv, hw[2], lw[2]);
-        mla_q_split4(v1[4] * inv, v1[5] * inv, v1[6] * inv, v1[7] * inv, hw[3], lw[3]);
-        // chunk l covers bf16 elements [8l, 8l+8): fp8 bytes [8l, 8l+8)
-        *reinterpret_cast<uint2*>(s_qh + hq * kXStride + 8 * lane) = uint2{hw[0], hw[1]};
-        *reinterpret_cast<uint2*>(s_ql + hq * kXStride + 8 * lane) = uint2{lw[0], lw[1]};
-        if (lane < 8) {
-            *reinterpret_cast<uint2*>(s_qh + hq * kXStride + 8 * (64 + lane)) = uint2{hw[2], hw[3]};
-            *reinterpret_cast<uint2*>(s_ql + hq * kXStride + 8 * (64 + lane)) = uint2{lw[2], lw[3]};
-        }
-        if (lane == 0) s_qsc[hq] = sq;
-    }
-    lds_sync();
-
-    // The query operand of this lane (head 16 hb + nn, lane group g) for the
-    // whole split: 9 chunks per term, in the QK K order.
-    v4i qh[9], ql[9];
-    {
-        const uint8_t* qh_row = s_qh + (16 * hb + nn) * kXStride;
-        const uint8_t* ql_row = s_ql + (16 * hb + nn) * kXStride;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                qh[2 * p + h] = *reinterpret_cast<const v4i*>(qh_row + 16 * qk_chunk(p, h, g));
-                ql[2 * p + h] = *reinterpret_cast<const v4i*>(ql_row + 16 * qk_chunk(p, h, g));
-            }
-        qh[8] = *reinterpret_cast<const v4i*>(qh_row + 16 * (32 + g));
-        ql[8] = *reinterpret_cast<const v4i*>(ql_row + 16 * (32 + g));
-    }
-
-    const float cq = a.sm_scale * s_qsc[16 * hb + nn];
-
     // Softmax state: in the QK layout a lane owns head 16 hb + nn (m_run,
     // and l_run: this wavefront's share of the denominator); in the PV
     // layout accumulator row i of lane group g is head 16 h2 + 4g + i.
@@ -382,24 +344,18 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
             lds_sync();
         }
 
-        // QK: token block tbk (A, rows), head block hb (B).
-        v4f ah = v4f{0.0f, 0.0f, 0.0f, 0.0f}, al = ah;
+        // QK: token block tbk (A, rows), head block hb (B), in bf16: each
+        // 16-byte key chunk of the lane's row is two 8-element K steps.
+        v4f a0 = v4f{0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
         {
             const uint8_t* xr = xb + (16 * tbk + nn) * kXStride;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const v4i x0 = *reinterpret_cast<const v4i*>(xr + 16 * qk_chunk(p, 0, g));
-                const v4i x1 = *reinterpret_cast<const v4i*>(xr + 16 * qk_chunk(p, 1, g));
-                const v8i xa = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                const v4i h0 = qh[2 * p], h1 = qh[2 * p + 1], l0 = ql[2 * p], l1 = ql[2 * p + 1];
-                ah = mfma_fp8_16x16x128(xa, v8i{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w}, ah);
-                al = mfma_fp8_16x16x128(xa, v8i{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w}, al);
+            for (int i = 0; i < 9; ++i) {
+                const int ch = i < 8 ? qk_chunk(i >> 1, i & 1, g) : 32 + g;
+                const v4i x = *reinterpret_cast<const v4i*>(xr + 16 * ch);
+                a0 = mfma_bf16_16x16x32(fp8x8_to_bf16x8((uint32_t)x.x, (uint32_t)x.y), qb[2 * i], a0);
+                a1 = mfma_bf16_16x16x32(fp8x8_to_bf16x8((uint32_t)x.z, (uint32_t)x.w), qb[2 * i + 1], a1);
             }
-            const v4i xt = *reinterpret_cast<const v4i*>(xr + 16 * (32 + g));
-            ah = mfma_fp8_16x16x32(v2i{xt.x, xt.y}, v2i{qh[8].x, qh[8].y}, ah);
-            ah = mfma_fp8_16x16x32(v2i{xt.z, xt.w}, v2i{qh[8].z, qh[8].w}, ah);
-            al = mfma_fp8_16x16x32(v2i{xt.x, xt.y}, v2i{ql[8].x, ql[8].y}, al);
-            al = mfma_fp8_16x16x32(v2i{xt.z, xt.w}, v2i{ql[8].z, ql[8].w}, al);
         }
 
         // Logits of this lane's tokens tk0 + i (tk0 = 16 tbk + 4g) for head
@@ -419,7 +375,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            lg[i] = live[i] ? (ah[i] + 0.0625f * al[i]) * (cq * ts[i]) : -INFINITY;
+            lg[i] = live[i] ? (a0[i] + a1[i]) * (cq * ts[i]) : -INFINITY;
             mx = fmaxf(mx, lg[i]);
         }
         mx = rows4_max(mx);

@@ -17,7 +17,7 @@ import os
 
 import torch
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN"}
@@ -34,7 +34,6 @@ _SIGS = {
     "dsa_abi_version": ([], ctypes.c_int),
     "dsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dsa_quantize_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
-    "dsa_quantize_mla_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_index_scores": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
     "dsa_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
@@ -124,19 +123,6 @@ def quantize_q(q_bf16, q_code=None, q_scale=None, stream=None):
     return q_code, q_scale
 
 
-def quantize_mla_q(q_bf16, q_terms=None, q_scale=None, stream=None):
-    """bf16 [R, H, 576] -> (two fp8 terms uint8 [R, H, 2, 576], scales f32 [R, H])."""
-    r, h, d = q_bf16.shape
-    if q_terms is None:
-        q_terms = torch.empty((r, h, 2, d), dtype=torch.uint8, device=q_bf16.device)
-    if q_scale is None:
-        q_scale = torch.empty((r, h), dtype=torch.float32, device=q_bf16.device)
-    _check(lib().dsa_quantize_mla_q(_ptr(q_bf16, _BF16, "q_bf16"), r, h, d,
-                                    _ptr(q_terms, _FP8, "q_terms"), _ptr(q_scale, torch.float32, "q_scale"),
-                                    _stream(stream)), "dsa_quantize_mla_q")
-    return q_terms, q_scale
-
-
 def index_scores(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis,
                  group_rows: int = 1, score_stride: int | None = None, scores=None, status=None,
                  stream=None):
@@ -192,8 +178,7 @@ def topk(scores, row_vis, top_k: int, n_splits: int = 1, workspace=None, topk_id
 def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_count,
                       n_splits: int = 1, sm_scale: float = 1.0 / 24.0, part_o=None, part_lse=None,
                       out=None, out_lse=None, status=None, stream=None):
-    """Split-K sparse MLA of the bf16 query q [R, H, 576] (split in the kernel
-    as quantize_mla_q does).  n_splits == 1 -> (out bf16 [R,H,512], out_lse f32
+    """Split-K sparse MLA of the bf16 query q [R, H, 576].  n_splits == 1 -> (out bf16 [R,H,512], out_lse f32
     [R,H]); otherwise -> (part_o f32 [R,H,S,512], part_lse f32 [R,H,S]).
     kv_cache is the packed uint8 [NP, P, 640] MLA cache (codes, fp32 scale at
     byte 576, pad)."""

@@ -31,8 +31,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_quantize_mla_q",
-            "dsa_index_scores",
+    assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_index_scores",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_merge"} <= set(names)
     raw = ctypes.CDLL(dsa.lib_path())
     for n in names:
@@ -132,9 +131,3 @@ def test_lse_merge_and_quantize_validation(L):
     assert q(P, -1, 64, 128, P, P, None) == SHAPE
     assert q(None, 4, 64, 128, P, P, None) == NULL
     assert q(P, 0, 64, 128, P, P, None) == OK
-    qm = L.dsa_quantize_mla_q
-    assert qm(P, 4, 32, 512, P, P, None) == UNSUP
-    assert qm(P, -1, 32, 576, P, P, None) == SHAPE
-    assert qm(P, 4, 0, 576, P, P, None) == SHAPE
-    assert qm(P, 4, 32, 576, P, None, None) == NULL
-    assert qm(P, 0, 32, 576, P, P, None) == OK

@@ -97,35 +97,6 @@ def test_quantize_q_bit_exact():
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
 
 
-def test_quantize_mla_q_terms():
-    """The prepared MLA query: a power-of-two scale per head, 2^ceil(log2(amax/448))
-    (1 for a zero head), and q = scale * (hi + lo / 16) exactly for every element
-    with |q / scale| >= 2^-6, within 2^-14 * scale below that."""
-    g = torch.Generator().manual_seed(11)
-    q = torch.randn(9, 32, 576, generator=g) * torch.exp(torch.randn(9, 32, 1, generator=g) * 4)
-    q[0, 0] = 0.0                      # all-zero head
-    q[0, 1, :] = 0.0
-    q[0, 1, 7] = -448.0                # amax exactly 448
-    q[0, 2, ::3] *= 1e-6               # elements far below the head's maximum
-    q[1, 5] *= 1e-30                   # tiny head
-    q[2, 7] *= 1e30                    # huge head
-    qb = q.to(torch.bfloat16)
-    terms, scale = dsa.quantize_mla_q(qb.cuda())
-    torch.cuda.synchronize()
-    terms, scale = terms.cpu(), scale.cpu().double()
-    x = qb.double()
-    amax = x.abs().amax(dim=2)
-    expect = torch.where(amax > 0, torch.exp2(torch.ceil(torch.log2(amax / 448.0))), torch.ones_like(amax))
-    assert torch.equal(scale, expect)
-    hi = terms[:, :, 0].view(torch.float8_e4m3fn).double()
-    lo = terms[:, :, 1].view(torch.float8_e4m3fn).double()
-    rec = scale[..., None] * (hi + lo / 16.0)
-    y = (x / scale[..., None]).abs()
-    exact = y >= 2.0 ** -6
-    assert torch.equal(rec[exact], x[exact])
-    assert ((rec - x).abs()[~exact] <= 2.0 ** -14 * scale[..., None].expand_as(x)[~exact]).all()
-
-
 # ------------------------------------------------------------------ top-k alone
 
 def _synthetic_scores(rng, r, stride, vis, tie_frac=0.3):
