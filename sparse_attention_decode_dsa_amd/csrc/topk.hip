@@ -16,13 +16,19 @@
 // Selection finds the k-th largest key `thr` and how many keys equal to it
 // belong to the top k, with few per-key LDS atomics (they serialise):
 //   1. the first key of every thread is a sample of the list; one atomic per
-//      thread builds its histogram over the top 12 key bits, and a scan of
+//      thread builds its histogram over the top 12 key bits, and one scan of
 //      it gives the bins holding the sample ranks rho -+ delta (rho = k *
 //      samples / n, delta = 4 binomial standard deviations + 4);
 //   2. keys in bins above that bracket are counted; keys inside it are
 //      compacted, in list order, into LDS;
-//   3. an exact radix select (12, 10 and 10 bits) over the compacted keys
-//      finds the rank k - (keys above) among them.
+//   3. an exact radix select over the compacted keys finds the rank
+//      k - (keys above) among them: two 12-bit passes when the bracket spans
+//      fewer than 16 bins (the first digit is the bin's offset in the bracket
+//      and key bits [19:12], the second bits [11:0]), else 12, 10 and 10 bits.
+// Barriers are the cost of a workgroup this size, so histograms are cleared
+// ahead under barriers that are needed anyway, and the scans alternate two
+// scratch arrays, which saves the barrier that would protect one array from
+// the next scan.
 // If the bracket misses or holds more keys than LDS has room for (heavy
 // ties), the same radix select runs over all keys instead.
 // Emission: per-thread counts and one workgroup scan give every selected
@@ -51,11 +57,14 @@ struct TopkSmem {
         struct {
             uint32_t hist[kBins0];
             uint32_t cand_key[kCandCap + kWave];   // + one dummy word per lane
+            uint32_t hist2[kBins0];
         } sel;
     } u;
-    uint32_t scan[kThreads / kWave + 1];
+    uint32_t h0[kBins0];   // sample histogram, cleared before the list is staged
+    uint32_t scan[2][kThreads / kWave + 1];
     int32_t offs[kMaxSplits + 1];
     uint32_t sel_digit;
+    uint32_t sel_digit2;
     uint32_t sel_need;
     int32_t n;
 };
@@ -68,23 +77,47 @@ __device__ __forceinline__ int keys_per_thread(int n) {
     return ((n + 4 * kThreads - 1) / (4 * kThreads)) * 4;
 }
 
-// Digit d (of NB bins, scanned from the largest) whose bin holds the kk-th
-// largest counted key: s.sel_digit = d, s.sel_need = kk minus the keys in
-// larger bins.  Thread t owns the NB/kThreads bins just below
+// Workgroup exclusive scan in two barriers.  Successive scans alternate the
+// two scratch arrays (`tog` flips on every call and is the same in every
+// thread), so a scan never writes the array the previous one is still
+// being read from.
+__device__ __forceinline__ uint32_t scan2(TopkSmem& s, uint32_t v, uint32_t* total, int& tog) {
+    constexpr int NW = kThreads / kWave;
+    uint32_t* scratch = s.scan[tog];
+    tog ^= 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const uint32_t inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) scratch[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        const uint32_t x = lane < NW ? scratch[lane] : 0u;
+        const uint32_t xi = wave_inclusive_scan(x);
+        if (lane < NW) scratch[lane] = xi - x;
+        if (lane == NW - 1) scratch[NW] = xi;
+    }
+    __syncthreads();
+    *total = scratch[NW];
+    return inc - v + scratch[w];
+}
+
+// Digit d (of NB bins of `hist`, scanned from the largest) whose bin holds
+// the kk-th largest counted key: s.sel_digit = d, s.sel_need = kk minus the
+// keys in larger bins.  Thread t owns the NB/kThreads bins just below
 // NB - t * (NB / kThreads).
 template <int NB>
-__device__ __forceinline__ uint32_t find_digit(TopkSmem& s, uint32_t kk) {
+__device__ __forceinline__ void find_digit(TopkSmem& s, const uint32_t* hist, uint32_t kk, int& tog) {
     constexpr int PER = NB / kThreads;
     const int tid = threadIdx.x;
     uint32_t c[PER];
     uint32_t sum = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        c[j] = s.u.sel.hist[NB - 1 - (tid * PER + j)];
+        c[j] = hist[NB - 1 - (tid * PER + j)];
         sum += c[j];
     }
     uint32_t total;
-    uint32_t above = block_exclusive_scan<kThreads>(sum, s.scan, &total);
+    uint32_t above = scan2(s, sum, &total, tog);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (above < kk && above + c[j] >= kk) {
@@ -94,7 +127,37 @@ __device__ __forceinline__ uint32_t find_digit(TopkSmem& s, uint32_t kk) {
         above += c[j];
     }
     __syncthreads();
-    return total;
+}
+
+// The bins holding the kk_hi-th and kk_lo-th largest keys of `hist`, in one
+// scan: s.sel_digit (kBins0 - 1 if kk_hi == 0) and s.sel_digit2 (0 if
+// kk_lo == 0).
+template <int NB>
+__device__ __forceinline__ void find_digit2(TopkSmem& s, const uint32_t* hist, uint32_t kk_hi, uint32_t kk_lo,
+                                            int& tog) {
+    constexpr int PER = NB / kThreads;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        s.sel_digit = NB - 1;
+        s.sel_digit2 = 0;
+    }
+    uint32_t c[PER];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        c[j] = hist[NB - 1 - (tid * PER + j)];
+        sum += c[j];
+    }
+    uint32_t total;
+    uint32_t above = scan2(s, sum, &total, tog);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t d = (uint32_t)(NB - 1 - (tid * PER + j));
+        if (above < kk_hi && above + c[j] >= kk_hi) s.sel_digit = d;
+        if (above < kk_lo && above + c[j] >= kk_lo) s.sel_digit2 = d;
+        above += c[j];
+    }
+    __syncthreads();
 }
 
 __device__ __forceinline__ void clear_hist(TopkSmem& s, int nb) {
@@ -107,7 +170,7 @@ __device__ __forceinline__ void clear_hist(TopkSmem& s, int nb) {
 // three histogram passes of 12, 10 and 10 bits.
 template <int M, typename Get>
 __device__ __forceinline__ void radix_select(TopkSmem& s, uint32_t kk, Get get, uint32_t* thr_out,
-                                             uint32_t* need_out) {
+                                             uint32_t* need_out, int& tog) {
     clear_hist(s, kBins0);
 #pragma unroll
     for (int i = 0; i < M; ++i) {
@@ -115,7 +178,7 @@ __device__ __forceinline__ void radix_select(TopkSmem& s, uint32_t kk, Get get, 
         if (get(i, &key)) atomicAdd(&s.u.sel.hist[bin0(key)], 1u);
     }
     __syncthreads();
-    find_digit<kBins0>(s, kk);
+    find_digit<kBins0>(s, s.u.sel.hist, kk, tog);
     uint32_t prefix = s.sel_digit << 20;
     kk = s.sel_need;
     uint32_t mask = 0xFFF00000u;
@@ -130,7 +193,7 @@ __device__ __forceinline__ void radix_select(TopkSmem& s, uint32_t kk, Get get, 
             if (get(i, &key) && (key & mask) == prefix) atomicAdd(&s.u.sel.hist[(key >> shift) & (kBins1 - 1)], 1u);
         }
         __syncthreads();
-        find_digit<kBins1>(s, kk);
+        find_digit<kBins1>(s, s.u.sel.hist, kk, tog);
         prefix |= s.sel_digit << shift;
         mask |= (uint32_t)(kBins1 - 1) << shift;
         kk = s.sel_need;
@@ -141,30 +204,31 @@ __device__ __forceinline__ void radix_select(TopkSmem& s, uint32_t kk, Get get, 
 }
 
 // k-th largest (1 <= k < n) of the n keys, thread t holding `mine` of them
-// in key[0, mine).
+// in key[0, mine).  s.h0 must be zero (the caller clears it before staging
+// the list).
 __device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kPer], int mine, int n, int k,
-                           uint32_t* thr_out, uint32_t* need_out) {
+                                           uint32_t* thr_out, uint32_t* need_out, int& tog) {
     const int tid = threadIdx.x;
     const int per = keys_per_thread(n);
     const int samples = (n + per - 1) / per;        // threads holding a key
+    // The candidate histograms live where the list was staged; clear them
+    // now, under the sample histogram's barrier.
+    for (int i = tid; i < kBins0; i += kThreads) {
+        s.u.sel.hist[i] = 0u;
+        s.u.sel.hist2[i] = 0u;
+    }
     // 1. Sample histogram and the bracket of bins around rank k.
-    clear_hist(s, kBins0);
-    if (mine > 0) atomicAdd(&s.u.sel.hist[bin0(key[0])], 1u);
+    if (mine > 0) atomicAdd(&s.h0[bin0(key[0])], 1u);
     __syncthreads();
     const float rho = (float)k * (float)samples / (float)n;
     const float sigma = sqrtf(fmaxf(rho * (1.0f - rho / (float)samples), 0.0f));
     const int delta = (int)ceilf(4.0f * sigma) + 4;
     const int r_hi = (int)rho - delta;
     const int r_lo = (int)ceilf(rho) + delta;
-    uint32_t b_hi = kBins0 - 1, b_lo = 0;   // bracket bins, inclusive
-    if (r_hi >= 1) {
-        find_digit<kBins0>(s, (uint32_t)r_hi);
-        b_hi = s.sel_digit;
-    }
-    if (r_lo <= samples) {
-        find_digit<kBins0>(s, (uint32_t)r_lo);
-        b_lo = s.sel_digit;
-    }
+    // bracket bins, inclusive: [b_lo, b_hi] (the whole range when a rank falls
+    // outside the sample)
+    find_digit2<kBins0>(s, s.h0, r_hi >= 1 ? (uint32_t)r_hi : 0u, r_lo <= samples ? (uint32_t)r_lo : 0u, tog);
+    uint32_t b_hi = s.sel_digit, b_lo = s.sel_digit2;
     // 2. Count keys above the bracket; compact the keys inside it in order.
     // Positions past a thread's share hold key 0 (bin 0); bin 0 is kept out
     // of the bracket, so they are never counted, and a real key of bin 0 (a
@@ -179,7 +243,7 @@ __device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kP
     }
     // One scan of (above, inside) in 16-bit halves (each total <= 32768).
     uint32_t tot;
-    const uint32_t both = block_exclusive_scan<kThreads>((above << 16) | inside, s.scan, &tot);
+    const uint32_t both = scan2(s, (above << 16) | inside, &tot, tog);
     const uint32_t tot_above = tot >> 16, tot_inside = tot & 0xFFFFu;
     uint32_t at = both & 0xFFFFu;
     const bool fast = tot_above < (uint32_t)k && tot_above + tot_inside >= (uint32_t)k &&
@@ -201,15 +265,47 @@ __device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kP
         __syncthreads();
         // 3. Exact rank among the compacted keys (4 per thread).
         const uint32_t nc = tot_inside;
+        const uint32_t kk = (uint32_t)k - tot_above;
+        if (b_hi - b_lo < 16u) {
+            // Two 12-bit passes: (bin offset in the bracket, bits [19:12]),
+            // then bits [11:0] among the keys sharing the first digit.
+            constexpr int M = kCandCap / kThreads;
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                const uint32_t j = (uint32_t)tid + (uint32_t)(kThreads * i);
+                if (j < nc) {
+                    const uint32_t kv = s.u.sel.cand_key[j];
+                    atomicAdd(&s.u.sel.hist[((bin0(kv) - b_lo) << 8) | ((kv >> 12) & 0xFFu)], 1u);
+                }
+            }
+            __syncthreads();
+            find_digit<kBins0>(s, s.u.sel.hist, kk, tog);
+            const uint32_t d1 = s.sel_digit;
+            const uint32_t kk2 = s.sel_need;
+            const uint32_t top20 = ((b_lo + (d1 >> 8)) << 8) | (d1 & 0xFFu);   // key bits [31:12]
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                const uint32_t j = (uint32_t)tid + (uint32_t)(kThreads * i);
+                if (j < nc) {
+                    const uint32_t kv = s.u.sel.cand_key[j];
+                    if ((kv >> 12) == top20) atomicAdd(&s.u.sel.hist2[kv & 0xFFFu], 1u);
+                }
+            }
+            __syncthreads();
+            find_digit<kBins0>(s, s.u.sel.hist2, kk2, tog);
+            *thr_out = (top20 << 12) | s.sel_digit;
+            *need_out = s.sel_need;
+            return;
+        }
         radix_select<kCandCap / kThreads>(
-            s, (uint32_t)k - tot_above,
+            s, kk,
             [&](int i, uint32_t* kv) {
                 const uint32_t j = (uint32_t)tid + (uint32_t)(kThreads * i);
                 if (j >= nc) return false;
                 *kv = s.u.sel.cand_key[j];
                 return true;
             },
-            thr_out, need_out);
+            thr_out, need_out, tog);
         return;
     }
     radix_select<kPer>(
@@ -219,7 +315,7 @@ __device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kP
             *kv = key[i];
             return true;
         },
-        thr_out, need_out);
+        thr_out, need_out, tog);
 }
 
 // LDS words of the emitted list positions and keys (each k + one dummy per
@@ -236,7 +332,7 @@ static_assert(2 * (kTopkMaxK + kWave) <= kTopkMaxList, "emission buffers fit the
 // taken goes to the lane's dummy word), for a coalesced copy out afterwards
 // (after a barrier, by the caller).
 __device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[kPer], int base,
-                                            uint32_t thr, uint32_t need_eq, int k) {
+                                            uint32_t thr, uint32_t need_eq, int k, int& tog) {
     // Positions past the thread's share hold key 0, which is never above a
     // threshold; equal keys are only counted for a nonzero threshold (a zero
     // one means NaN scores, an error the caller is told about).
@@ -251,7 +347,7 @@ __device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[k
     // One scan of (gt, eq) packed in 16-bit halves (each total <= 32768):
     // the equal keys taken before this thread are min(eq_before, need_eq).
     uint32_t tot;
-    const uint32_t both = block_exclusive_scan<kThreads>((gt << 16) | eq, s.scan, &tot);
+    const uint32_t both = scan2(s, (gt << 16) | eq, &tot, tog);
     const uint32_t eq_before = both & 0xFFFFu;
     uint32_t eq_left = min(eq, need_eq > eq_before ? need_eq - eq_before : 0u);
     uint32_t rank = (both >> 16) + min(eq_before, need_eq);
@@ -275,7 +371,7 @@ __device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[k
 // thread walks only the set bits of its taken-key mask and writes the list
 // positions straight to `out` at their ranks.
 __device__ __forceinline__ void emit_direct(TopkSmem& s, const uint32_t (&key)[kPer], int base, uint32_t thr,
-                                            uint32_t need_eq, int k, int32_t* out, int lo) {
+                                            uint32_t need_eq, int k, int32_t* out, int lo, int& tog) {
     const uint32_t eq_key = thr != 0u ? thr : 0xFFFFFFFFu;
     const bool eq_ok = thr != 0u;
     uint32_t gtm = 0u, eqm = 0u;
@@ -285,8 +381,7 @@ __device__ __forceinline__ void emit_direct(TopkSmem& s, const uint32_t (&key)[k
         eqm |= (key[i] == eq_key && eq_ok ? 1u : 0u) << i;
     }
     uint32_t tot;
-    const uint32_t both = block_exclusive_scan<kThreads>(((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm),
-                                                          s.scan, &tot);
+    const uint32_t both = scan2(s, ((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm), &tot, tog);
     const uint32_t eq_before = both & 0xFFFFu;
     uint32_t take_eq = min((uint32_t)__popc(eqm), need_eq > eq_before ? need_eq - eq_before : 0u);
     uint32_t tm = gtm;
@@ -433,6 +528,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
     const int mine = max(0, min(per, n - base));
     uint32_t key[kPer];
     bool nan = false;
+    for (int i = threadIdx.x; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
     if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
         load_list_vec(s, src, n, base, mine, key, nan);
     } else {
@@ -444,13 +540,14 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
     }
     if (__ballot(nan) != 0ull && (threadIdx.x & 63) == 0) flag(a.status, DSA_DEV_NAN);
     uint32_t thr, need;
-    select_kth(s, key, mine, n, k, &thr, &need);
+    int tog = 0;
+    select_kth(s, key, mine, n, k, &thr, &need, tog);
     // A right selection takes exactly k keys; ranks are clamped below k so
     // that a wrong one could not write past the buffers.
     if (direct) {
-        emit_direct(s, key, base, thr, need, k, out_idx, lo);
+        emit_direct(s, key, base, thr, need, k, out_idx, lo, tog);
     } else {
-        emit_to_lds(s, key, base, thr, need, k);
+        emit_to_lds(s, key, base, thr, need, k, tog);
         __syncthreads();
         for (int i = threadIdx.x; i < k; i += kThreads) {
             out_idx[i] = lo + (int)s.u.stage[kEmitPos + i];
@@ -509,10 +606,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
         return;
     }
     uint32_t key[kPer];
+    for (int i = threadIdx.x; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
     load_list(s, n, base, mine, key, [&](int i) { return ckey[entry(i)]; });
     uint32_t thr, need;
-    select_kth(s, key, mine, n, k, &thr, &need);
-    emit_to_lds(s, key, base, thr, need, k);
+    int tog = 0;
+    select_kth(s, key, mine, n, k, &thr, &need, tog);
+    emit_to_lds(s, key, base, thr, need, k, tog);
     __syncthreads();
     for (int i = threadIdx.x; i < k; i += kThreads) out_idx[i] = cslot[entry((int)s.u.stage[kEmitPos + i])];
 }
