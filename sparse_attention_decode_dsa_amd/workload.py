@@ -219,6 +219,8 @@ def make(name_or_cfg, seed: int | None = None, device="cpu", poison: bool = True
     if poison:
         valid = torch.zeros((n_pool, p), dtype=torch.bool)
         for i, n in enumerate(pages_per_req):
+            if n == 0:
+                continue
             pages = page_table[i, :n].long()
             valid[pages] = True
             tail = int(kv[i]) - (n - 1) * p

@@ -4,12 +4,15 @@ Inputs are seeded and synthetic (sparse_attention_decode_dsa_amd.workload);
 the oracle never sees anything the GPU computed.  Rules and tolerances are in
 tests/parity_util.py.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 from oracle import dsa_oracle as O
-from parity_util import (bf16_to_f64, check_out, check_scores, check_topk_row)
+from parity_util import (bf16_to_f64, check_out, check_scores, check_topk_row,
+                         score_magnitudes)
 from sparse_attention_decode_dsa_amd import dsa
 from sparse_attention_decode_dsa_amd import workload as W
 
@@ -42,7 +45,11 @@ def compare_step(inp, step, rows, max_swap_rows=None):
     g_scores = step.scores[rows].cpu().double().numpy()
     r_scores = np.full_like(g_scores, -np.inf)
     r_scores[:, :ref["scores"].shape[1]] = ref["scores"]
-    check_scores(g_scores, r_scores, vis)
+    sub_np = W.as_numpy(sub)
+    mags = score_magnitudes(sub_np, ref["q_code"], ref["q_scale"])
+    hi, di = ref["q_code"].shape[1:]
+    ulps = check_scores(g_scores, r_scores, vis, mags, di + hi + 2)
+    say(f"  scores: max err {ulps:.2f} u*A (bound {di + hi + 2} u*A)")
     g_idx = step.topk_idx[rows].cpu().numpy()
     g_cnt = step.topk_count[rows].cpu().numpy()
     g_out = bf16_to_f64(step.out[rows])
@@ -192,6 +199,46 @@ def test_bulk_decode_sampled_rows(name):
     ref, sub, swapped = compare_step(inp, step, rows, max_swap_rows=2)
     say(f"{name}: rows {rows} swapped {swapped}")
     mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
+
+
+# ------------------------------------------------------------------ edge rows, page sizes, strides
+
+EDGE_DECODE = W.Config("edge_decode", batch=10, kv_lens=(0, 1, 63, 64, 65, 2047, 2048, 2049, 5000, 777),
+                       page_size=16, mla_heads=16)
+
+
+@pytest.mark.parametrize("page_size,top_k,splits,stride_pad,heads", [
+    (16, 2048, (1, 1), 0, 16),      # empty, one-token and page-edge rows; k above most rows
+    (1024, 2048, (3, 5), 3, 32),    # one page holds most rows; odd stride (unaligned rows)
+    (64, 100, (2, 64), 1, 16),      # small k, more attention splits than entries
+    (16, 1, (1, 2), 0, 32),         # k = 1
+])
+def test_edge_rows_match_oracle(page_size, top_k, splits, stride_pad, heads):
+    cfg = dataclasses.replace(EDGE_DECODE, page_size=page_size, top_k=top_k, mla_heads=heads,
+                              index_splits=splits[0], attn_splits=splits[1])
+    inp = W.to(W.make(cfg), "cuda")
+    stride = (int(inp.row_vis.max()) + 63) // 64 * 64 + stride_pad
+    say(f"edge decode P={page_size} k={top_k} splits={splits} stride={stride} H={heads}")
+    step = run_step(inp, splits[0], splits[1], None, stride)
+    compare_step(inp, step, range(inp.n_rows), max_swap_rows=2)
+    assert step.topk_count[0].item() == 0 and step.topk_count[1].item() == 1
+    assert torch.all(step.out[0] == 0) and torch.all(torch.isneginf(step.out_lse[0]))
+
+
+@pytest.mark.parametrize("cfg", [
+    # Two rows per request scored as one group: a dead group (kv_len 0), short
+    # and page-straddling spans on the balanced schedule.
+    W.Config("edge_g2", batch=4, kv_lens=(0, 130, 2100, 70), rows_per_req=2, page_size=64,
+             mla_heads=16, group_rows=2, index_splits=1, attn_splits=3),
+    # MTP-style causal groups of three, spans down to one token, 1024-token pages.
+    W.Config("edge_mtp", batch=5, kv_lens=(3, 4, 64, 300, 3000), rows_per_req=3, causal="mtp",
+             page_size=1024, mla_heads=32, group_rows=3, index_splits=1, attn_splits=2),
+], ids=["groups_of_2", "mtp_groups_of_3"])
+def test_edge_groups_match_oracle(cfg):
+    inp = W.to(W.make(cfg), "cuda")
+    say(f"{cfg.name}: rows={inp.n_rows} vis={inp.row_vis.tolist()}")
+    step = run_step(inp)
+    compare_step(inp, step, range(inp.n_rows), max_swap_rows=2)
 
 
 # ------------------------------------------------------------------ long context, MTP verify, prefill
