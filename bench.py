@@ -79,33 +79,39 @@ def algorithmic_bytes(inp) -> dict:
                                                      for v in vis)}
 
 
-def cpu_baseline(inp_gpu, seconds: float) -> dict:
-    """The oracle, as it stands, on rows of the same workload until the time
-    budget is spent; scaled to steps/s of the full batch."""
+def cpu_baseline(inps, seconds: float) -> dict:
+    """The oracle, as it stands, on rows of the same workload (the rotated
+    input sets in turn) until the time budget is spent; scaled to steps/s of
+    the full batch."""
     import numpy as np  # noqa: F401
     from threadpoolctl import threadpool_info
 
     from oracle import dsa_oracle as O
     from sparse_attention_decode_dsa_amd import workload as W
 
-    rows = list(range(inp_gpu.n_rows))
-    done = 0
-    t_total = 0.0
+    n_rows = inps[0].n_rows
+    rows = list(range(n_rows))
     # deterministic order: every 8th row first, then the rest
     order = rows[::8] + [r for r in rows if r % 8]
-    for r in order:
-        sub = W.as_numpy(W.subset(inp_gpu, [r]))
-        t0 = time.perf_counter()
-        O.decode_step(sub, inp_gpu.cfg.index_splits, inp_gpu.cfg.attn_splits)
-        t_total += time.perf_counter() - t0
-        done += 1
+    done = 0
+    t_total = 0.0
+    for inp in inps:
+        for r in order:
+            sub = W.as_numpy(W.subset(inp, [r]))
+            t0 = time.perf_counter()
+            O.decode_step(sub, inp.cfg.index_splits, inp.cfg.attn_splits)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= seconds:
+                break
         if t_total >= seconds:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": done / t_total / inp_gpu.n_rows, "unit": "steps/s", "cores": int(threads),
+    return {"value": done / t_total / n_rows, "unit": "steps/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {inp_gpu.n_rows} rows of one step, timed one row at a time "
-                      f"({t_total:.1f} s), scaled by {inp_gpu.n_rows}/{done} to a whole step"}
+            "sample": f"{done} rows ({done / n_rows:.2f} steps of {n_rows} rows, over "
+                      f"{len(inps)} input sets), timed one row at a time ({t_total:.1f} s), "
+                      f"scaled to whole steps"}
 
 
 def main():
@@ -301,7 +307,7 @@ def main():
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inps, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
