@@ -124,8 +124,8 @@ int dsa_index_scores(const uint16_t* q, const float* head_w,
                      float* scores, int32_t score_stride, int32_t* status, hipStream_t stream);
 
 /*
- * Workspace bytes dsa_topk needs for n_splits > 1: candidate keys and slots
- * [n_rows, n_splits, top_k] and per-split counts.  0 when n_splits == 1.
+ * Workspace bytes dsa_topk needs for n_splits > 1: candidate keys and slots,
+ * n_splits * top_k of each per row.  0 when n_splits == 1.
  */
 size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits);
 

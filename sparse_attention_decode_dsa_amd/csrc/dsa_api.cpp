@@ -95,7 +95,7 @@ int dsa_index_scores(const uint16_t* q, const float* head_w,
 
 size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits) {
     if (n_rows <= 0 || top_k <= 0 || n_splits <= 1) return 0;
-    return 2 * topk_ws_keys(n_rows, top_k, n_splits) + (size_t)n_rows * n_splits * sizeof(int32_t);
+    return 2 * topk_ws_keys(n_rows, top_k, n_splits);
 }
 
 int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
@@ -111,7 +111,7 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
     dsa::TopkArgs a;
     a.scores = scores; a.score_stride = score_stride; a.row_vis = row_vis;
     a.n_rows = n_rows; a.top_k = top_k; a.n_splits = n_splits;
-    a.cand_key = nullptr; a.cand_slot = nullptr; a.cand_count = nullptr;
+    a.cand_key = nullptr; a.cand_slot = nullptr;
     if (n_splits > 1) {
         const size_t need = dsa_topk_workspace_size(n_rows, top_k, n_splits);
         if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
@@ -119,7 +119,6 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
         const size_t kb = topk_ws_keys(n_rows, top_k, n_splits);
         a.cand_key = reinterpret_cast<uint32_t*>(ws);
         a.cand_slot = reinterpret_cast<int32_t*>(ws + kb);
-        a.cand_count = reinterpret_cast<int32_t*>(ws + 2 * kb);
     }
     a.topk_idx = topk_idx; a.topk_count = topk_count; a.status = status;
     return launch_status(dsa::launch_topk(a, stream));

@@ -30,9 +30,8 @@ struct TopkArgs {
     int32_t score_stride;
     const int32_t* row_vis;
     int32_t n_rows, top_k, n_splits;
-    uint32_t* cand_key;   // [n_rows, n_splits, top_k]
-    int32_t* cand_slot;   // [n_rows, n_splits, top_k]
-    int32_t* cand_count;  // [n_rows, n_splits]
+    uint32_t* cand_key;   // [n_rows, n_splits * top_k]: a row's candidates, first to last split
+    int32_t* cand_slot;   // [n_rows, n_splits * top_k]
     int32_t* topk_idx;
     int32_t* topk_count;
     int32_t* status;

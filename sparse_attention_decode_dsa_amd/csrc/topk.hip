@@ -5,14 +5,18 @@
 // order:
 //   - direct (one split): the row's scores [0, row_vis);
 //   - split pass: one contiguous slot range of the row -> candidate keys and
-//     slots in a workspace;
-//   - merge pass: the concatenated candidates of the row's splits, in split
-//     order.
+//     slots in a workspace, at an offset that the row's visible count alone
+//     fixes (the candidates of the splits before it), so the row's
+//     candidates form one list in split order;
+//   - merge pass: that list.
 // Local top-k per split followed by an exact merge equals the global top-k
 // because every member of the global top-k is in its own split's top-k.
 //
 // Scores become order-preserving uint32 keys.  Thread t holds the keys of
-// list positions [t*P, t*P + P) in registers (P = ceil(n / 1024) <= 32).
+// list positions [t*p, t*p + p) in registers (p = ceil(n / 1024) rounded up
+// to a multiple of 4, at most 32).  Every pass over them is compiled for
+// P = 4, 8, 16 or 32 keys; a launch uses the smallest P >= p of its longest
+// possible list, so short lists cost proportionally less work per thread.
 // Selection finds the k-th largest key `thr` and how many keys equal to it
 // belong to the top k, with few per-key LDS atomics (they serialise):
 //   1. the first key of every thread is a sample of the list; one atomic per
@@ -39,12 +43,15 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace dsa {
 
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kPer = kTopkMaxList / kThreads;   // keys per thread (32)
+constexpr int kPer = kTopkMaxList / kThreads;   // most keys per thread (32)
+static_assert(kPer == 32, "the largest key count with_keys_per_thread compiles for");
 constexpr int kBins0 = 4096;                    // key bits [31:20]
 constexpr int kBins1 = 1024;                    // then [19:10] and [9:0]
 constexpr int kCandCap = 4096;
@@ -62,11 +69,9 @@ struct TopkSmem {
     } u;
     uint32_t h0[kBins0];   // sample histogram, cleared before the list is staged
     uint32_t scan[2][kThreads / kWave + 1];
-    int32_t offs[kMaxSplits + 1];
     uint32_t sel_digit;
     uint32_t sel_digit2;
     uint32_t sel_need;
-    int32_t n;
 };
 
 __device__ __forceinline__ uint32_t bin0(uint32_t key) { return key >> 20; }
@@ -206,7 +211,8 @@ __device__ __forceinline__ void radix_select(TopkSmem& s, uint32_t kk, Get get, 
 // k-th largest (1 <= k < n) of the n keys, thread t holding `mine` of them
 // in key[0, mine).  s.h0 must be zero (the caller clears it before staging
 // the list).
-__device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kPer], int mine, int n, int k,
+template <int P>
+__device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[P], int mine, int n, int k,
                                            uint32_t* thr_out, uint32_t* need_out, int& tog) {
     const int tid = threadIdx.x;
     const int per = keys_per_thread(n);
@@ -236,7 +242,7 @@ __device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kP
     b_lo = max(b_lo, 1u);
     uint32_t above = 0, inside = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         const uint32_t b = bin0(key[i]);
         above += b > b_hi;
         inside += b >= b_lo && b <= b_hi;
@@ -256,7 +262,7 @@ __device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kP
         pin(b_hi);
         const uint32_t dummy = (uint32_t)kCandCap + (threadIdx.x & (kWave - 1));
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
+        for (int i = 0; i < P; ++i) {
             const uint32_t b = bin0(key[i]);
             const bool in = b >= b_lo && b <= b_hi;
             s.u.sel.cand_key[in ? at : dummy] = key[i];
@@ -308,7 +314,7 @@ __device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[kP
             thr_out, need_out, tog);
         return;
     }
-    radix_select<kPer>(
+    radix_select<P>(
         s, (uint32_t)k,
         [&](int i, uint32_t* kv) {
             if (i >= mine) return false;
@@ -331,7 +337,8 @@ static_assert(2 * (kTopkMaxK + kWave) <= kTopkMaxList, "emission buffers fit the
 // i) and keys are written to LDS at those ranks without branches (a key not
 // taken goes to the lane's dummy word), for a coalesced copy out afterwards
 // (after a barrier, by the caller).
-__device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[kPer], int base,
+template <int P>
+__device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[P], int base,
                                             uint32_t thr, uint32_t need_eq, int k, int& tog) {
     // Positions past the thread's share hold key 0, which is never above a
     // threshold; equal keys are only counted for a nonzero threshold (a zero
@@ -340,7 +347,7 @@ __device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[k
     const bool eq_ok = thr != 0u;
     uint32_t eq = 0, gt = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         eq += key[i] == eq_key && eq_ok;
         gt += key[i] > thr;
     }
@@ -356,7 +363,7 @@ __device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[k
     pin(thr2);
     pin(eq_key2);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         const bool is_eq = key[i] == eq_key2 && eq_ok;
         const bool take = key[i] > thr2 || (is_eq && eq_left > 0);
         eq_left -= (is_eq && take) ? 1u : 0u;
@@ -370,13 +377,14 @@ __device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[k
 // Direct emission (one split): the same selection as emit_to_lds, but each
 // thread walks only the set bits of its taken-key mask and writes the list
 // positions straight to `out` at their ranks.
-__device__ __forceinline__ void emit_direct(TopkSmem& s, const uint32_t (&key)[kPer], int base, uint32_t thr,
+template <int P>
+__device__ __forceinline__ void emit_direct(TopkSmem& s, const uint32_t (&key)[P], int base, uint32_t thr,
                                             uint32_t need_eq, int k, int32_t* out, int lo, int& tog) {
     const uint32_t eq_key = thr != 0u ? thr : 0xFFFFFFFFu;
     const bool eq_ok = thr != 0u;
     uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         gtm |= (key[i] > thr ? 1u : 0u) << i;
         eqm |= (key[i] == eq_key && eq_ok ? 1u : 0u) << i;
     }
@@ -405,30 +413,41 @@ __device__ __forceinline__ void emit_direct(TopkSmem& s, const uint32_t (&key)[k
 __device__ __forceinline__ int chunk_swz(int c) { return c ^ ((c >> 5) & 7); }
 
 // Keys of list positions [base, base + mine) into registers from a 16-byte
-// aligned list of floats, in 16-byte loads (coalesced across lanes, all
-// issued before any use) and 16-byte LDS accesses.  Chunks past the list
-// reload its last chunk and are never read back; positions past n in the
-// last chunk are masked.  Sets `nan` if a listed score is NaN.
-__device__ __forceinline__ void load_list_vec(TopkSmem& s, const float* src, int n, int base, int mine,
-                                              uint32_t (&key)[kPer], bool& nan) {
+// aligned list (fp32 scores, turned into keys, or keys already), in 16-byte
+// loads (coalesced across lanes, all issued before any use) and 16-byte LDS
+// accesses.  Chunks past the list reload its last chunk and are never read
+// back; positions past n in the last chunk are masked.  Sets `nan` if a
+// listed score is NaN.
+template <int P, bool kScores>
+__device__ __forceinline__ void load_list_vec(TopkSmem& s, const void* src, int n, int base, int mine,
+                                              uint32_t (&key)[P], bool& nan) {
     constexpr int kChunks = kTopkMaxList / 4;
     const int nch = (n + 3) >> 2;
-    float4 v[kPer / 4];
-#pragma unroll
-    for (int u = 0; u < kPer / 4; ++u)
-        v[u] = reinterpret_cast<const float4*>(src)[min(u * kThreads + (int)threadIdx.x, nch - 1)];
     uint4* stage4 = reinterpret_cast<uint4*>(s.u.stage);
+    if constexpr (kScores) {
+        float4 v[P / 4];
 #pragma unroll
-    for (int u = 0; u < kPer / 4; ++u) {
-        const int q = u * kThreads + (int)threadIdx.x;
-        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int u = 0; u < P / 4; ++u)
+            v[u] = reinterpret_cast<const float4*>(src)[min(u * kThreads + (int)threadIdx.x, nch - 1)];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) nan |= (f[j] != f[j]) && 4 * q + j < n;
-        stage4[chunk_swz(q)] = uint4{monotone_key(f[0]), monotone_key(f[1]), monotone_key(f[2]), monotone_key(f[3])};
+        for (int u = 0; u < P / 4; ++u) {
+            const int q = u * kThreads + (int)threadIdx.x;
+            const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) nan |= (f[j] != f[j]) && 4 * q + j < n;
+            stage4[chunk_swz(q)] = uint4{monotone_key(f[0]), monotone_key(f[1]), monotone_key(f[2]), monotone_key(f[3])};
+        }
+    } else {
+        uint4 v[P / 4];
+#pragma unroll
+        for (int u = 0; u < P / 4; ++u)
+            v[u] = reinterpret_cast<const uint4*>(src)[min(u * kThreads + (int)threadIdx.x, nch - 1)];
+#pragma unroll
+        for (int u = 0; u < P / 4; ++u) stage4[chunk_swz(u * kThreads + (int)threadIdx.x)] = v[u];
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < kPer / 4; ++m) {
+    for (int m = 0; m < P / 4; ++m) {
         const uint4 x = stage4[chunk_swz(min((base >> 2) + m, kChunks - 1))];
         key[4 * m + 0] = 4 * m + 0 < mine ? x.x : 0u;
         key[4 * m + 1] = 4 * m + 1 < mine ? x.y : 0u;
@@ -450,21 +469,21 @@ __device__ __forceinline__ int stage_index(int i) {
 // Keys of list positions [base, base + mine) into registers.  `get(i)`
 // gives the key of list position i; it is called with consecutive i across
 // lanes (coalesced) and every load of a thread is issued before any use.
-template <typename Get>
-__device__ __forceinline__ void load_list(TopkSmem& s, int n, int base, int mine, uint32_t (&key)[kPer], Get get) {
+template <int P, typename Get>
+__device__ __forceinline__ void load_list(TopkSmem& s, int n, int base, int mine, uint32_t (&key)[P], Get get) {
     // Positions past n load position n - 1 again and are never read back;
     // every index stays inside the 32768-word staging buffer.
-    uint32_t v[kPer];
+    uint32_t v[P];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < P; ++u) {
         const int i = u * kThreads + (int)threadIdx.x;
         v[u] = get(min(i, n - 1));
     }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) s.u.stage[stage_index(u * kThreads + (int)threadIdx.x)] = v[u];
+    for (int u = 0; u < P; ++u) s.u.stage[stage_index(u * kThreads + (int)threadIdx.x)] = v[u];
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < P; ++i) {
         const uint32_t x = s.u.stage[stage_index(min(base + i, kTopkMaxList - 1))];
         key[i] = i < mine ? x : 0u;
     }
@@ -484,55 +503,79 @@ __device__ __forceinline__ void pad_tail(int32_t* out, int from, int k) {
     for (int i = from + threadIdx.x; i < k; i += kThreads) out[i] = -1;
 }
 
-// One split, or the whole row: grid (n_splits, n_rows).
+// Split j of a row with `v` visible slots: [lo, hi) with split length
+// ceil(v / n_splits) rounded up to whole 16-byte chunks.
+struct SplitRange {
+    int lo, hi;
+};
+__device__ __forceinline__ SplitRange split_range(int v, int ns, int j) {
+    const int c = (((v + ns - 1) / ns) + 3) & ~3;
+    const int lo = min(v, j * c);
+    return {lo, min(v, lo + c)};
+}
+
+// Candidates that the splits before split j of a row put in the workspace
+// (each keeps min(its length, k)); with j = n_splits, the row's total.
+__device__ __forceinline__ int candidates_before(int v, int ns, int j, int k) {
+    int o = 0;
+    for (int i = 0; i < j; ++i) {
+        const SplitRange sr = split_range(v, ns, i);
+        o += min(sr.hi - sr.lo, k);
+    }
+    return o;
+}
+
+// One split, or the whole row: grid (n_splits, n_rows); no list is longer
+// than P keys per thread.
+template <int P>
 __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
     __shared__ TopkSmem s;
     const int r = blockIdx.y;
     const int j = blockIdx.x;
     const int v = checked_vis(a, r);
-    // Split length ceil(v / n_splits), rounded up to whole 16-byte chunks.
-    const int c = (((v + a.n_splits - 1) / a.n_splits) + 3) & ~3;
-    const int lo = min(v, j * c);
-    const int hi = min(v, lo + c);
-    const int n = hi - lo;
+    const SplitRange sr = split_range(v, a.n_splits, j);
+    const int lo = sr.lo;
+    const int n = sr.hi - sr.lo;
     const int k = a.top_k;
     const bool direct = a.n_splits == 1;
-    int32_t* out_idx = direct ? a.topk_idx + (size_t)r * k
-                              : a.cand_slot + ((size_t)r * a.n_splits + j) * k;
-    uint32_t* out_key = direct ? nullptr : a.cand_key + ((size_t)r * a.n_splits + j) * k;
-    const int cnt = min(n, k);
-    if (threadIdx.x == 0) {
-        if (direct) a.topk_count[r] = cnt;
-        else a.cand_count[(size_t)r * a.n_splits + j] = cnt;
-    }
+    // Output pointers are formed where they are used, so that they are not
+    // held across the selection.
+    auto cand_at = [&]() { return (size_t)r * a.n_splits * k + candidates_before(v, a.n_splits, j, k); };
+    if (direct && threadIdx.x == 0) a.topk_count[r] = min(n, k);
     const float* src = a.scores + (size_t)r * a.score_stride + lo;
     if (n <= k) {
         // Everything in the range is selected.
         if (direct) {
+            int32_t* out_idx = a.topk_idx + (size_t)r * k;
             for (int i = threadIdx.x; i < n; i += kThreads) out_idx[i] = lo + i;
             pad_tail(out_idx, n, k);
         } else {
+            const size_t at = cand_at();
             bool nan = false;
             for (int i = threadIdx.x; i < n; i += kThreads) {
                 const float f = src[i];
                 nan |= (f != f);
-                out_idx[i] = lo + i;
-                out_key[i] = monotone_key(f);
+                a.cand_slot[at + i] = lo + i;
+                a.cand_key[at + i] = monotone_key(f);
             }
             if (__ballot(nan) != 0ull && (threadIdx.x & 63) == 0) flag(a.status, DSA_DEV_NAN);
         }
         return;
     }
     const int per = keys_per_thread(n);
+    if (per > P) {   // the launch bound the list length by score_stride
+        if (threadIdx.x == 0) flag(a.status, DSA_DEV_ROW_RANGE);
+        return;
+    }
     const int base = threadIdx.x * per;
     const int mine = max(0, min(per, n - base));
-    uint32_t key[kPer];
+    uint32_t key[P];
     bool nan = false;
     for (int i = threadIdx.x; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
     if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-        load_list_vec(s, src, n, base, mine, key, nan);
+        load_list_vec<P, true>(s, src, n, base, mine, key, nan);
     } else {
-        load_list(s, n, base, mine, key, [&](int i) {
+        load_list<P>(s, n, base, mine, key, [&](int i) {
             const float f = src[i];
             nan |= (f != f);
             return monotone_key(f);
@@ -541,90 +584,102 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
     if (__ballot(nan) != 0ull && (threadIdx.x & 63) == 0) flag(a.status, DSA_DEV_NAN);
     uint32_t thr, need;
     int tog = 0;
-    select_kth(s, key, mine, n, k, &thr, &need, tog);
+    select_kth<P>(s, key, mine, n, k, &thr, &need, tog);
     // A right selection takes exactly k keys; ranks are clamped below k so
     // that a wrong one could not write past the buffers.
     if (direct) {
-        emit_direct(s, key, base, thr, need, k, out_idx, lo, tog);
+        emit_direct<P>(s, key, base, thr, need, k, a.topk_idx + (size_t)r * k, lo, tog);
     } else {
-        emit_to_lds(s, key, base, thr, need, k, tog);
+        emit_to_lds<P>(s, key, base, thr, need, k, tog);
         __syncthreads();
+        const size_t at = cand_at();
         for (int i = threadIdx.x; i < k; i += kThreads) {
-            out_idx[i] = lo + (int)s.u.stage[kEmitPos + i];
-            out_key[i] = s.u.stage[kEmitKey + i];
+            a.cand_slot[at + i] = lo + (int)s.u.stage[kEmitPos + i];
+            a.cand_key[at + i] = s.u.stage[kEmitKey + i];
         }
     }
 }
 
-// Split owning position `pos` of the concatenated candidate list: the last
-// split whose offset is <= pos (empty splits share the next one's offset).
-__device__ __forceinline__ int split_of(const TopkSmem& s, int ns, int pos) {
-    int lo = 0, hi = ns - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s.offs[mid] <= pos) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-// Merge of the split candidates of one row: grid (n_rows).
+// Merge of the split candidates of one row: grid (n_rows).  The row's
+// candidates are the first n entries of its workspace block, in split order
+// (n <= n_splits * k, at most P keys per thread).
+template <int P>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     __shared__ TopkSmem s;
     const int r = blockIdx.x;
     const int k = a.top_k;
     const int ns = a.n_splits;
     int32_t* out_idx = a.topk_idx + (size_t)r * k;
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        const int c = lane < ns ? min(max(a.cand_count[(size_t)r * ns + lane], 0), k) : 0;
-        const uint32_t inc = wave_inclusive_scan((uint32_t)c);
-        if (lane < ns) s.offs[lane] = (int)(inc - c);
-        if (lane == 63) s.n = (int)inc;
-    }
-    __syncthreads();
-    const int n = s.n;
+    const int n = candidates_before(checked_vis(a, r), ns, ns, k);
     if (threadIdx.x == 0) a.topk_count[r] = min(n, k);
     const int32_t* cslot = a.cand_slot + (size_t)r * ns * k;
     const uint32_t* ckey = a.cand_key + (size_t)r * ns * k;
-    // Candidate list position -> its entry in the workspace.
-    auto entry = [&](int pos) -> size_t {
-        const int j = split_of(s, ns, pos);
-        return (size_t)j * k + (pos - s.offs[j]);
-    };
-    const int per = keys_per_thread(n);
-    const int base = threadIdx.x * per;
-    const int mine = max(0, min(per, n - base));
     if (n <= k) {
         // Every candidate is selected, in list order.
-        int32_t sl[kPer];
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) sl[i] = i < mine ? cslot[entry(base + i)] : -1;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (i < mine) out_idx[base + i] = sl[i];
+        for (int i = threadIdx.x; i < n; i += kThreads) out_idx[i] = cslot[i];
         pad_tail(out_idx, n, k);
         return;
     }
-    uint32_t key[kPer];
+    const int per = keys_per_thread(n);
+    if (per > P) {   // cannot happen: n <= n_splits * k, which the launch bounds
+        if (threadIdx.x == 0) flag(a.status, DSA_DEV_ROW_RANGE);
+        return;
+    }
+    const int base = threadIdx.x * per;
+    const int mine = max(0, min(per, n - base));
+    uint32_t key[P];
     for (int i = threadIdx.x; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
-    load_list(s, n, base, mine, key, [&](int i) { return ckey[entry(i)]; });
+    if ((reinterpret_cast<uintptr_t>(ckey) & 15) == 0) {
+        bool unused = false;
+        load_list_vec<P, false>(s, ckey, n, base, mine, key, unused);
+    } else {
+        load_list<P>(s, n, base, mine, key, [&](int i) { return ckey[i]; });
+    }
     uint32_t thr, need;
     int tog = 0;
-    select_kth(s, key, mine, n, k, &thr, &need, tog);
-    emit_to_lds(s, key, base, thr, need, k, tog);
+    select_kth<P>(s, key, mine, n, k, &thr, &need, tog);
+    emit_to_lds<P>(s, key, base, thr, need, k, tog);
     __syncthreads();
-    for (int i = threadIdx.x; i < k; i += kThreads) out_idx[i] = cslot[entry((int)s.u.stage[kEmitPos + i])];
+    for (int i = threadIdx.x; i < k; i += kThreads) out_idx[i] = cslot[s.u.stage[kEmitPos + i]];
+}
+
+}  // namespace
+
+namespace {
+
+// Keys per thread a launch is compiled for: the smallest of 4, 8, 16, 32
+// that holds a list of up to `longest` entries.
+int keys_class(int64_t longest) {
+    const int64_t per = (longest + 4 * kThreads - 1) / (4 * kThreads) * 4;
+    return per <= 4 ? 4 : per <= 8 ? 8 : per <= 16 ? 16 : 32;
+}
+
+template <typename F>
+hipError_t by_class(int cls, F f) {
+    switch (cls) {
+        case 4: return f(std::integral_constant<int, 4>{});
+        case 8: return f(std::integral_constant<int, 8>{});
+        case 16: return f(std::integral_constant<int, 16>{});
+        default: return f(std::integral_constant<int, 32>{});
+    }
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     if (a.n_rows == 0) return hipSuccess;
-    topk_split_kernel<<<dim3(a.n_splits, a.n_rows), kThreads, 0, stream>>>(a);
-    hipError_t e = hipGetLastError();
+    // Longest split: ceil(score_stride / n_splits) rounded up to whole chunks
+    // (row_vis <= score_stride is checked on the device).
+    const int64_t split_max = (((int64_t)a.score_stride + a.n_splits - 1) / a.n_splits + 3) & ~int64_t{3};
+    hipError_t e = by_class(keys_class(split_max), [&](auto pc) {
+        topk_split_kernel<decltype(pc)::value><<<dim3(a.n_splits, a.n_rows), kThreads, 0, stream>>>(a);
+        return hipGetLastError();
+    });
     if (e != hipSuccess || a.n_splits == 1) return e;
-    topk_merge_kernel<<<a.n_rows, kThreads, 0, stream>>>(a);
-    return hipGetLastError();
+    return by_class(keys_class((int64_t)a.n_splits * a.top_k), [&](auto pc) {
+        topk_merge_kernel<decltype(pc)::value><<<a.n_rows, kThreads, 0, stream>>>(a);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace dsa
