@@ -21,6 +21,11 @@ context parallel (DCP) for GLM-5 / DeepSeek-V3.2" (sgl-project/sglang PR
   LSE; with a single split the partial already is the result.
 * Page "DeepSeek V4 DSpark Internals" (pypto.ai), kernel mapping: block tables
   hold -1 past each request's span.
+* The step before the path, the cache write: Modifications ("Writes", and the
+  fused rope + KV-cache write named under "Disabled under DCP") and Future
+  work (the write location computed once per step and fused into the write
+  kernels).  New tokens' MLA rows (rope part rotated) and index keys are
+  quantized to fp8 with one fp32 scale per token and stored at their slots.
 
 The pages never print the formulas.  The readings taken here are the plainest
 ones consistent with the configurations: indexer score
@@ -127,6 +132,123 @@ def quantize_q(q_bf16_bits) -> tuple[np.ndarray, np.ndarray]:
     scale[nz] = np.exp2(np.ceil(np.log2(amax[nz] / FP8_MAX)))
     codes = fp8_e4m3fn_encode_rne(q / scale[..., None])
     return codes, scale
+
+
+# ---------------------------------------------------------------------------
+# Cache write (the step before the path: new tokens into the paged caches)
+# ---------------------------------------------------------------------------
+
+D_LATENT_W = 512   # latent entries of an MLA row
+D_ROPE_W = 64      # rope entries of an MLA row, rotated before they are stored
+D_INDEX_W = 128    # entries of an index key
+KV_ROW_BYTES_W = 640   # bytes of an MLA cache row: 576 codes, fp32 scale at 576, pad
+
+
+def rope_interleaved_f32(rope_bits, cos, sin, pos) -> np.ndarray:
+    """Rotary embedding of the rope part of new MLA rows, in float32.
+
+    The page "[ROCm] Support decode context parallel (DCP) for GLM-5 /
+    DeepSeek-V3.2" names a fused rope + KV-cache write (Modifications,
+    "Disabled under DCP") but not the rotation.  Reading taken here: the 64
+    rope entries form 32 pairs (2j, 2j+1), and pair j of a token at position
+    p is turned by the angle whose cosine and sine the caller tabulates at
+    cos[p, j], sin[p, j]:
+        y[2j]   = x[2j] * c - x[2j+1] * s
+        y[2j+1] = x[2j] * s + x[2j+1] * c
+    each product rounded to float32, then the sum or difference (no fused
+    multiply-add), which fixes every bit of the result.  The position of a
+    token is the slot it is written to.
+
+    rope_bits uint16 [n, 64] bf16; cos, sin float32 [max_pos, 32]; pos [n].
+    Returns float32 [n, 64].
+    """
+    x = bf16_decode(rope_bits).astype(np.float32)
+    pos = np.asarray(pos, dtype=np.int64)
+    c = np.asarray(cos, dtype=np.float32)[pos]
+    s = np.asarray(sin, dtype=np.float32)[pos]
+    x0, x1 = x[:, 0::2], x[:, 1::2]
+    y = np.empty_like(x)
+    y[:, 0::2] = (x0 * c) - (x1 * s)
+    y[:, 1::2] = (x0 * s) + (x1 * c)
+    return y
+
+
+def quantize_rows_f32(v) -> tuple[np.ndarray, np.ndarray]:
+    """E4M3FN codes and one fp32 scale per row, the rule the caches are
+    written with: scale = max|x| / 448 (1 for an all-zero row) and
+    code = RNE(clamp(x / scale, -448, 448)), the division and the scale in
+    float32, so that the decision of every code is taken in float32.
+
+    The pages fix only "fp8 rows with an fp32 scale per token"; max|x| / 448
+    is the plainest scale that uses the format's whole range.
+    v float32 [n, d].  Returns (codes uint8 [n, d], scale float32 [n]).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.max(np.abs(v), axis=1)
+    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    y = np.clip(v / scale[:, None], np.float32(-FP8_MAX), np.float32(FP8_MAX))
+    return fp8_e4m3fn_encode_rne(y.astype(np.float64)), scale
+
+
+def cache_write(latent_bits, rope_bits, index_bits, cos, sin, tok_req, tok_slot, page_table,
+                page_size: int, kv_cache, k_code, k_scale):
+    """Write new tokens into the paged caches.
+
+    Token i belongs to request tok_req[i] and is stored at logical slot
+    tok_slot[i] (its position): physical row page_table[b][t / P] * P + t % P
+    (page "DeepSeek V4 DSpark Internals", kernel mapping).  Its MLA row is
+    the 512 latent entries followed by the 64 rope entries rotated as in
+    rope_interleaved_f32 (no rotation when cos is None), quantized as in
+    quantize_rows_f32 into bytes 0..575 of the row with the scale at bytes
+    576..579; bytes 580..639 are left as they are.  Its 128-entry index key
+    is quantized the same way into k_code / k_scale, unrotated (the pages say
+    nothing of a rotation of the index key; a caller rotates it beforehand).
+    A token whose request, slot or page id is out of range, or whose position
+    lies past the rotation tables, writes nothing.
+
+    Inputs are not modified.  Returns (kv_cache, k_code, k_scale, written)
+    with written bool [n].
+    """
+    latent_bits = np.asarray(latent_bits, dtype=np.uint16)
+    rope_bits = np.asarray(rope_bits, dtype=np.uint16)
+    index_bits = np.asarray(index_bits, dtype=np.uint16)
+    tok_req = np.asarray(tok_req, dtype=np.int64)
+    tok_slot = np.asarray(tok_slot, dtype=np.int64)
+    page_table = np.asarray(page_table, dtype=np.int64)
+    kv = np.array(kv_cache, dtype=np.uint8, copy=True)
+    kc = np.array(k_code, dtype=np.uint8, copy=True)
+    ks = np.array(k_scale, dtype=np.float32, copy=True)
+    n_pages = kv.shape[0]
+    batch, max_pages = page_table.shape
+    n = len(tok_req)
+    written = np.zeros(n, dtype=bool)
+    if n == 0:
+        return kv, kc, ks, written
+    if cos is None:
+        rope = bf16_decode(rope_bits).astype(np.float32)
+    else:
+        pos = np.clip(tok_slot, 0, np.asarray(cos).shape[0] - 1)
+        rope = rope_interleaved_f32(rope_bits, cos, sin, pos)
+    mla = np.concatenate([bf16_decode(latent_bits).astype(np.float32), rope], axis=1)
+    mla_codes, mla_scale = quantize_rows_f32(mla)
+    idx_codes, idx_scale = quantize_rows_f32(bf16_decode(index_bits).astype(np.float32))
+    for i in range(n):
+        b, t = int(tok_req[i]), int(tok_slot[i])
+        if not (0 <= b < batch and 0 <= t < max_pages * page_size):
+            continue
+        if cos is not None and t >= np.asarray(cos).shape[0]:
+            continue
+        page = int(page_table[b, t // page_size])
+        if not (0 <= page < n_pages):
+            continue
+        off = t % page_size
+        kv[page, off, :D_LATENT_W + D_ROPE_W] = mla_codes[i]
+        kv[page, off, D_LATENT_W + D_ROPE_W:D_LATENT_W + D_ROPE_W + 4] = \
+            np.frombuffer(np.float32(mla_scale[i]).tobytes(), dtype=np.uint8)
+        kc[page, off] = idx_codes[i]
+        ks[page, off] = idx_scale[i]
+        written[i] = True
+    return kv, kc, ks, written
 
 
 # ---------------------------------------------------------------------------
