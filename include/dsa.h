@@ -13,6 +13,8 @@
  *                            (partial output, natural-log LSE) pairs
  *   4. dsa_lse_merge         merge of the split partials by their LSE
  * dsa_quantize_q exposes the query quantization of step 1 on its own.
+ * dsa_cache_write is the step before the path: it stores new tokens' MLA rows
+ * and index keys in the paged caches the four steps read.
  *
  * Conventions shared by every entry point:
  *  - Every array pointer is DEVICE memory owned by the caller.  The library
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 5
+#define DSA_ABI_VERSION 6
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -73,8 +75,44 @@ enum {
     DSA_DEV_ROW_RANGE = 4,  /* row_req out of [0, batch), or row_vis < 0, > kv_len,
                                > max_pages * page_size or > score_stride */
     DSA_DEV_GROUP = 8,      /* rows of one scoring group belong to different requests */
-    DSA_DEV_NAN = 16        /* a NaN score reached the top-k (ordered, but reported) */
+    DSA_DEV_NAN = 16,       /* a NaN score reached the top-k (ordered, but reported) */
+    DSA_DEV_WRITE = 32      /* a new token's request, slot or position is out of range */
 };
+
+/*
+ * dsa_cache_write -- new tokens into the paged caches (subject page,
+ * Modifications: writes and the fused rope + KV-cache write; Future work:
+ * the write location computed once per step inside the write kernel).
+ * Token i of request tok_req[i] is stored at logical slot t = tok_slot[i]
+ * (its position), physical row page_table[b][t / P] * P + t % P:
+ *   MLA row: the 512 latent entries, then the 64 rope entries with pair
+ *     (2j, 2j+1) of a token at position t turned by c = rope_cos[t][j],
+ *     s = rope_sin[t][j]:  y0 = x0*c - x1*s,  y1 = x0*s + x1*c  (each product
+ *     and the sum rounded to fp32 on its own); no rotation when both tables
+ *     are NULL.  Codes E4M3FN of clamp(x / scale, +-448) rounded to nearest
+ *     even, scale = max|x| / 448 in fp32 (1 for an all-zero row), into bytes
+ *     0..575 of the row, the scale at bytes 576..579; bytes 580..639 are not
+ *     written.
+ *   index key: its 128 entries, unrotated, quantized the same way into
+ *     k_code[row] with k_scale[row].
+ *   latent [n_tok, 512], rope [n_tok, 64], index_k [n_tok, 128] bf16 bit
+ *     patterns, 16-byte aligned rows; rope_cos, rope_sin [max_pos, 32] f32 or
+ *     both NULL; tok_req, tok_slot [n_tok] i32; page_table [batch, max_pages].
+ *   kv_cache [num_pages, page_size, 640] u8, k_code [num_pages, page_size,
+ *     128] u8, k_scale [num_pages, page_size] f32: written in place.
+ * A token whose request is out of [0, batch), whose slot is out of
+ * [0, max_pages * page_size) or whose position is >= max_pos (with tables)
+ * writes nothing and sets DSA_DEV_WRITE; one whose page id is out of
+ * [0, num_pages) writes nothing and sets DSA_DEV_PAGE_OOB.  Two tokens with
+ * the same destination leave either one's row.  n_tok == 0 enqueues nothing
+ * and reads no array (its pointers may be NULL).
+ */
+int dsa_cache_write(const uint16_t* latent, const uint16_t* rope, const uint16_t* index_k,
+                    const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                    const int32_t* tok_req, const int32_t* tok_slot, int32_t n_tok,
+                    const int32_t* page_table, int32_t batch, int32_t num_pages, int32_t max_pages,
+                    int32_t page_size, uint8_t* kv_cache, uint8_t* k_code, float* k_scale,
+                    int32_t* status, hipStream_t stream);
 
 /* DSA_ABI_VERSION of the built library; loaders refuse a mismatch. */
 int dsa_abi_version(void);

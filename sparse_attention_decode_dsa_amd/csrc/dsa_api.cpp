@@ -93,6 +93,36 @@ int dsa_index_scores(const uint16_t* q, const float* head_w,
     return launch_status(dsa::launch_index_scores(a, stream));
 }
 
+int dsa_cache_write(const uint16_t* latent, const uint16_t* rope, const uint16_t* index_k,
+                    const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                    const int32_t* tok_req, const int32_t* tok_slot, int32_t n_tok,
+                    const int32_t* page_table, int32_t batch, int32_t num_pages, int32_t max_pages,
+                    int32_t page_size, uint8_t* kv_cache, uint8_t* k_code, float* k_scale,
+                    int32_t* status, hipStream_t stream) {
+    if (n_tok < 0 || n_tok > kMaxRows) return DSA_ERR_SHAPE;
+    int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
+    if (rc != DSA_OK) return rc;
+    if ((rope_cos == nullptr) != (rope_sin == nullptr)) return DSA_ERR_NULL;
+    if (rope_cos != nullptr && max_pos < 1) return DSA_ERR_SHAPE;
+    if (n_tok == 0) return DSA_OK;   // nothing to enqueue; no array is read
+    if (!latent || !rope || !index_k || !tok_req || !tok_slot || !page_table || !kv_cache || !k_code ||
+        !k_scale || !status)
+        return DSA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(latent) & 15) != 0 || (reinterpret_cast<uintptr_t>(rope) & 3) != 0 ||
+        (reinterpret_cast<uintptr_t>(index_k) & 3) != 0 || (reinterpret_cast<uintptr_t>(kv_cache) & 7) != 0 ||
+        (reinterpret_cast<uintptr_t>(k_code) & 1) != 0 || (reinterpret_cast<uintptr_t>(k_scale) & 3) != 0)
+        return DSA_ERR_SHAPE;
+    dsa::CacheWriteArgs a;
+    a.latent = latent; a.rope = rope; a.index_k = index_k;
+    a.rope_cos = rope_cos; a.rope_sin = rope_sin; a.max_pos = max_pos;
+    a.tok_req = tok_req; a.tok_slot = tok_slot; a.n_tok = n_tok;
+    a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
+    a.page_size = page_size; a.log2_page = log2i(page_size);
+    a.page_table = page_table; a.kv_cache = kv_cache; a.k_code = k_code; a.k_scale = k_scale;
+    a.status = status;
+    return launch_status(dsa::launch_cache_write(a, stream));
+}
+
 size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits) {
     if (n_rows <= 0 || top_k <= 0 || n_splits <= 1) return 0;
     return 2 * topk_ws_keys(n_rows, top_k, n_splits);

@@ -54,6 +54,23 @@ struct MlaArgs {
     int32_t* status;
 };
 
+struct CacheWriteArgs {
+    const uint16_t* latent;    // [n_tok, 512] bf16
+    const uint16_t* rope;      // [n_tok, 64] bf16, before rotation
+    const uint16_t* index_k;   // [n_tok, 128] bf16
+    const float* rope_cos;     // [max_pos, 32] or null (no rotation)
+    const float* rope_sin;
+    int32_t max_pos;
+    const int32_t* tok_req;
+    const int32_t* tok_slot;
+    int32_t n_tok, batch, num_pages, max_pages, page_size, log2_page;
+    const int32_t* page_table;
+    uint8_t* kv_cache;         // [num_pages, page_size, 640]
+    uint8_t* k_code;           // [num_pages, page_size, 128]
+    float* k_scale;            // [num_pages, page_size]
+    int32_t* status;
+};
+
 struct MergeArgs {
     const float* part_o;
     const float* part_lse;
@@ -73,5 +90,6 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
 
 }  // namespace dsa

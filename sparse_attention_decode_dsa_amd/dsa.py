@@ -17,10 +17,11 @@ import os
 
 import torch
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
-DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN"}
+DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE"}
+DEV_PAGE_OOB, DEV_TOPK_OOB, DEV_ROW_RANGE, DEV_GROUP, DEV_NAN, DEV_WRITE = 1, 2, 4, 8, 16, 32
 
 
 class DsaError(RuntimeError):
@@ -41,6 +42,8 @@ _SIGS = {
     "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "dsa_lse_merge": ([_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
+    "dsa_cache_write": ([_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
+                         _p, _p, _p, _p, _p], ctypes.c_int),
 }
 
 _lib = None
@@ -230,6 +233,28 @@ def lse_merge(part_o, part_lse, out=None, out_lse=None, stream=None):
                                _ptr(out, _BF16, "out"), _ptr(out_lse, torch.float32, "out_lse"),
                                _stream(stream)), "dsa_lse_merge")
     return out, out_lse
+
+
+def cache_write(latent, rope, index_k, tok_req, tok_slot, page_table, kv_cache, k_code, k_scale,
+                rope_cos=None, rope_sin=None, status=None, stream=None):
+    """New tokens into the paged caches, in place: latent bf16 [n, 512], rope
+    bf16 [n, 64] (rotated by rope_cos / rope_sin f32 [max_pos, 32] at each
+    token's slot, or stored as given), index_k bf16 [n, 128]; returns status."""
+    n = latent.shape[0]
+    n_pages, p, _ = kv_cache.shape
+    batch, max_pages = page_table.shape
+    if status is None:
+        status = new_status(latent.device)
+    max_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    _check(lib().dsa_cache_write(
+        _ptr(latent, _BF16, "latent"), _ptr(rope, _BF16, "rope"), _ptr(index_k, _BF16, "index_k"),
+        _ptr(rope_cos, torch.float32, "rope_cos"), _ptr(rope_sin, torch.float32, "rope_sin"), max_pos,
+        _ptr(tok_req, torch.int32, "tok_req"), _ptr(tok_slot, torch.int32, "tok_slot"), n,
+        _ptr(page_table, torch.int32, "page_table"), batch, n_pages, max_pages, p,
+        _ptr(kv_cache, torch.uint8, "kv_cache"), _ptr(k_code, _FP8, "k_code"),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(status, torch.int32, "status"),
+        _stream(stream)), "dsa_cache_write")
+    return status
 
 
 class DecodeStep:

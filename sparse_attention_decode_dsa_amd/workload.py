@@ -321,3 +321,55 @@ def as_numpy(inp: Inputs) -> dict:
         "row_req": inp.row_req.cpu().numpy(), "row_vis": inp.row_vis.cpu().numpy(),
         "page_size": inp.page_size, "top_k": inp.top_k, "sm_scale": inp.sm_scale,
     }
+
+
+# --------------------------------------------------------------------------
+# New tokens for the cache write (the step before the decode path)
+# --------------------------------------------------------------------------
+
+ROPE_BASE = 10000.0
+
+
+@dataclass
+class NewTokens:
+    latent: torch.Tensor      # bf16 [n, 512]
+    rope: torch.Tensor        # bf16 [n, 64], before rotation
+    index_k: torch.Tensor     # bf16 [n, 128]
+    tok_req: torch.Tensor     # i32 [n]
+    tok_slot: torch.Tensor    # i32 [n]
+    rope_cos: torch.Tensor    # f32 [max_pos, 32]
+    rope_sin: torch.Tensor    # f32 [max_pos, 32]
+
+
+def rope_tables(max_pos: int, base: float = ROPE_BASE, device="cpu"):
+    """cos / sin f32 [max_pos, 32] of the angles pos * base^(-j / 32): an
+    input of the cache write, tabulated the usual way."""
+    j = torch.arange(32, dtype=torch.float64)
+    theta = torch.arange(max_pos, dtype=torch.float64)[:, None] * base ** (-j / 32.0)[None, :]
+    return theta.cos().float().to(device), theta.sin().float().to(device)
+
+
+def make_new_tokens(inp: Inputs, tok_req, tok_slot, seed: int = 0, device=None) -> NewTokens:
+    """Seeded bf16 rows for tokens (tok_req[i], tok_slot[i]): latent, rope and
+    index entries N(0, 1) times a per-token magnitude in [1e-3, 1e2], with an
+    all-zero token and a token holding -0.0 entries when there are enough
+    tokens; rotation tables cover every slot of the block table."""
+    device = device or inp.k_code.device
+    g = torch.Generator().manual_seed(seed)
+    tok_req = torch.as_tensor(tok_req, dtype=torch.int32)
+    tok_slot = torch.as_tensor(tok_slot, dtype=torch.int32)
+    n = int(tok_req.shape[0])
+    mag = torch.exp(torch.empty(n, 1).uniform_(math.log(1e-3), math.log(1e2), generator=g))
+    latent = torch.randn(n, 512, generator=g) * mag
+    rope = torch.randn(n, 64, generator=g) * mag
+    index_k = torch.randn(n, 128, generator=g) * mag
+    if n >= 3:
+        latent[1] = 0.0
+        rope[1] = 0.0
+        index_k[1] = 0.0
+        latent[2, ::7] = -0.0
+        index_k[2, ::5] = -0.0
+    cos, sin = rope_tables(inp.max_pages * inp.page_size)
+    return NewTokens(latent=latent.to(torch.bfloat16).to(device), rope=rope.to(torch.bfloat16).to(device),
+                     index_k=index_k.to(torch.bfloat16).to(device), tok_req=tok_req.to(device),
+                     tok_slot=tok_slot.to(device), rope_cos=cos.to(device), rope_sin=sin.to(device))

@@ -32,7 +32,8 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_index_scores",
-            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_merge"} <= set(names)
+            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_merge",
+            "dsa_cache_write"} <= set(names)
     raw = ctypes.CDLL(dsa.lib_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -131,3 +132,27 @@ def test_lse_merge_and_quantize_validation(L):
     assert q(P, -1, 64, 128, P, P, None) == SHAPE
     assert q(None, 4, 64, 128, P, P, None) == NULL
     assert q(P, 0, 64, 128, P, P, None) == OK
+
+
+def _cw(L, **kw):
+    a = dict(latent=P, rope=P, index_k=P, rope_cos=None, rope_sin=None, max_pos=0, tok_req=P, tok_slot=P,
+             n_tok=4, page_table=P, batch=2, num_pages=10, max_pages=5, page_size=256, kv_cache=P,
+             k_code=P, k_scale=P, status=P, stream=None)
+    a.update(kw)
+    return L.dsa_cache_write(*a.values())
+
+
+def test_cache_write_validation(L):
+    assert _cw(L, n_tok=-1) == SHAPE
+    assert _cw(L, page_size=100) == UNSUP
+    assert _cw(L, batch=0) == SHAPE
+    assert _cw(L, rope_cos=P) == NULL                         # one table without the other
+    assert _cw(L, rope_cos=P, rope_sin=P, max_pos=0) == SHAPE
+    assert _cw(L, latent=None) == NULL
+    assert _cw(L, kv_cache=None) == NULL
+    assert _cw(L, status=None) == NULL
+    assert _cw(L, latent=P + 8) == SHAPE                      # rows must be 16-byte aligned
+    assert _cw(L, kv_cache=P + 4) == SHAPE
+    assert _cw(L, n_tok=0) == OK                              # nothing to enqueue
+    assert _cw(L, n_tok=0, latent=None, kv_cache=None) == OK  # empty batches may pass NULL arrays
+    assert _cw(L, n_tok=0, rope_cos=P, rope_sin=P, max_pos=64) == OK
