@@ -5,8 +5,8 @@
 A step is the whole hot path for one batch: fp8 indexer scores over every
 cached token (the bf16 indexer queries quantized in the kernel), exact
 top-2048 (per split, then merged), split-K sparse absorbed-MLA attention over
-the selected paged fp8 rows (the bf16 query split into two fp8 terms in the
-kernel), and the LSE merge.  Inputs are seeded synthetic tensors already resident
+the selected paged fp8 rows (QK on bf16 matrix cores with the bf16 query as it
+is), and the LSE merge.  Inputs are seeded synthetic tensors already resident
 in HBM.  Prints ONE JSON line (rank 0).
 
 The default workload is bulk decode at the metric's point: 64 requests, one
@@ -21,8 +21,10 @@ memory-side cache: every step reads its inputs from HBM, as the layers of a
 real decode step do.  Then every kernel is replayed back to back from a graph
 of 20 launches (cycling through the input sets) between two HIP events on the
 stream it runs on, for per-kernel durations and the roofline of the dominant
-kernel.  The oracle (fp64, CPU) is timed on a bounded sample of the same
-workload as a reported baseline.
+kernel.  The cache write (the step before the path: one new token per request
+into the paged caches) is timed the same way and reported on its own; it is
+not part of the step.  The oracle (fp64, CPU) is timed on a bounded sample of
+the same workload as a reported baseline.
 """
 
 from __future__ import annotations
@@ -60,6 +62,9 @@ def parse():
                     help="independent input sets that consecutive steps and launches cycle through, "
                          "so that no launch re-reads what the one before left in the memory-side cache")
     return ap.parse_args()
+
+
+CACHE_WRITE_BYTES_PER_TOKEN = 1024 + 128 + 256 + 256 + 12 + 580 + 132
 
 
 def algorithmic_bytes(inp) -> dict:
@@ -221,8 +226,20 @@ def main():
                 part_lse=st.part_lse, status=st.status)
             fns["lse_merge"] = lambda: dsa.lse_merge(st.part_o, st.part_lse, out=st.out,
                                                      out_lse=st.out_lse)
+        # The step before the path, timed on its own: one new token per
+        # request, written at its last slot (kv_len - 1) with the rope part
+        # rotated.  It runs after the timed steps, so they never see it.
+        nt = new_tokens[id(i)]
+        fns["cache_write"] = lambda: dsa.cache_write(
+            nt.latent, nt.rope, nt.index_k, nt.tok_req, nt.tok_slot, i.page_table, i.kv_cache,
+            i.k_code, i.k_scale, rope_cos=nt.rope_cos, rope_sin=nt.rope_sin, status=st.status)
         return fns
 
+    new_tokens = {}
+    for k, x in enumerate(inps):
+        live = torch.nonzero(x.kv_lens > 0).flatten().cpu()
+        new_tokens[id(x)] = W.make_new_tokens(x, live, (x.kv_lens[live] - 1).cpu(), seed=base_seed + k)
+    n_new = int(new_tokens[id(inps[0])].tok_req.shape[0])
     per_set = [kernel_launches(x, st) for x, st in zip(inps, steps)]
     kern_us = {}
     reps = 20
@@ -305,6 +322,16 @@ def main():
         "step_algorithmic_bytes": ab["step"],
         "step_hbm_frac": ab["step"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
+        # The step before the path (not in the step above): per new token it
+        # reads 1024 + 128 + 256 B of bf16 rows, a 256 B cos/sin row, 12 B of
+        # request, slot and page id, and writes 580 + 132 B of codes and scales.
+        "cache_write": {
+            "tokens": n_new,
+            "us_per_launch": round(kern_us["cache_write"], 2),
+            "algorithmic_bytes": CACHE_WRITE_BYTES_PER_TOKEN * n_new,
+            "achieved_GBps": round(CACHE_WRITE_BYTES_PER_TOKEN * n_new / (kern_us["cache_write"] * 1e3), 1),
+            "bound": "latency",
+        },
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inps, args.cpu_seconds)
