@@ -26,6 +26,9 @@ context parallel (DCP) for GLM-5 / DeepSeek-V3.2" (sgl-project/sglang PR
   work (the write location computed once per step and fused into the write
   kernels).  New tokens' MLA rows (rope part rotated) and index keys are
   quantized to fp8 with one fp32 scale per token and stored at their slots.
+* The step after the path: Future work, projecting V (W_UV) before the LSE
+  merge; here the merge is followed by the projection, which is the same
+  linear map applied once.
 
 The pages never print the formulas.  The readings taken here are the plainest
 ones consistent with the configurations: indexer score
@@ -443,6 +446,38 @@ def lse_merge(part_o, part_lse) -> tuple[np.ndarray, np.ndarray]:
     out = np.sum(wts[..., None] * po, axis=-2) / np.where(empty, 1.0, tot)
     out = np.where(empty, 0.0, out)
     return out, lse
+
+
+def project_v(out_latent, w_uv_bits) -> np.ndarray:
+    """The value projection W_UV of absorbed MLA, applied to latent outputs.
+
+    Page "[ROCm] Support decode context parallel (DCP) for GLM-5 /
+    DeepSeek-V3.2", Future work: projecting V before the LSE merge (a
+    follow-up that cut decode ITL).  Absorbed MLA keeps the attention output
+    in the 512-wide latent space (R11); head h's value output is
+    v[d] = sum_k latent[k] * W[h][d][k] for d < Dv.  The page gives no Dv or
+    layout; reading: Dv = 128 and the weights bf16 [H, Dv, 512] (each output
+    dimension's weights one contiguous row).
+
+    out_latent [..., H, 512] float; w_uv_bits uint16 [H, Dv, 512] bf16.
+    Returns float64 [..., H, Dv].
+    """
+    x = np.asarray(out_latent, dtype=np.float64)
+    w = bf16_decode(w_uv_bits)
+    return np.einsum("...hk,hdk->...hd", x, w)
+
+
+def lse_merge_project(part_o, part_lse, w_uv_bits) -> tuple[np.ndarray, np.ndarray]:
+    """The LSE merge followed by the value projection: since the projection
+    is linear and the merge is a weighted sum with weights summing to one,
+    this equals projecting each split before merging (the page's order),
+    with the merge applied once instead of per split.
+
+    part_o [R, H, S, 512]; part_lse [R, H, S]; w_uv_bits [H, Dv, 512].
+    Returns (out [R, H, Dv] float64, lse [R, H]).
+    """
+    out, lse = lse_merge(part_o, part_lse)
+    return project_v(out, w_uv_bits), lse
 
 
 def gather_mla_rows(kv_code, kv_scale, page_table_row, slots, page_size: int) -> np.ndarray:
