@@ -15,6 +15,8 @@
  * dsa_quantize_q exposes the query quantization of step 1 on its own.
  * dsa_cache_write is the step before the path: it stores new tokens' MLA rows
  * and index keys in the paged caches the four steps read.
+ * dsa_lse_merge_project is the step after it: step 4 followed by the value
+ * projection W_UV, in one launch.
  *
  * Conventions shared by every entry point:
  *  - Every array pointer is DEVICE memory owned by the caller.  The library
@@ -113,6 +115,27 @@ int dsa_cache_write(const uint16_t* latent, const uint16_t* rope, const uint16_t
                     const int32_t* page_table, int32_t batch, int32_t num_pages, int32_t max_pages,
                     int32_t page_size, uint8_t* kv_cache, uint8_t* k_code, float* k_scale,
                     int32_t* status, hipStream_t stream);
+
+/*
+ * dsa_lse_merge_project -- the LSE merge of step 4 followed by the value
+ * projection of absorbed MLA (subject page, Future work: projecting V before
+ * the LSE merge; the projection is linear and the merge weights add to one,
+ * so merging first and projecting once gives the same values):
+ *   latent[r,h] = merge of part_o[r,h,:] by part_lse[r,h,:] as dsa_lse_merge,
+ *                 then rounded to bf16 (nearest even)
+ *   out[r,h,d]  = sum_k latent[r,h,k] * w_uv[h][d][k]   (fp32 accumulation,
+ *                 rounded to bf16)
+ *   out_lse[r,h] as dsa_lse_merge (may be NULL).
+ *   part_o [n_rows, n_heads, n_splits, d_latent] f32 (16-byte aligned),
+ *   part_lse [n_rows, n_heads, n_splits] f32, w_uv [n_heads, d_v, d_latent]
+ *   bf16 (16-byte aligned; each output dimension's weights one contiguous
+ *   row), out [n_rows, n_heads, d_v] bf16.
+ * A row no split saw gives out = 0 and lse = -inf.
+ * Supported: d_latent == 512, d_v == 128, 1 <= n_splits <= 64.
+ */
+int dsa_lse_merge_project(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
+                          int32_t n_splits, int32_t d_latent, const uint16_t* w_uv, int32_t d_v,
+                          uint16_t* out, float* out_lse, hipStream_t stream);
 
 /* DSA_ABI_VERSION of the built library; loaders refuse a mismatch. */
 int dsa_abi_version(void);

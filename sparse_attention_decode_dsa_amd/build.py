@@ -22,7 +22,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
 SOURCES = ["dsa_api.cpp", "quantize_q.hip", "index_scores.hip", "topk.hip",
-           "sparse_mla.hip", "lse_merge.hip", "cache_write.hip"]
+           "sparse_mla.hip", "lse_merge.hip", "cache_write.hip", "merge_project.hip"]
 
 
 def hipcc() -> str:

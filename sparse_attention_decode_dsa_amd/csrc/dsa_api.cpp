@@ -123,6 +123,23 @@ int dsa_cache_write(const uint16_t* latent, const uint16_t* rope, const uint16_t
     return launch_status(dsa::launch_cache_write(a, stream));
 }
 
+int dsa_lse_merge_project(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
+                          int32_t n_splits, int32_t d_latent, const uint16_t* w_uv, int32_t d_v,
+                          uint16_t* out, float* out_lse, hipStream_t stream) {
+    if (n_rows < 0 || n_rows > kMaxRows * 16 || n_heads < 1 || n_heads > 65535) return DSA_ERR_SHAPE;
+    if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
+    if (d_latent != 512 || d_v != 128) return DSA_ERR_UNSUPPORTED;
+    if (!part_o || !part_lse || !w_uv || !out) return DSA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(part_o) & 15) != 0 || (reinterpret_cast<uintptr_t>(w_uv) & 15) != 0)
+        return DSA_ERR_SHAPE;
+    if (n_rows == 0) return DSA_OK;
+    dsa::MergeProjectArgs a;
+    a.part_o = part_o; a.part_lse = part_lse; a.w_uv = w_uv;
+    a.n_rows = n_rows; a.n_heads = n_heads; a.n_splits = n_splits;
+    a.out = out; a.out_lse = out_lse;
+    return launch_status(dsa::launch_merge_project(a, stream));
+}
+
 size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits) {
     if (n_rows <= 0 || top_k <= 0 || n_splits <= 1) return 0;
     return 2 * topk_ws_keys(n_rows, top_k, n_splits);

@@ -71,6 +71,15 @@ struct CacheWriteArgs {
     int32_t* status;
 };
 
+struct MergeProjectArgs {
+    const float* part_o;       // [n_rows, n_heads, n_splits, 512]
+    const float* part_lse;     // [n_rows, n_heads, n_splits]
+    const uint16_t* w_uv;      // [n_heads, 128, 512] bf16
+    int32_t n_rows, n_heads, n_splits;
+    uint16_t* out;             // [n_rows, n_heads, 128] bf16
+    float* out_lse;            // [n_rows, n_heads] or null
+};
+
 struct MergeArgs {
     const float* part_o;
     const float* part_lse;
@@ -91,5 +100,6 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+hipError_t launch_merge_project(const MergeProjectArgs& a, hipStream_t stream);
 
 }  // namespace dsa

@@ -42,6 +42,7 @@ _SIGS = {
     "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "dsa_lse_merge": ([_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
+    "dsa_lse_merge_project": ([_p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_cache_write": ([_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
                          _p, _p, _p, _p, _p], ctypes.c_int),
 }
@@ -232,6 +233,24 @@ def lse_merge(part_o, part_lse, out=None, out_lse=None, stream=None):
                                _ptr(part_lse, torch.float32, "part_lse"), r, h, s, dv,
                                _ptr(out, _BF16, "out"), _ptr(out_lse, torch.float32, "out_lse"),
                                _stream(stream)), "dsa_lse_merge")
+    return out, out_lse
+
+
+def lse_merge_project(part_o, part_lse, w_uv, out=None, out_lse=None, stream=None):
+    """Merge split partials, then project with W_UV bf16 [H, 128, 512] ->
+    (out bf16 [R, H, 128], out_lse f32 [R, H])."""
+    r, h, s, dl = part_o.shape
+    dv = w_uv.shape[1]
+    dev = part_o.device
+    if out is None:
+        out = torch.empty((r, h, dv), dtype=torch.bfloat16, device=dev)
+    if out_lse is None:
+        out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
+    _check(lib().dsa_lse_merge_project(_ptr(part_o, torch.float32, "part_o"),
+                                       _ptr(part_lse, torch.float32, "part_lse"), r, h, s, dl,
+                                       _ptr(w_uv, _BF16, "w_uv"), dv, _ptr(out, _BF16, "out"),
+                                       _ptr(out_lse, torch.float32, "out_lse"), _stream(stream)),
+           "dsa_lse_merge_project")
     return out, out_lse
 
 

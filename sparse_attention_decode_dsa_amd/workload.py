@@ -373,3 +373,35 @@ def make_new_tokens(inp: Inputs, tok_req, tok_slot, seed: int = 0, device=None) 
     return NewTokens(latent=latent.to(torch.bfloat16).to(device), rope=rope.to(torch.bfloat16).to(device),
                      index_k=index_k.to(torch.bfloat16).to(device), tok_req=tok_req.to(device),
                      tok_slot=tok_slot.to(device), rope_cos=cos.to(device), rope_sin=sin.to(device))
+
+
+
+# --------------------------------------------------------------------------
+# Value projection (the step after the decode path)
+# --------------------------------------------------------------------------
+
+D_V = 128
+
+
+def make_w_uv(n_heads: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Seeded W_UV of one head shard: bf16 [H, 128, 512], entries
+    N(0, 1/512), so a unit-scale latent projects to unit-scale values."""
+    g = torch.Generator().manual_seed(seed)
+    w = torch.randn(n_heads, D_V, 512, generator=g) / math.sqrt(512.0)
+    return w.to(torch.bfloat16).to(device)
+
+
+def make_partials(n_rows: int, n_heads: int, n_splits: int, seed: int = 0, device="cpu"):
+    """Seeded split partials for the merge: part_o N(0, 1) f32 [R, H, S, 512],
+    part_lse N(0, 9) f32 [R, H, S], with an empty split (lse -inf, o 0) and,
+    for R >= 3, a row whose splits are all empty."""
+    g = torch.Generator().manual_seed(seed)
+    po = torch.randn(n_rows, n_heads, n_splits, 512, generator=g)
+    pl = torch.randn(n_rows, n_heads, n_splits, generator=g) * 3.0
+    if n_splits > 1 and n_rows > 0:
+        pl[0, 0, n_splits - 1] = -math.inf
+        po[0, 0, n_splits - 1] = 0.0
+    if n_rows >= 3:
+        pl[2, :, :] = -math.inf
+        po[2, :, :, :] = 0.0
+    return po.to(device), pl.to(device)

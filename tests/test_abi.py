@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert {"dsa_abi_version", "dsa_status_string", "dsa_quantize_q", "dsa_index_scores",
             "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_merge",
-            "dsa_cache_write"} <= set(names)
+            "dsa_cache_write", "dsa_lse_merge_project"} <= set(names)
     raw = ctypes.CDLL(dsa.lib_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -156,3 +156,24 @@ def test_cache_write_validation(L):
     assert _cw(L, n_tok=0) == OK                              # nothing to enqueue
     assert _cw(L, n_tok=0, latent=None, kv_cache=None) == OK  # empty batches may pass NULL arrays
     assert _cw(L, n_tok=0, rope_cos=P, rope_sin=P, max_pos=64) == OK
+
+
+def _mp(L, **kw):
+    a = dict(part_o=P, part_lse=P, n_rows=4, n_heads=32, n_splits=4, d_latent=512, w_uv=P, d_v=128,
+             out=P, out_lse=None, stream=None)
+    a.update(kw)
+    return L.dsa_lse_merge_project(*a.values())
+
+
+def test_lse_merge_project_validation(L):
+    assert _mp(L, d_v=64) == UNSUP
+    assert _mp(L, d_latent=576) == UNSUP
+    assert _mp(L, n_splits=0) == SHAPE
+    assert _mp(L, n_splits=65) == SHAPE
+    assert _mp(L, n_heads=0) == SHAPE
+    assert _mp(L, n_rows=-1) == SHAPE
+    assert _mp(L, w_uv=None) == NULL
+    assert _mp(L, out=None) == NULL
+    assert _mp(L, part_o=P + 4) == SHAPE        # 16-byte aligned partials
+    assert _mp(L, w_uv=P + 8) == SHAPE          # 16-byte aligned weights
+    assert _mp(L, n_rows=0) == OK
