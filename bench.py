@@ -22,7 +22,8 @@ real decode step do.  Then every kernel is replayed back to back from a graph
 of 20 launches (cycling through the input sets) between two HIP events on the
 stream it runs on, for per-kernel durations and the roofline of the dominant
 kernel.  The cache write (the step before the path: one new token per request
-into the paged caches) is timed the same way and reported on its own; it is
+into the paged caches) and the merge fused with the W_UV value projection (the
+step after it) are timed the same way and reported on their own; they are
 not part of the step.  The oracle (fp64, CPU) is timed on a bounded sample of
 the same workload as a reported baseline.
 """
@@ -65,6 +66,13 @@ def parse():
 
 
 CACHE_WRITE_BYTES_PER_TOKEN = 1024 + 128 + 256 + 256 + 12 + 580 + 132
+
+
+def merge_project_bytes(inp, n_splits: int) -> int:
+    """Per (row, head): S fp32 partials of 512 and S lse read, 128 bf16 and
+    one lse written; the bf16 weights [H, 128, 512] once."""
+    r, h = inp.n_rows, inp.mla_heads
+    return r * h * (n_splits * (512 * 4 + 4) + 128 * 2 + 4) + h * 128 * 512 * 2
 
 
 def algorithmic_bytes(inp) -> dict:
@@ -229,14 +237,21 @@ def main():
         # The step before the path, timed on its own: one new token per
         # request, written at its last slot (kv_len - 1) with the rope part
         # rotated.  It runs after the timed steps, so they never see it.
+        if st.attn_splits > 1:
+            # The step after the path, timed on its own: the merge fused with
+            # the W_UV value projection (it would replace lse_merge).
+            fns["lse_merge_project"] = lambda: dsa.lse_merge_project(
+                st.part_o, st.part_lse, w_uv[id(i)], out=proj_out[id(i)], out_lse=st.out_lse)
         nt = new_tokens[id(i)]
         fns["cache_write"] = lambda: dsa.cache_write(
             nt.latent, nt.rope, nt.index_k, nt.tok_req, nt.tok_slot, i.page_table, i.kv_cache,
             i.k_code, i.k_scale, rope_cos=nt.rope_cos, rope_sin=nt.rope_sin, status=st.status)
         return fns
 
-    new_tokens = {}
+    new_tokens, w_uv, proj_out = {}, {}, {}
     for k, x in enumerate(inps):
+        w_uv[id(x)] = W.make_w_uv(x.mla_heads, seed=base_seed + k, device=dev)
+        proj_out[id(x)] = torch.empty((x.n_rows, x.mla_heads, W.D_V), dtype=torch.bfloat16, device=dev)
         live = torch.nonzero(x.kv_lens > 0).flatten().cpu()
         new_tokens[id(x)] = W.make_new_tokens(x, live, (x.kv_lens[live] - 1).cpu(), seed=base_seed + k)
     n_new = int(new_tokens[id(inps[0])].tok_req.shape[0])
@@ -325,6 +340,13 @@ def main():
         # The step before the path (not in the step above): per new token it
         # reads 1024 + 128 + 256 B of bf16 rows, a 256 B cos/sin row, 12 B of
         # request, slot and page id, and writes 580 + 132 B of codes and scales.
+        "lse_merge_project": (None if "lse_merge_project" not in kern_us else {
+            "us_per_launch": round(kern_us["lse_merge_project"], 2),
+            "algorithmic_bytes": merge_project_bytes(inp, steps[0].attn_splits),
+            "achieved_GBps": round(merge_project_bytes(inp, steps[0].attn_splits)
+                                   / (kern_us["lse_merge_project"] * 1e3), 1),
+            "bound": "hbm",
+        }),
         "cache_write": {
             "tokens": n_new,
             "us_per_launch": round(kern_us["cache_write"], 2),

@@ -126,7 +126,7 @@ int dsa_cache_write(const uint16_t* latent, const uint16_t* rope, const uint16_t
 int dsa_lse_merge_project(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
                           int32_t n_splits, int32_t d_latent, const uint16_t* w_uv, int32_t d_v,
                           uint16_t* out, float* out_lse, hipStream_t stream) {
-    if (n_rows < 0 || n_rows > kMaxRows * 16 || n_heads < 1 || n_heads > 65535) return DSA_ERR_SHAPE;
+    if (n_rows < 0 || n_rows > kMaxRows * 8 || n_heads < 1 || n_heads > 65535) return DSA_ERR_SHAPE;
     if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
     if (d_latent != 512 || d_v != 128) return DSA_ERR_UNSUPPORTED;
     if (!part_o || !part_lse || !w_uv || !out) return DSA_ERR_NULL;
