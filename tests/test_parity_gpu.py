@@ -316,3 +316,35 @@ def test_bad_page_id_is_reported_not_read():
     torch.cuda.synchronize()
     with pytest.raises(dsa.DsaError, match="PAGE_OOB"):
         dsa.check_status(step.status)
+
+
+@pytest.mark.parametrize("cfg", ["c0", "c2"])
+def test_graph_replays_match_eager(cfg):
+    """The step captured in a HIP graph (as bench.py times it) and replayed
+    several times, with eager work and synchronisations in between, gives the
+    eager result bit for bit on every replay."""
+    inp = W.to(W.make(cfg), "cuda")
+    step = run_step(inp)
+    want = (step.scores.clone(), step.topk_idx.clone(), step.topk_count.clone(), step.out.clone(),
+            step.out_lse.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run()
+    for rep in range(4):
+        step.scores.fill_(0.5)          # eager work between replays
+        step.out.zero_()
+        step.topk_idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        dsa.check_status(step.status)
+        got = (step.scores, step.topk_idx, step.topk_count, step.out, step.out_lse)
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                               b.view(torch.uint8) if b.dtype != torch.int32 else b), f"replay {rep}"
