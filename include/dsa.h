@@ -29,9 +29,14 @@
  *    enqueued.  dsa_status_string() names every code.
  *  - Kernels check what only the device can see (page ids, row geometry,
  *    top-k indices).  A violation ORs a DSA_DEV_* bit into the caller's int32
- *    `status` word (device memory, not cleared by the library) and the
- *    offending row's output is written as empty (scores -inf, count 0,
- *    output 0, lse -inf) rather than read out of bounds.
+ *    `status` word (device memory, not cleared by the library) and nothing is
+ *    read out of bounds.  Each call writes a row whose geometry it finds
+ *    inconsistent as empty (dsa_index_scores: scores -inf; dsa_topk: count
+ *    0; dsa_sparse_mla_decode: output 0, lse -inf); a call checks what its
+ *    arguments show (only dsa_index_scores sees kv_lens).  A token on an
+ *    invalid page scores -inf; a selected entry outside its row's span or on
+ *    an invalid page is left out of the attention (the row attends the
+ *    others).  Once a bit is set, the step's results are not to be used.
  *  - Page pool layout: NP pages of P tokens.  Indexer keys: k_code uint8
  *    [NP, P, 128] (E4M3FN codes) and k_scale float32 [NP, P].  MLA rows:
  *    kv_cache uint8 [NP, P, 640], one 640-byte row per token: bytes

@@ -348,3 +348,113 @@ def test_graph_replays_match_eager(cfg):
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
                                b.view(torch.uint8) if b.dtype != torch.int32 else b), f"replay {rep}"
+
+
+# ------------------------------------------------------------------ error paths
+
+def test_nan_score_is_reported_and_selection_stays_valid():
+    rng = np.random.default_rng(21)
+    r, stride, k = 3, 4096, 100
+    s = torch.from_numpy(rng.standard_normal((r, stride)).astype(np.float32))
+    s[1, 17] = float("nan")
+    s[1, 3000] = float("nan")
+    vis = torch.tensor([4096, 3100, 50], dtype=torch.int32)
+    st = dsa.new_status()
+    idx, cnt, _ = dsa.topk(s.cuda(), vis.cuda(), k, 1, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & dsa.DEV_NAN
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for i in range(r):
+        c = min(k, int(vis[i]))
+        assert cnt[i] == c
+        sel = idx[i, :c]
+        assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < vis[i] and np.all(idx[i, c:] == -1)
+    # rows without a NaN select exactly as the oracle does
+    for i in (0, 2):
+        o_idx, o_cnt = O.topk_global(s[i].double().numpy(), int(vis[i]), k)
+        np.testing.assert_array_equal(idx[i, :o_cnt], o_idx[:o_cnt])
+
+
+def test_invalid_selected_entries_are_left_out_and_reported():
+    """Entries past the row's span or negative are skipped: the row attends the
+    remaining ones, which the oracle computes from the filtered list."""
+    inp = W.to(W.make("c0"), "cuda")
+    step = run_step(inp, 1, 4)
+    idx = step.topk_idx.clone()
+    cnt = step.topk_count.clone()
+    vis = inp.row_vis.cpu().numpy()
+    bad = idx.cpu().numpy().copy()
+    bad[0, 3] = vis[0] + 5          # past the span
+    bad[1, 0] = -2                  # negative
+    bad[1, 100] = vis[1]            # one past the end
+    st = dsa.new_status()
+    po, pl, _ = dsa.sparse_mla_decode(inp.q_mla, inp.kv_cache, inp.page_table, inp.row_req, inp.row_vis,
+                                      torch.from_numpy(bad).cuda(), cnt, 4, inp.sm_scale, status=st)
+    out, lse = dsa.lse_merge(po, pl)
+    torch.cuda.synchronize()
+    assert int(st.item()) & dsa.DEV_TOPK_OOB
+    sub = W.subset(inp, range(inp.n_rows))
+    n = W.as_numpy(sub)
+    c = cnt.cpu().numpy()
+    keep = [np.array([t for t in bad[i, :c[i]] if 0 <= t < vis[i]]) for i in range(inp.n_rows)]
+    k = bad.shape[1]
+    f_idx = np.full((inp.n_rows, k), -1, dtype=np.int64)
+    f_cnt = np.array([len(x) for x in keep])
+    for i, x in enumerate(keep):
+        f_idx[i, :len(x)] = x
+    kv_code = n["kv_code"]
+    r_po, r_pl = O.sparse_mla(n["q_mla"], kv_code, n["kv_scale"], n["page_table"], n["row_req"], f_idx, f_cnt,
+                              inp.sm_scale, 1, inp.page_size)
+    r_out, r_lse = O.lse_merge(r_po, r_pl)
+    check_out(bf16_to_f64(out), lse.cpu().double().numpy(), r_out, r_lse)
+
+
+def test_inconsistent_row_geometry_gives_an_empty_row():
+    """Each call writes a row whose geometry it finds inconsistent as empty,
+    reports it, and leaves the other rows as a clean call writes them."""
+    from dataclasses import replace
+    inp = W.to(W.make("c0"), "cuda")
+    good = run_step(inp, 1, 1)
+    args = (inp.q_idx, inp.head_w, inp.k_code, inp.k_scale, inp.page_table, inp.kv_lens)
+    # indexer: a span past the request's kv_len
+    vis = inp.row_vis.clone()
+    vis[0] = inp.kv_lens[int(inp.row_req[0])] + 1
+    st = dsa.new_status()
+    sc, _ = dsa.index_scores(*args, inp.row_req, vis, score_stride=good.score_stride, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & dsa.DEV_ROW_RANGE
+    assert torch.all(torch.isneginf(sc[0])) and torch.equal(sc[1], good.scores[1])
+    # top-k: a span past the score stride
+    vis = inp.row_vis.clone()
+    vis[0] = good.score_stride + 1
+    st = dsa.new_status()
+    idx, cnt, _ = dsa.topk(good.scores, vis, inp.top_k, 1, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & dsa.DEV_ROW_RANGE
+    assert int(cnt[0]) == 0 and torch.all(idx[0] == -1)
+    assert torch.equal(idx[1], good.topk_idx[1]) and int(cnt[1]) == int(good.topk_count[1])
+    # attention: a request out of range
+    rr = inp.row_req.clone()
+    rr[0] = inp.page_table.shape[0]
+    st = dsa.new_status()
+    out, lse, _ = dsa.sparse_mla_decode(inp.q_mla, inp.kv_cache, inp.page_table, rr, inp.row_vis,
+                                        good.topk_idx, good.topk_count, 1, inp.sm_scale, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & dsa.DEV_ROW_RANGE
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.equal(out[1], good.out[1])
+
+
+def test_rows_of_different_requests_in_one_group_are_reported():
+    cfg = W.Config("grp_err", batch=2, kv_lens=(300, 500), rows_per_req=2, page_size=64, mla_heads=16,
+                   group_rows=2, index_splits=1, attn_splits=1)
+    inp = W.to(W.make(cfg), "cuda")
+    rr = inp.row_req.clone()
+    rr[1] = 1 - rr[1]          # the first group now mixes the two requests
+    from dataclasses import replace
+    st = dsa.new_status()
+    sc, _ = dsa.index_scores(inp.q_idx, inp.head_w, inp.k_code, inp.k_scale, inp.page_table, inp.kv_lens,
+                             rr, inp.row_vis, group_rows=2, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & dsa.DEV_GROUP
+    assert torch.all(torch.isneginf(sc[1]))     # the offending row is empty
