@@ -43,6 +43,14 @@ constexpr int kQStride = 144;   // LDS bytes per query head row (128 + 16 pad: c
 
 constexpr int kMaxChunkPages = kMaxChunk / 16;  // pages of one chunk at the smallest page size
 
+// A read-only value at a wavefront-uniform address, through the scalar
+// cache: it does not queue behind the wavefront's vector loads, so reading
+// it never waits for them.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 __device__ __forceinline__ v8i load_q_operand(const uint8_t* head_row, int g) {
     const uint4 lo = *reinterpret_cast<const uint4*>(head_row + 16 * g);
     const uint4 hi = *reinterpret_cast<const uint4*>(head_row + 64 + 16 * g);
@@ -104,11 +112,9 @@ __device__ __forceinline__ float group_dot(const v8i (&qa)[4], const float (&wq)
 template <int G>
 constexpr int max_balanced_groups() { return G > 4 ? 512 : 1024; }
 
-template <int G>
+template <int G, int NT>
 struct IndexSmem {
-    int req[G];
-    int vis[G];   // spans checked against the launch's bounds (-1: reported invalid)
-    int vok[G];   // spans also checked against kv_len (0 for an invalid row)
+    int vok[G];   // the rows' checked spans (0 for an invalid row)
     int page[kMaxChunkPages];
     __attribute__((aligned(16))) uint8_t q[G * 64 * kQStride];   // fp8 query codes
     __attribute__((aligned(16))) float wq[G * 64];              // head weight * query scale
@@ -117,82 +123,111 @@ struct IndexSmem {
     // writes are mixed in).  Several rows write as they go.
     __attribute__((aligned(16))) float sc[G == 1 ? kMaxChunk : 4];
     int pre[max_balanced_groups<G>() + 1];   // balanced launch: first tile of each group
-    uint32_t scan[256 / kWave + 1];
+    uint32_t scan[NT / kWave + 1];
+    int next;     // balanced launch: the range's next unclaimed 64-token group
 };
 
-// Scores of rows [r0, r0 + G) at tokens [t0, t_end) (t0 a multiple of 64,
-// t_end - t0 <= kMaxChunk; -inf where a row's span ends) and -inf over
-// [fill_lo, fill_hi).  `report`: this call reports the rows' geometry errors
+// Scores of rows [r0, r0 + G) at tokens [t0, t_end) (t0 a multiple of 64;
+// -inf where a row's span ends) and -inf over [fill_lo, fill_hi), by a
+// workgroup of NT threads.  The range's pages must fit the LDS page array
+// (kMaxChunkPages).  `report`: this call reports the rows' geometry errors
 // (one call per row does).  `quantize`: the group's queries are not in LDS
-// yet (the previous call, if any, was for another group).
-template <int G>
-__device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G>& s, int r0, int t0, int t_end,
+// yet (the previous call, if any, was for another group).  kDynamic: the
+// wavefronts claim the range's 64-token groups from an LDS counter, so a
+// wavefront that the compute unit serves first also does more of them;
+// otherwise wavefront w takes groups w, w + NT/64, ...
+template <int G, int NT, bool kDynamic>
+__device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>& s, int r0, int t0, int t_end,
                                             int fill_lo, int fill_hi, bool report, bool quantize) {
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
-    __syncthreads();   // the previous range is done with the shared arrays
+    lds_sync();   // the previous range is done with the shared arrays
+    if (kDynamic && threadIdx.x == 0) s.next = 0;
 
-    // Row geometry, in two steps so that the block-table loads need not
-    // wait for kv_lens: the request and span are checked against the
-    // launch's bounds now; the span against the request's kv_len below,
-    // alongside the block-table loads.
-    if (threadIdx.x < G) {
-        const int r = r0 + threadIdx.x;
-        const int b = a.row_req[r];
-        int v = a.row_vis[r];
-        const int b0 = a.row_req[r0];
-        const bool ok = b >= 0 && b < a.batch && v >= 0 && v <= a.score_stride &&
-                        v <= a.max_pages * a.page_size;
-        if (!ok) {
-            if (report) flag(a.status, DSA_DEV_ROW_RANGE);
-            v = -1;   // reported; no second report below
-        } else if (b != b0) {
-            if (report) flag(a.status, DSA_DEV_GROUP);
-            v = -1;
-        }
-        s.req[threadIdx.x] = ok ? b : 0;
-        s.vis[threadIdx.x] = v;
-    }
-    // The group's bf16 queries and head weights, loaded now (before any key,
-    // so that no wait for them also waits for keys) and quantized once the
-    // first keys are in flight: four threads per head (head row
-    // p * 64 + threadIdx / 4 of pass p), elements [32 c, 32 c + 32) each,
-    // c = threadIdx % 4.
+    // The group's bf16 queries and head weights, loaded first (nothing waits
+    // for them until the first keys are about to go out) and quantized once
+    // those keys are in flight: four threads per head, elements [32 c,
+    // 32 c + 32) each, c = threadIdx % 4; 256 threads cover the 64 heads of
+    // one row, and the rows (passes) go round the NT / 256 sets of them.
+    constexpr int kSets = NT / 256;
+    constexpr int kPasses = (G + kSets - 1) / kSets;
     const int qc = threadIdx.x & 3;
-    const int qh = threadIdx.x >> 2;
-    uint4 qraw[G][4];
-    float hw[G];   // head weight of this thread's head in each pass (used by qc == 0)
+    const int qh = (threadIdx.x >> 2) & 63;
+    const int qset = threadIdx.x >> 8;
+    uint4 qraw[kPasses][4];
+    float hw[kPasses];   // head weight of this thread's head in each pass (used by qc == 0)
     if (quantize) {
 #pragma unroll
-        for (int p = 0; p < G; ++p) {
+        for (int j = 0; j < kPasses; ++j) {
+            const int p = min(qset + kSets * j, G - 1);   // a set past the last row repeats it
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                qraw[p][k] = reinterpret_cast<const uint4*>(a.q + ((size_t)r0 * 64 + p * 64 + qh) * 128 + 32 * qc)[k];
-            hw[p] = a.head_w[(size_t)r0 * 64 + p * 64 + qh];
+                qraw[j][k] = reinterpret_cast<const uint4*>(a.q + ((size_t)r0 * 64 + p * 64 + qh) * 128 + 32 * qc)[k];
+            hw[j] = a.head_w[(size_t)r0 * 64 + p * 64 + qh];
         }
     }
-    __syncthreads();
 
-    const int b = s.req[0];
+    // Row geometry, the same in every thread (uniform loads, no LDS round
+    // trip): the request and span against the launch's bounds, the group's
+    // rows against its first row's request, then the spans against that
+    // request's kv_len.  Thread j reports row j.  vis[j] = -1 marks a row
+    // already reported; vok[j] is the checked span (0 for an invalid row).
+    int req[G], vis[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {   // all loads first, then the checks
+        req[j] = load_uniform(a.row_req + r0 + j);
+        vis[j] = load_uniform(a.row_vis + r0 + j);
+    }
+    const int b0 = req[0];
+    const int b = b0 >= 0 && b0 < a.batch ? b0 : 0;
     int vmax = 0;   // longest span before the kv_len check (a superset)
 #pragma unroll
-    for (int j = 0; j < G; ++j) vmax = max(vmax, s.vis[j]);
+    for (int j = 0; j < G; ++j) {
+        const int bj = req[j];
+        int v = vis[j];
+        const bool ok = (bj >= 0) & (bj < a.batch) & (v >= 0) & (v <= a.score_stride) &
+                        (v <= a.max_pages * a.page_size);
+        if (!ok) {
+            if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_ROW_RANGE);
+            v = -1;
+        } else if (bj != b0) {
+            if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_GROUP);
+            v = -1;
+        }
+        vis[j] = v;
+        vmax = max(vmax, v);
+    }
+    const int kv = load_uniform(a.kv_lens + b);
+    const bool kv_ok = kv <= a.max_pages * a.page_size;
+    int vrow[G];   // checked spans
+    int vchk = 0;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        int v = vis[j];
+        if (v >= 0 && (v > kv || !kv_ok)) {
+            if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_ROW_RANGE);
+            v = 0;
+        }
+        vrow[j] = max(v, 0);
+        vchk = max(vchk, vrow[j]);
+        if ((int)threadIdx.x == j) s.vok[j] = vrow[j];   // for the row loop below
+    }
     const int pmask = a.page_size - 1;
     // Tokens [t0, t_comp) are computed in 64-token groups; the rest of the
     // range only needs -inf.
     const int t_comp = min(t_end, t0 + ((max(vmax - t0, 0) + 63) & ~63));
 
     // Block table of the range, once: page ids of the pages [t0, t_comp)
-    // touches (-1 for invalid ones), and the spans against kv_len.  An
-    // invalid page is reported only if it lies inside a checked span.
+    // touches (-1 for invalid ones).  An invalid page is reported only if it
+    // lies inside a checked span.
     const int p0 = t0 >> a.log2_page;
-    int bad_from = INT_MAX;   // first token of an invalid page this thread saw
     {
+        int bad_from = INT_MAX;   // first token of an invalid page this thread saw
         const int np = t_comp > t0 ? ((t_comp - 1) >> a.log2_page) - p0 + 1 : 0;
         const int* pt = a.page_table + (size_t)b * a.max_pages;
-        for (int i = threadIdx.x; i < np; i += 256) {
+        for (int i = threadIdx.x; i < np; i += NT) {
             int page = -1;
             if (((p0 + i) << a.log2_page) < vmax) {
                 page = pt[p0 + i];
@@ -203,25 +238,9 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G>& s,
             }
             s.page[i] = page;
         }
-    }
-    if (threadIdx.x < G) {
-        int v = s.vis[threadIdx.x];
-        if (v >= 0) {
-            const int kv = a.kv_lens[s.req[threadIdx.x]];
-            if (v > kv || kv > a.max_pages * a.page_size) {
-                if (report) flag(a.status, DSA_DEV_ROW_RANGE);
-                v = 0;
-            }
-        }
-        s.vok[threadIdx.x] = max(v, 0);
-    }
-    __syncthreads();
-    {
-        int vchk = 0;
-#pragma unroll
-        for (int j = 0; j < G; ++j) vchk = max(vchk, s.vok[j]);
         if (bad_from < vchk) flag(a.status, DSA_DEV_PAGE_OOB);
     }
+    lds_sync();   // page ids and the claim counter are in place
 
     v8i qa[4];
     float wq[4][4];
@@ -278,19 +297,31 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G>& s,
         }
     };
 
+    // The wavefront's first 64-token group, and the one after tg.
+    constexpr int kStride = NT;   // static order: the workgroup's wavefronts cover NT tokens a round
+    auto claim = [&]() -> int {
+        int i = 0;
+        if (lane == 0) i = atomicAdd(&s.next, 1);
+        return t0 + 64 * __builtin_amdgcn_readfirstlane(i);
+    };
+    auto after = [&](int tg) -> int {
+        if constexpr (kDynamic) return claim();
+        else return tg + kStride;
+    };
+
     KeyGroup ka, kb;
-    int tg = t0 + wv * 64;
+    int tg = kDynamic ? claim() : t0 + wv * 64;
     if (quantize) {
         // The query loads are long done; consuming them here, before any key
         // load goes out, keeps the compiler from waiting for keys as well
         // when the quantization below first reads them.
 #pragma unroll
-        for (int p = 0; p < G; ++p) {
+        for (int j = 0; j < kPasses; ++j) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                pin(qraw[p][k].x); pin(qraw[p][k].y); pin(qraw[p][k].z); pin(qraw[p][k].w);
+                pin(qraw[j][k].x); pin(qraw[j][k].y); pin(qraw[j][k].z); pin(qraw[j][k].w);
             }
-            pin(hw[p]);
+            pin(hw[j]);
         }
     }
     if (tg < t_comp) load_group(tg, ka);
@@ -300,32 +331,35 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G>& s,
         // while the first keys load: the head's amax over its four threads,
         // one power-of-two scale, fp8 codes.
 #pragma unroll
-        for (int p = 0; p < G; ++p) {
+        for (int j = 0; j < kPasses; ++j) {
+            const int p = qset + kSets * j;
             float v[32];
             float amax = 0.0f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 float x[8];
-                bf16x8_to_f32(qraw[p][k], x);
+                bf16x8_to_f32(qraw[j][k], x);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     v[8 * k + u] = x[u];
                     amax = fmaxf(amax, fabsf(x[u]));
                 }
             }
-            amax = fmaxf(amax, __shfl_xor(amax, 1));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            amax = fmaxf(amax, dpp<0xB1>(amax));   // the head's four threads are one quad
+            amax = fmaxf(amax, dpp<0x4E>(amax));
             const int e = idx_q_exponent(amax);
             const IdxQFactors f = idx_q_factors(e);
             uint32_t w[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 w[k] = idx_q_code2(v[4 * k], v[4 * k + 1], f) | (idx_q_code2(v[4 * k + 2], v[4 * k + 3], f) << 16);
-            const int hr = p * 64 + qh;
-            uint4* dst = reinterpret_cast<uint4*>(s.q + hr * kQStride + 32 * qc);
-            dst[0] = uint4{w[0], w[1], w[2], w[3]};
-            dst[1] = uint4{w[4], w[5], w[6], w[7]};
-            if (qc == 0) s.wq[hr] = hw[p] * ldexpf(1.0f, e);
+            if (p < G) {
+                const int hr = p * 64 + qh;
+                uint4* dst = reinterpret_cast<uint4*>(s.q + hr * kQStride + 32 * qc);
+                dst[0] = uint4{w[0], w[1], w[2], w[3]};
+                dst[1] = uint4{w[4], w[5], w[6], w[7]};
+                if (qc == 0) s.wq[hr] = hw[j] * ldexpf(1.0f, e);
+            }
         }
         lds_sync();
     }
@@ -345,70 +379,85 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G>& s,
     // branching around the loads.
     if (tg < t_comp) {
         while (true) {
-            const bool m1 = tg + 256 < t_comp;
-            load_group(m1 ? tg + 256 : tg, kb);
+            const int t1 = after(tg);
+            const bool m1 = t1 < t_comp;
+            load_group(m1 ? t1 : tg, kb);
             process(ka, tg);
-            tg += 256;
             if (!m1) break;
-            const bool m2 = tg + 256 < t_comp;
-            load_group(m2 ? tg + 256 : tg, ka);
+            tg = t1;
+            const int t2 = after(tg);
+            const bool m2 = t2 < t_comp;
+            load_group(m2 ? t2 : tg, ka);
             process(kb, tg);
-            tg += 256;
             if (!m2) break;
+            tg = t2;
         }
     }
 
     if constexpr (G == 1) {
         // -inf past the span, then the whole range out: 16-byte stores where
         // the row's range is 16-byte aligned, else one float per lane.
-        for (int t = t_comp + threadIdx.x; t < t_end; t += 256) s.sc[t - t0] = -INFINITY;
+        for (int t = t_comp + threadIdx.x; t < t_end; t += NT) s.sc[t - t0] = -INFINITY;
         __syncthreads();
         float* dst = a.scores + (size_t)r0 * a.score_stride + t0;
         const int cnt = t_end - t0;
         if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-            for (int i = 4 * threadIdx.x; i + 3 < cnt; i += 1024)
+            for (int i = 4 * threadIdx.x; i + 3 < cnt; i += 4 * NT)
                 *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&s.sc[i]);
-            for (int i = (cnt & ~3) + threadIdx.x; i < cnt; i += 256) dst[i] = s.sc[i];
+            for (int i = (cnt & ~3) + threadIdx.x; i < cnt; i += NT) dst[i] = s.sc[i];
         } else {
-            for (int i = threadIdx.x; i < cnt; i += 256) dst[i] = s.sc[i];
+            for (int i = threadIdx.x; i < cnt; i += NT) dst[i] = s.sc[i];
         }
     } else {
         // -inf for the part of the range past every row's span.
         for (int rr = 0; rr < G; ++rr) {
             float* srow = a.scores + (size_t)(r0 + rr) * a.score_stride;
-            for (int t = t_comp + threadIdx.x; t < t_end; t += 256) srow[t] = -INFINITY;
+            for (int t = t_comp + threadIdx.x; t < t_end; t += NT) srow[t] = -INFINITY;
         }
     }
     // This range's share of the rows' tail past their tiles.
     for (int rr = 0; rr < G; ++rr) {
         float* srow = a.scores + (size_t)(r0 + rr) * a.score_stride;
-        for (int t = fill_lo + threadIdx.x; t < fill_hi; t += 256) srow[t] = -INFINITY;
+        for (int t = fill_lo + threadIdx.x; t < fill_hi; t += NT) srow[t] = -INFINITY;
     }
 }
 
 // Two launch shapes:
-//   chunked:  grid (chunks, groups); a workgroup scores one chunk of a.chunk
-//             tokens of one group of G rows;
-//   balanced: a 1-D grid; every workgroup counts the live 64-token tiles of
-//             every group (max(1, ceil(vmax / 64)), vmax the group's longest
-//             row, so that a dead group still owns one tile), and takes an
-//             equal share of the concatenated tiles, group by group, in
-//             ranges of at most kMaxChunk tokens.  A group's tail past its
-//             tiles, [64 T, score_stride), is cut in proportion to the tiles,
-//             so every position of every row is written exactly once.  Rows
-//             of very different lengths then cost each workgroup the same.
+//   chunked:  grid (chunks, groups) of 256-thread workgroups; a workgroup
+//             scores one chunk of a.chunk tokens of one group of G rows;
+//   balanced: one 512-thread workgroup per compute unit; every workgroup
+//             counts the live 64-token tiles of every group (max(1,
+//             ceil(vmax / 64)), vmax the group's longest row, so that a dead
+//             group still owns one tile), and takes an equal share of the
+//             concatenated tiles, group by group, in ranges whose pages fit
+//             the LDS page array.  A group's tail past its tiles, [64 T,
+//             score_stride), is cut in proportion to the tiles, so every
+//             position of every row is written exactly once.  Rows of very
+//             different lengths then cost each workgroup the same.
 // Groups of several rows (MTP verify, prefill) use the balanced shape; one
 // row per group (decode) the chunked one, whose workgroups start sooner
 // (measured faster for decode batches, ragged ones included).
+//
+// The balanced shape is compute-bound, and a compute unit serves its oldest
+// wavefronts first.  Two workgroups per unit with fixed shares measured a
+// long tail in which the younger one ran alone, one wavefront per SIMD; one
+// workgroup whose wavefronts claim tiles as they go ends them together, and
+// quantizes each group's queries once per unit instead of twice.
 template <int G>
 __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
-    __shared__ IndexSmem<G> s;
-    if (!a.balanced) {
-        const int t0 = blockIdx.x * a.chunk;
-        score_range<G>(a, s, blockIdx.y * G, t0, min(t0 + a.chunk, a.score_stride), 0, 0, blockIdx.x == 0, true);
-        return;
-    }
-    constexpr int kPer = max_balanced_groups<G>() / 256;   // groups per thread in the scan
+    __shared__ IndexSmem<G, 256> s;
+    const int t0 = blockIdx.x * a.chunk;
+    score_range<G, 256, false>(a, s, blockIdx.y * G, t0, min(t0 + a.chunk, a.score_stride), 0, 0, blockIdx.x == 0,
+                               true);
+}
+
+constexpr int kBalancedThreads = 512;
+
+template <int G>
+__global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel(IndexArgs a) {
+    constexpr int NT = kBalancedThreads;
+    __shared__ IndexSmem<G, NT> s;
+    constexpr int kPer = (max_balanced_groups<G>() + NT - 1) / NT;   // groups per thread in the scan
     const int ng = a.n_rows / G;
     const int cap = min(a.score_stride, a.max_pages * a.page_size);
     int cnt[kPer];
@@ -424,7 +473,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
         sum += cnt[k];
     }
     uint32_t total;
-    int ex = (int)block_exclusive_scan<256>((uint32_t)sum, s.scan, &total);
+    int ex = (int)block_exclusive_scan<NT>((uint32_t)sum, s.scan, &total);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int gi = kPer * (int)threadIdx.x + k;
@@ -444,40 +493,44 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
         if (s.pre[mid] <= A) lo = mid;
         else hi = mid - 1;
     }
-    constexpr int kMaxTiles = kMaxChunk / 64;
+    // Tiles per range: its pages (one more where it starts inside a page)
+    // must fit the page array.
+    const int max_tiles = (int)min<int64_t>(
+        INT_MAX / 64, max<int64_t>(kMaxChunk / 64, ((int64_t)(kMaxChunkPages - 1) << a.log2_page) / 64));
     int last = -1;
     for (int gi = lo; gi < ng && s.pre[gi] < B; ++gi) {
         const int base = s.pre[gi];
         const int tiles = s.pre[gi + 1] - base;
         const int j0 = max(A, base) - base, j1 = min(B, base + tiles) - base;
         const int tail = max(0, a.score_stride - 64 * tiles);
-        for (int js = j0; js < j1; js += kMaxTiles) {
-            const int je = min(j1, js + kMaxTiles);
+        for (int js = j0; js < j1; js += max_tiles) {
+            const int je = min(j1, js + max_tiles);
             const int f_lo = 64 * tiles + (int)((int64_t)tail * js / tiles);
             const int f_hi = 64 * tiles + (int)((int64_t)tail * je / tiles);
-            score_range<G>(a, s, gi * G, 64 * js, min(64 * je, a.score_stride), f_lo, f_hi, js == 0, gi != last);
+            score_range<G, NT, true>(a, s, gi * G, 64 * js, min(64 * je, a.score_stride), f_lo, f_hi, js == 0,
+                                     gi != last);
             last = gi;
         }
     }
 }
 
-// Target grid size: two workgroups per compute unit (256 units).  Registers
+// Chunked grid size: two workgroups per compute unit (256 units).  Registers
 // would allow three at G = 1, but two larger chunks each measure faster.
 constexpr int kResidentWgs = 512;
+constexpr int kComputeUnits = 256;
 
 template <int G>
 hipError_t launch_g(IndexArgs a, hipStream_t stream) {
     const int groups = a.n_rows / G;
-    if (G > 1 && groups <= max_balanced_groups<G>()) {
-        a.balanced = 1;
-        a.chunk = 0;
-        index_scores_kernel<G><<<kResidentWgs, 256, 0, stream>>>(a);
-        return hipGetLastError();
+    if constexpr (G > 1) {
+        if (groups <= max_balanced_groups<G>()) {
+            index_scores_balanced_kernel<G><<<kComputeUnits, kBalancedThreads, 0, stream>>>(a);
+            return hipGetLastError();
+        }
     }
     const int per_group = max(1, kResidentWgs / groups);
     int chunk = (a.score_stride + per_group - 1) / per_group;
     chunk = min(kMaxChunk, max(kMinChunk, (chunk + 255) & ~255));
-    a.balanced = 0;
     a.chunk = chunk;
     dim3 grid((a.score_stride + chunk - 1) / chunk, groups);
     index_scores_kernel<G><<<grid, 256, 0, stream>>>(a);

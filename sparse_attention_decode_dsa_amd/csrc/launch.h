@@ -22,7 +22,6 @@ struct IndexArgs {
     int32_t score_stride;
     int32_t* status;
     int32_t chunk;     // chunked launch: tokens per workgroup (set by the launcher)
-    int32_t balanced;  // 1: balanced launch (set by the launcher)
 };
 
 struct TopkArgs {
