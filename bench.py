@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 
 METRIC = "DSA decode steps/s (index+top-k+sparse MLA) at B=64 L=32k; % peak HBM BW"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, vendor figure (no sparsity)
 
 
 def parse():
@@ -78,18 +79,22 @@ def merge_project_bytes(inp, n_splits: int) -> int:
 def algorithmic_bytes(inp) -> dict:
     """Bytes the method must move per step, from the actual geometry.
 
-    Per row with V visible slots: 132 B per slot of index key + scale,
-    580 B per selected MLA row + scale, 4 B per page-table entry, the bf16
-    indexer query (64 x 128 x 2) and head weights (64 x 4), the bf16 MLA query
-    (H x 576 x 2), the bf16 output (H x 512 x 2) and its lse (H x 4).
+    Per row with V visible slots: 132 B per slot of index key + scale and
+    4 B per page-table entry, the bf16 indexer query (64 x 128 x 2) and head
+    weights (64 x 4), 580 B per selected MLA row + scale, the bf16 MLA query
+    (H x 576 x 2), the bf16 output (H x 512 x 2) and its lse (H x 4).  Rows
+    scored together (a group of query rows of one request: MTP verify,
+    prefill) share their keys, which count once, at the group's longest span.
     Intermediates (scores, top-k lists, split partials) are not counted.
+    The indexer kernel's share is the first part; its fp8 contraction does
+    2 x 64 x 128 flops per visible slot of a row.
     """
     vis = inp.row_vis.cpu().tolist()
-    p, k, h = inp.page_size, inp.top_k, inp.mla_heads
-    idx = sum(132 * v + 4 * math.ceil(v / p) + 64 * 128 * 2 + 64 * 4 for v in vis)
+    p, k, h, g = inp.page_size, inp.top_k, inp.mla_heads, inp.cfg.group_rows
+    keys = sum(132 * m + 4 * math.ceil(m / p) for m in (max(vis[i:i + g]) for i in range(0, len(vis), g)))
+    idx = keys + len(vis) * (64 * 128 * 2 + 64 * 4)
     mla = sum(580 * min(v, k) + h * 576 * 2 + h * 512 * 2 + h * 4 for v in vis)
-    return {"step": idx + mla, "index_kernel": sum(132 * v + 4 * math.ceil(v / p) + 64 * 128 + 64 * 8
-                                                     for v in vis)}
+    return {"step": idx + mla, "index_kernel": idx, "index_flops": sum(2 * 64 * 128 * v for v in vis)}
 
 
 def cpu_baseline(inps, seconds: float) -> dict:
@@ -294,6 +299,10 @@ def main():
     ab = algorithmic_bytes(inp)
     idx_us = kern_us["index_scores"]
     achieved = ab["index_kernel"] / (idx_us * 1e-6) / 1e9
+    # Several query rows per key (MTP verify, prefill): the indexer is a dense
+    # fp8 contraction, and its roofline is the MFMA peak.
+    multi = step.group_rows > 1
+    tflops = ab["index_flops"] / (idx_us * 1e-6) / 1e12
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "index_scores_c1_l32k_traffic.json")
     if os.path.exists(tfile) and args.config == "c1_l32k":
@@ -325,7 +334,16 @@ def main():
             "launch": "eager" if round_graph is None else "hipgraph",
             "input_sets": n_sets,
         },
-        "roofline": {
+        "roofline": ({
+            "kernel": "index_scores",
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / FP8_PEAK_TFLOPS,
+            "traffic": None,
+            "hbm_GBps": achieved,
+        } if multi else {
             "kernel": "index_scores",
             "bound": "hbm",
             "achieved": achieved,
@@ -333,7 +351,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-        },
+        }),
         "step_algorithmic_bytes": ab["step"],
         "step_hbm_frac": ab["step"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "kernels_us": {n: round(v, 2) for n, v in kern_us.items()},
