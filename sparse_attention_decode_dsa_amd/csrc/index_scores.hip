@@ -458,6 +458,12 @@ __global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel
     constexpr int NT = kBalancedThreads;
     __shared__ IndexSmem<G, NT> s;
     constexpr int kPer = (max_balanced_groups<G>() + NT - 1) / NT;   // groups per thread in the scan
+    // A workgroup pays a prologue (query loads and quantization, block
+    // table) for every group it works on, about as long as kPrologue tiles
+    // of that group.  Each group therefore starts with kPrologue virtual
+    // tiles in the concatenation that the shares cut: a share that runs
+    // into a second group gets that many fewer real tiles.
+    constexpr int kPrologue = 2 * G + 2;
     const int ng = a.n_rows / G;
     const int cap = min(a.score_stride, a.max_pages * a.page_size);
     int cnt[kPer];
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel
         if (gi < ng) {
             for (int j = 0; j < G; ++j) vm = max(vm, min(max(a.row_vis[gi * G + j], 0), cap));
         }
-        cnt[k] = gi < ng ? max(1, (vm + 63) >> 6) : 0;
+        cnt[k] = gi < ng ? kPrologue + max(1, (vm + 63) >> 6) : 0;
         sum += cnt[k];
     }
     uint32_t total;
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel
     const int A = (int)((int64_t)blockIdx.x * T / gridDim.x);
     const int B = (int)((int64_t)(blockIdx.x + 1) * T / gridDim.x);
     if (A >= B) return;
-    // First group: the last one starting at or before tile A.
+    // First group: the last one starting at or before position A.
     int lo = 0, hi = ng - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -499,9 +505,9 @@ __global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel
         INT_MAX / 64, max<int64_t>(kMaxChunk / 64, ((int64_t)(kMaxChunkPages - 1) << a.log2_page) / 64));
     int last = -1;
     for (int gi = lo; gi < ng && s.pre[gi] < B; ++gi) {
-        const int base = s.pre[gi];
+        const int base = s.pre[gi] + kPrologue;   // position of the group's first real tile
         const int tiles = s.pre[gi + 1] - base;
-        const int j0 = max(A, base) - base, j1 = min(B, base + tiles) - base;
+        const int j0 = max(A, base) - base, j1 = min(B, base + tiles) - base;   // j1 <= j0: none here
         const int tail = max(0, a.score_stride - 64 * tiles);
         for (int js = j0; js < j1; js += max_tiles) {
             const int je = min(j1, js + max_tiles);

@@ -21,20 +21,21 @@ __device__ __forceinline__ int idx_q_exponent(float amax) {
     return e;
 }
 
-// q * 2^-e is taken in two exact power-of-two steps, (q * f1) * f2, so that
-// no factor leaves the fp32 range.
+// q * 2^-e in one exact step (v_ldexp_f32: a single rounding, and only where
+// the result is below the fp32 normal range, far under the smallest fp8
+// subnormal, so every such value still codes to a signed zero).
 struct IdxQFactors {
-    float f1, f2;
+    int neg_e;
 };
 __device__ __forceinline__ IdxQFactors idx_q_factors(int e) {
-    const int h1 = (-e) / 2, h2 = -e - h1;
-    return IdxQFactors{ldexpf(1.0f, h1), ldexpf(1.0f, h2)};
+    return IdxQFactors{-e};
 }
 
 // Two codes (round to nearest even into E4M3FN; |q * 2^-e| <= 448 by
 // construction) in the low 16 bits.
 __device__ __forceinline__ uint32_t idx_q_code2(float x0, float x1, IdxQFactors f) {
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((x0 * f.f1) * f.f2, (x1 * f.f1) * f.f2, 0, false) & 0xFFFFu;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x0, f.neg_e),
+                                                     __builtin_amdgcn_ldexpf(x1, f.neg_e), 0, false) & 0xFFFFu;
 }
 
 // bf16 bit patterns of a 16-byte chunk -> 8 floats.
