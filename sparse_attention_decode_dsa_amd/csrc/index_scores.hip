@@ -16,13 +16,16 @@
 // two 16-byte loads of a wavefront then reads one contiguous 64-byte half of
 // 16 consecutive 128-byte key rows.
 //
-// Work split: a workgroup (4 wavefronts) owns a chunk of a.chunk tokens of a
-// group of G rows of one request; wavefronts take 64-token groups in turn.
-// The chunk (a multiple of 256, at most kMaxChunk) is picked at launch so that
-// the grid is about two workgroups per compute unit, all resident at once: a
+// Work split, decode (G = 1): a workgroup (4 wavefronts) owns a chunk of
+// a.chunk tokens of one row; wavefronts take 64-token groups in turn.  The
+// chunk (a multiple of 256, at most kMaxChunk) is picked at launch so that the
+// grid is about two workgroups per compute unit, all resident at once: a
 // second, partial round of workgroups would run with most of the chip idle.
 // With G > 1 (MTP verify, prefill) the keys of a 64-token group are loaded
-// once and reused for every row of the group, whose queries sit in LDS.
+// once and reused for every row of the group, whose queries sit in LDS; one
+// 8-wavefront workgroup per compute unit takes an equal share of all groups'
+// tiles, and its wavefronts claim the 64-token groups of that share as they go
+// (the launch shapes are described above the kernels).
 //
 // Latency hiding: the chunk's page ids are read once into LDS, so key
 // addresses never wait on a block-table load; each wavefront issues the
