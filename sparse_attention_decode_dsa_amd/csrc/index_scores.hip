@@ -23,7 +23,7 @@
 // second, partial round of workgroups would run with most of the chip idle.
 // With G > 1 (MTP verify, prefill) the keys of a 64-token group are loaded
 // once and reused for every row of the group, whose queries sit in LDS; one
-// 8-wavefront workgroup per compute unit takes an equal share of all groups'
+// 12-wavefront workgroup per compute unit takes an equal share of all groups'
 // tiles, and its wavefronts claim the 64-token groups of that share as they go
 // (the launch shapes are described above the kernels).
 //
@@ -135,13 +135,16 @@ struct IndexSmem {
 // workgroup of NT threads.  The range's pages must fit the LDS page array
 // (kMaxChunkPages).  `report`: this call reports the rows' geometry errors
 // (one call per row does).  `quantize`: the group's queries are not in LDS
-// yet (the previous call, if any, was for another group).  kDynamic: the
-// wavefronts claim the range's 64-token groups from an LDS counter, so a
-// wavefront that the compute unit serves first also does more of them;
-// otherwise wavefront w takes groups w, w + NT/64, ...
+// yet (the previous call, if any, was for another group).  kDynamic (the
+// balanced launch): the wavefronts claim the range's 64-token groups from an
+// LDS counter, so a wavefront that the compute unit serves first also does
+// more of them, and the rows' geometry comes checked and reported from the
+// caller (geo_vis: the rows' checked spans, geo_b: their request); otherwise
+// wavefront w takes groups w, w + NT/64, ... and the geometry is read here.
 template <int G, int NT, bool kDynamic>
 __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>& s, int r0, int t0, int t_end,
-                                            int fill_lo, int fill_hi, bool report, bool quantize) {
+                                            int fill_lo, int fill_hi, bool report, bool quantize,
+                                            const int* geo_vis = nullptr, int geo_b = 0) {
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int n = lane & 15;
@@ -172,51 +175,67 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
         }
     }
 
-    // Row geometry, the same in every thread (uniform loads, no LDS round
-    // trip): the request and span against the launch's bounds, the group's
-    // rows against its first row's request, then the spans against that
-    // request's kv_len.  Thread j reports row j.  vis[j] = -1 marks a row
-    // already reported; vok[j] is the checked span (0 for an invalid row).
-    int req[G], vis[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {   // all loads first, then the checks
-        req[j] = load_uniform(a.row_req + r0 + j);
-        vis[j] = load_uniform(a.row_vis + r0 + j);
-    }
-    const int b0 = req[0];
-    const int b = b0 >= 0 && b0 < a.batch ? b0 : 0;
-    int vmax = 0;   // longest span before the kv_len check (a superset)
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const int bj = req[j];
-        int v = vis[j];
-        const bool ok = (bj >= 0) & (bj < a.batch) & (v >= 0) & (v <= a.score_stride) &
-                        (v <= a.max_pages * a.page_size);
-        if (!ok) {
-            if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_ROW_RANGE);
-            v = -1;
-        } else if (bj != b0) {
-            if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_GROUP);
-            v = -1;
-        }
-        vis[j] = v;
-        vmax = max(vmax, v);
-    }
-    const int kv = load_uniform(a.kv_lens + b);
-    const bool kv_ok = kv <= a.max_pages * a.page_size;
+    int b, vmax, vchk;
     int vrow[G];   // checked spans
-    int vchk = 0;
+    if constexpr (kDynamic) {
+        b = geo_b;
+        vmax = 0;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        int v = vis[j];
-        if (v >= 0 && (v > kv || !kv_ok)) {
-            if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_ROW_RANGE);
-            v = 0;
+        for (int j = 0; j < G; ++j) {
+            vrow[j] = geo_vis[j];
+            vmax = max(vmax, vrow[j]);
         }
-        vrow[j] = max(v, 0);
-        vchk = max(vchk, vrow[j]);
-        if ((int)threadIdx.x == j) s.vok[j] = vrow[j];   // for the row loop below
+        vchk = vmax;
+    } else {
+        // Row geometry, the same in every thread (uniform loads, no LDS
+        // round trip): the request and span against the launch's bounds, the
+        // group's rows against its first row's request, then the spans
+        // against that request's kv_len.  Thread j reports row j.  vis[j] =
+        // -1 marks a row already reported.  vmax, the longest span before
+        // the kv_len check, lets the block-table loads go out without
+        // waiting for kv_len.
+        int req[G], vis[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {   // all loads first, then the checks
+            req[j] = load_uniform(a.row_req + r0 + j);
+            vis[j] = load_uniform(a.row_vis + r0 + j);
+        }
+        const int b0 = req[0];
+        b = b0 >= 0 && b0 < a.batch ? b0 : 0;
+        vmax = 0;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int bj = req[j];
+            int v = vis[j];
+            const bool ok = (bj >= 0) & (bj < a.batch) & (v >= 0) & (v <= a.score_stride) &
+                            (v <= a.max_pages * a.page_size);
+            if (!ok) {
+                if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_ROW_RANGE);
+                v = -1;
+            } else if (bj != b0) {
+                if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_GROUP);
+                v = -1;
+            }
+            vis[j] = v;
+            vmax = max(vmax, v);
+        }
+        const int kv = load_uniform(a.kv_lens + b);
+        const bool kv_ok = kv <= a.max_pages * a.page_size;
+        vchk = 0;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            int v = vis[j];
+            if (v >= 0 && (v > kv || !kv_ok)) {
+                if (report && (int)threadIdx.x == j) flag(a.status, DSA_DEV_ROW_RANGE);
+                v = 0;
+            }
+            vrow[j] = max(v, 0);
+            vchk = max(vchk, vrow[j]);
+        }
     }
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        if ((int)threadIdx.x == j) s.vok[j] = vrow[j];   // for the row loop below
     const int pmask = a.page_size - 1;
     // Tokens [t0, t_comp) are computed in 64-token groups; the rest of the
     // range only needs -inf.
@@ -428,7 +447,8 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
 // Two launch shapes:
 //   chunked:  grid (chunks, groups) of 256-thread workgroups; a workgroup
 //             scores one chunk of a.chunk tokens of one group of G rows;
-//   balanced: one 512-thread workgroup per compute unit; every workgroup
+//   balanced: one 768-thread workgroup per compute unit (three wavefronts
+//             per SIMD, as many as 168 VGPRs allow); every workgroup
 //             counts the live 64-token tiles of every group (max(1,
 //             ceil(vmax / 64)), vmax the group's longest row, so that a dead
 //             group still owns one tile), and takes an equal share of the
@@ -454,7 +474,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
                                true);
 }
 
-constexpr int kBalancedThreads = 512;
+constexpr int kBalancedThreads = 768;
 
 template <int G>
 __global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel(IndexArgs a) {
@@ -469,15 +489,35 @@ __global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel
     constexpr int kPrologue = 2 * G + 2;
     const int ng = a.n_rows / G;
     const int cap = min(a.score_stride, a.max_pages * a.page_size);
+    // The groups' row geometry, read and checked once here for the whole
+    // launch (the first workgroup reports): each row's request and span
+    // against the launch's bounds, its request against its group's first
+    // row's, its span against that request's kv_len.  rvis holds the checked
+    // spans (0 for an invalid row), greq each group's request.  The kv_len
+    // loads complete while the tile counts are scanned.
+    __shared__ int rvis[max_balanced_groups<G>() * G];
+    __shared__ int greq[max_balanced_groups<G>()];
+    const bool report = blockIdx.x == 0;
+    int req[kPer][G], vis[kPer][G], kv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int gi = kPer * (int)threadIdx.x + k;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            req[k][j] = gi < ng ? a.row_req[gi * G + j] : 0;
+            vis[k][j] = gi < ng ? a.row_vis[gi * G + j] : 0;
+        }
+    }
     int cnt[kPer];
     int sum = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int gi = kPer * (int)threadIdx.x + k;
+        const int b0 = req[k][0];
+        kv[k] = gi < ng && b0 >= 0 && b0 < a.batch ? a.kv_lens[b0] : 0;
         int vm = 0;
-        if (gi < ng) {
-            for (int j = 0; j < G; ++j) vm = max(vm, min(max(a.row_vis[gi * G + j], 0), cap));
-        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) vm = max(vm, min(max(vis[k][j], 0), cap));
         cnt[k] = gi < ng ? kPrologue + max(1, (vm + 63) >> 6) : 0;
         sum += cnt[k];
     }
@@ -486,7 +526,30 @@ __global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int gi = kPer * (int)threadIdx.x + k;
-        if (gi < ng) s.pre[gi] = ex;
+        if (gi < ng) {
+            s.pre[gi] = ex;
+            const int b0 = req[k][0];
+            const bool kv_ok = kv[k] <= a.max_pages * a.page_size;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int bj = req[k][j];
+                int v = vis[k][j];
+                const bool ok = (bj >= 0) & (bj < a.batch) & (v >= 0) & (v <= a.score_stride) &
+                                (v <= a.max_pages * a.page_size);
+                if (!ok) {
+                    if (report) flag(a.status, DSA_DEV_ROW_RANGE);
+                    v = 0;
+                } else if (bj != b0) {
+                    if (report) flag(a.status, DSA_DEV_GROUP);
+                    v = 0;
+                } else if (v > kv[k] || !kv_ok) {
+                    if (report) flag(a.status, DSA_DEV_ROW_RANGE);
+                    v = 0;
+                }
+                rvis[gi * G + j] = v;
+            }
+            greq[gi] = b0 >= 0 && b0 < a.batch ? b0 : 0;
+        }
         ex += cnt[k];
     }
     if (threadIdx.x == 0) s.pre[ng] = (int)total;
@@ -517,7 +580,7 @@ __global__ __launch_bounds__(kBalancedThreads) void index_scores_balanced_kernel
             const int f_lo = 64 * tiles + (int)((int64_t)tail * js / tiles);
             const int f_hi = 64 * tiles + (int)((int64_t)tail * je / tiles);
             score_range<G, NT, true>(a, s, gi * G, 64 * js, min(64 * je, a.score_stride), f_lo, f_hi, js == 0,
-                                     gi != last);
+                                     gi != last, &rvis[gi * G], greq[gi]);
             last = gi;
         }
     }
