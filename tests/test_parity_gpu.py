@@ -241,6 +241,24 @@ def test_edge_groups_match_oracle(cfg):
     compare_step(inp, step, range(inp.n_rows), max_swap_rows=2)
 
 
+@pytest.mark.parametrize("group_rows,groups", [
+    (2, 1030),   # more groups than one balanced launch holds: the chunked launch of row groups
+    (2, 1024),   # exactly as many as it holds: the largest partition scan
+    (6, 513),    # the same past the limit for groups of six
+], ids=["g2_chunked", "g2_balanced_full", "g6_chunked"])
+def test_many_row_groups_sampled_rows(group_rows, groups):
+    cfg = W.Config(f"many_g{group_rows}", batch=groups, kv_range=(group_rows, 700), rows_per_req=group_rows,
+                   causal="mtp", page_size=64, mla_heads=16, group_rows=group_rows, index_splits=1,
+                   attn_splits=1)
+    inp = W.to(W.make(cfg), "cuda")
+    vis = inp.row_vis.cpu().numpy()
+    say(f"{cfg.name}: groups={groups} rows={inp.n_rows} vis {int(vis.min())}..{int(vis.max())}")
+    step = run_step(inp)
+    n = inp.n_rows
+    rows = sorted({0, 1, group_rows, n // 2, n // 2 + 1, n - group_rows, n - 1, int(np.argmax(vis))})
+    compare_step(inp, step, rows, max_swap_rows=2)
+
+
 # ------------------------------------------------------------------ long context, MTP verify, prefill
 
 def test_long_context_planted_sampled_rows():
