@@ -90,8 +90,10 @@ CONFIGS = {
     "c3": Config("c3", batch=32, kv_range=(16384, 65536), rows_per_req=6, causal="mtp",
                  mla_heads=32, index_splits=2, attn_splits=1, group_rows=6),
     # Long-prefix prefill on the owned top-k path: 4096 new rows after 65536.
+    # Five index splits keep each split's list (69632 / 5 scores) within 16
+    # keys a thread.
     "c4": Config("c4", batch=1, kv_lens=(65536 + 4096,), rows_per_req=4096,
-                 causal="prefill", prefix=65536, mla_heads=32, index_splits=4,
+                 causal="prefill", prefix=65536, mla_heads=32, index_splits=5,
                  attn_splits=1, group_rows=8),
 }
 
