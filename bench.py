@@ -325,7 +325,7 @@ def main():
         "dtype": "fp8",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.config}: {inp.n_rows} decode rows, kv_len "
+            "workload": f"{args.config}: {inp.n_rows} query rows, kv_len "
                         f"{int(inp.row_vis.min())}..{int(inp.row_vis.max())}, top-{inp.top_k}, "
                         f"indexer 64x128 fp8, MLA {inp.mla_heads} heads x 576 fp8, page {inp.page_size}",
             "batch": inp.n_rows, "kv_len_max": int(inp.row_vis.max()), "top_k": inp.top_k,
