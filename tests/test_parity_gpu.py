@@ -233,7 +233,15 @@ def test_edge_rows_match_oracle(page_size, top_k, splits, stride_pad, heads):
     # MTP-style causal groups of three, spans down to one token, 1024-token pages.
     W.Config("edge_mtp", batch=5, kv_lens=(3, 4, 64, 300, 3000), rows_per_req=3, causal="mtp",
              page_size=1024, mla_heads=32, group_rows=3, index_splits=1, attn_splits=2),
-], ids=["groups_of_2", "mtp_groups_of_3"])
+    # The remaining group sizes of the balanced schedule, MTP-causal, spans
+    # from one token to past a 2048-token page boundary.
+    W.Config("edge_g4", batch=3, kv_lens=(4, 700, 2500), rows_per_req=4, causal="mtp",
+             page_size=64, mla_heads=16, group_rows=4, index_splits=1, attn_splits=2),
+    W.Config("edge_g5", batch=3, kv_lens=(5, 1000, 2100), rows_per_req=5, causal="mtp",
+             page_size=256, mla_heads=16, group_rows=5, index_splits=2, attn_splits=1),
+    W.Config("edge_g7", batch=2, kv_lens=(7, 3000), rows_per_req=7, causal="mtp",
+             page_size=16, mla_heads=32, group_rows=7, index_splits=1, attn_splits=3),
+], ids=["groups_of_2", "mtp_groups_of_3", "mtp_groups_of_4", "mtp_groups_of_5", "mtp_groups_of_7"])
 def test_edge_groups_match_oracle(cfg):
     inp = W.to(W.make(cfg), "cuda")
     say(f"{cfg.name}: rows={inp.n_rows} vis={inp.row_vis.tolist()}")
