@@ -83,7 +83,10 @@ enum {
                                > max_pages * page_size or > score_stride */
     DSA_DEV_GROUP = 8,      /* rows of one scoring group belong to different requests */
     DSA_DEV_NAN = 16,       /* a NaN score reached the top-k (ordered, but reported) */
-    DSA_DEV_WRITE = 32      /* a new token's request, slot or position is out of range */
+    DSA_DEV_WRITE = 32,     /* a new token's request, slot or position is out of range */
+    DSA_DEV_SCALE = 64      /* a key or MLA row read for a row has a scale that is not a
+                               positive finite number; that token is left out (score -inf,
+                               not attended) */
 };
 
 /*
@@ -142,10 +145,21 @@ int dsa_lse_merge_project(const float* part_o, const float* part_lse, int32_t n_
                           int32_t n_splits, int32_t d_latent, const uint16_t* w_uv, int32_t d_v,
                           uint16_t* out, float* out_lse, hipStream_t stream);
 
-/* DSA_ABI_VERSION of the built library; loaders refuse a mismatch. */
+/*
+ * DSA_ABI_VERSION of the built library; loaders refuse a mismatch.  The
+ * version check follows the narrow native ABI of page "Harden DeepSeek V4
+ * DSpark DP2 serving" (section 4.1: the loader requires an exact ABI version
+ * and geometry; section 4.3 warning: a missing library or a wrong ABI aborts
+ * the path, with no fallback).
+ */
 int dsa_abi_version(void);
 
-/* Static, never-NULL name of a DSA_OK / DSA_ERR_* code ("unknown" otherwise). */
+/*
+ * Static, never-NULL name of a DSA_OK / DSA_ERR_* code ("unknown" otherwise),
+ * so that a binding can turn every native error into an exception with a
+ * readable message (same page, section 4.1: any native error becomes a Python
+ * exception).
+ */
 const char* dsa_status_string(int status);
 
 /*
@@ -191,7 +205,11 @@ int dsa_index_scores(const uint16_t* q, const float* head_w,
 
 /*
  * Workspace bytes dsa_topk needs for n_splits > 1: candidate keys and slots,
- * n_splits * top_k of each per row.  0 when n_splits == 1.
+ * n_splits * top_k of each per row.  0 when n_splits == 1.  The caller
+ * reserves the workspace once, up front, and a call with a smaller one is
+ * rejected (DSA_ERR_WORKSPACE) rather than served by an allocation (page
+ * "Harden DeepSeek V4 DSpark DP2 serving", section 6.3: workspaces reserved
+ * before graph capture, whose slices reject capacity or geometry changes).
  */
 size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits);
 
@@ -205,7 +223,8 @@ size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits);
  * be short or empty); each keeps its top-min(top_k, len) candidates and one
  * merge keeps the top-k of their union.  n_splits == 1 selects directly.
  * Score rows whose start is 16-byte aligned (score_stride a multiple of 4)
- * are read in 16-byte loads.
+ * are read in 16-byte loads; nothing outside [0, row_vis) of a row is used,
+ * and nothing past the row's score_stride entries is read.
  *   scores [n_rows, score_stride] f32 (only [0, row_vis) is read)
  *   topk_idx [n_rows, top_k] i32 out: selected slots in ascending order, then -1
  *   topk_count [n_rows] i32 out: min(top_k, row_vis)

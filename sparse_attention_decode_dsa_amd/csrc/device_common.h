@@ -218,6 +218,13 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// A per-token scale is usable when it is a positive finite number: its bit
+// pattern lies in [0x00000001, 0x7F7FFFFF] (zero, negatives, infinities and
+// NaNs all fall outside).
+__device__ __forceinline__ bool scale_ok(float s) {
+    return __float_as_uint(s) - 1u < 0x7F7FFFFFu;
+}
+
 __device__ __forceinline__ void flag(int32_t* status, int32_t bit) {
     atomicOr(status, bit);
 }

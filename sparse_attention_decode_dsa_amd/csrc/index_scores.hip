@@ -294,6 +294,12 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
         for (int j = 0; j < 4; ++j) pin(kg.b[j]);
         pin(kg.scale);
         const int t = tg + lane;
+        // A key whose scale is not a positive finite number is not scored
+        // (the head reduction relies on a positive scale); one inside a
+        // checked span is reported.
+        const bool sok = scale_ok(kg.scale);
+        if (__ballot(kg.ok && !sok && t < vchk) != 0ull && lane == 0) flag(a.status, DSA_DEV_SCALE);
+        kg.ok = kg.ok && sok;
 #pragma unroll 1
         for (int rr = 0; rr < G; ++rr) {
             const int r = r0 + rr;

@@ -371,6 +371,18 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) live[i] = live[i] && row_at(tile, tk0 + i) >= 0;
         }
+        // A selected row whose scale is not a positive finite number is left
+        // out of the attention and reported.
+        {
+            bool sbad = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = scale_ok(ts[i]);
+                sbad |= live[i] && !ok;
+                live[i] = live[i] && ok;
+            }
+            if (__ballot(sbad) != 0ull && lane == 0) flag(a.status, DSA_DEV_SCALE);
+        }
         float lg[4];
         float mx = -INFINITY;
 #pragma unroll
@@ -397,8 +409,11 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         }
         l_run = l_run * alpha + rows4_sum(ps);
         // tokens t = 16 tbk + 4g + i: group t / 8 = 2 tbk + g / 2, slot 4 (g & 1) + i
-        const v2bf p01 = v2bf{(__bf16)(pv[0] * ts[0]), (__bf16)(pv[1] * ts[1])};
-        const v2bf p23 = v2bf{(__bf16)(pv[2] * ts[2]), (__bf16)(pv[3] * ts[3])};
+        float pt4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pt4[i] = live[i] ? pv[i] * ts[i] : 0.0f;   // no 0 * (bad scale)
+        const v2bf p01 = v2bf{(__bf16)pt4[0], (__bf16)pt4[1]};
+        const v2bf p23 = v2bf{(__bf16)pt4[2], (__bf16)pt4[3]};
         *reinterpret_cast<uint2*>(s_p + (2 * tbk + (g >> 1)) * kPGroup + h * 16 + 8 * (g & 1)) =
             uint2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
         const bool any_moved = __ballot(moved) != 0ull;   // same in the 4 wavefronts of head block hb

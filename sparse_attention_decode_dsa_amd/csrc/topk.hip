@@ -572,7 +572,9 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
     uint32_t key[P];
     bool nan = false;
     for (int i = threadIdx.x; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
-    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    // 16-byte loads read whole chunks, so the last one may reach up to three
+    // floats past the list: taken only where those stay inside the row.
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && lo + ((n + 3) & ~3) <= a.score_stride) {
         load_list_vec<P, true>(s, src, n, base, mine, key, nan);
     } else {
         load_list<P>(s, n, base, mine, key, [&](int i) {

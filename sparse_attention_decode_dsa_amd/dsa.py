@@ -20,8 +20,8 @@ import torch
 ABI_VERSION = 6
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
-DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE"}
-DEV_PAGE_OOB, DEV_TOPK_OOB, DEV_ROW_RANGE, DEV_GROUP, DEV_NAN, DEV_WRITE = 1, 2, 4, 8, 16, 32
+DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE", 64: "SCALE"}
+DEV_PAGE_OOB, DEV_TOPK_OOB, DEV_ROW_RANGE, DEV_GROUP, DEV_NAN, DEV_WRITE, DEV_SCALE = 1, 2, 4, 8, 16, 32, 64
 
 
 class DsaError(RuntimeError):

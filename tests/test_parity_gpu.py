@@ -56,15 +56,36 @@ def compare_step(inp, step, rows, max_swap_rows=None):
     g_lse = step.out_lse[rows].cpu().double().numpy()
     swapped = []
     for i in range(len(rows)):
-        sw = check_topk_row(g_idx[i], g_cnt[i], ref["topk_idx"][i], ref["topk_count"][i],
-                            ref["scores"][i], vis[i], inp.top_k)
-        if sw:
-            swapped.append(rows[i])
-            continue
-        check_out(g_out[i], g_lse[i], ref["out"][i], ref["lse"][i])
+        if check_topk_row(g_idx[i], g_cnt[i], ref["topk_idx"][i], ref["topk_count"][i],
+                          ref["scores"][i], vis[i], inp.top_k):
+            swapped.append(i)
+    # What each row's output is compared with: the oracle's own step, except
+    # for rows whose selection differs from the oracle's inside the tie band.
+    # Those attend other tokens, so the oracle attends the GPU's selection
+    # (validated just above) for them; no row goes unchecked.
+    ref["out_cmp"] = ref["out"].copy()
+    ref["lse_cmp"] = ref["lse"].copy()
+    if swapped:
+        r_out, r_lse = oracle_on_selection(sub_np, swapped, g_idx, g_cnt, step.attn_splits)
+        ref["out_cmp"][swapped] = r_out
+        ref["lse_cmp"][swapped] = r_lse
+    for i in range(len(rows)):
+        check_out(g_out[i], g_lse[i], ref["out_cmp"][i], ref["lse_cmp"][i])
+    swapped = [rows[i] for i in swapped]
     if max_swap_rows is not None:
         assert len(swapped) <= max_swap_rows, swapped
     return ref, sub, swapped
+
+
+def oracle_on_selection(sub_np, which, g_idx, g_cnt, n_splits):
+    """The oracle's attention and merge for rows `which` of the subset, over
+    the given (GPU) selected lists instead of its own."""
+    which = list(which)
+    po, pl = O.sparse_mla(sub_np["q_mla"][which], sub_np["kv_code"], sub_np["kv_scale"],
+                          sub_np["page_table"], np.asarray(sub_np["row_req"])[which],
+                          np.asarray(g_idx)[which], np.asarray(g_cnt)[which], float(sub_np["sm_scale"]),
+                          n_splits, int(sub_np["page_size"]))
+    return O.lse_merge(po, pl)
 
 
 def mla_on_oracle_selection(sub, ref, n_splits):
@@ -271,15 +292,31 @@ def test_many_row_groups_sampled_rows(group_rows, groups):
 
 def test_long_context_planted_sampled_rows():
     """8 requests up to 131072 tokens, 16 index splits, 32 attention splits,
-    4 planted slots per request (both caches' scales x8)."""
+    4 planted slots per request (both caches' scales x8).  Sampled rows cover
+    every request length (9600, 38000, 77000, 131072)."""
     inp = W.make("c2", device="cuda")
     say(f"c2: B={inp.n_rows} vis={inp.row_vis.tolist()}")
     step = run_step(inp)
     idx = step.topk_idx.cpu().numpy()
     hit = sum(len(set(inp.planted_slots[b].tolist()) & set(idx[b].tolist())) for b in range(inp.n_rows))
     say(f"c2: {hit} of {inp.planted_slots.numel()} planted slots selected")
-    ref, sub, swapped = compare_step(inp, step, [0, 3, 6], max_swap_rows=1)
+    rows = [0, 1, 3, 5, 6]
+    ref, sub, swapped = compare_step(inp, step, rows, max_swap_rows=2)
     say(f"c2: swapped {swapped}")
+    # A planted slot whose oracle score lies clearly above the row's k-th
+    # score (outside the tie band) is in the oracle's top-k, so the GPU must
+    # have selected it.
+    must = 0
+    for i, r in enumerate(rows):
+        s = ref["scores"][i]
+        tau = np.min(s[ref["topk_idx"][i][:ref["topk_count"][i]]])
+        b = int(inp.row_req[r])
+        for t in inp.planted_slots[b].tolist():
+            if s[t] > tau + 1e-3 * abs(tau):
+                must += 1
+                assert t in set(idx[r].tolist()), f"row {r}: planted slot {t} (score {s[t]:.4g} > {tau:.4g})"
+    say(f"c2: {must} planted slots above the k-th score, all selected")
+    assert must > 0
     mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
 
 
@@ -297,7 +334,7 @@ def test_mtp_verify_grouped_rows():
 
 def test_long_prefix_prefill_sampled_rows():
     """4096 prefill rows after a 65536-token prefix, groups of 8 rows,
-    4 index splits, one attention split; sampled rows across the range."""
+    5 index splits, one attention split; sampled rows across the range."""
     inp = W.make("c4", device="cuda")
     say(f"c4: R={inp.n_rows} vis {int(inp.row_vis.min())}..{int(inp.row_vis.max())}")
     step = run_step(inp)
@@ -484,3 +521,62 @@ def test_rows_of_different_requests_in_one_group_are_reported():
     torch.cuda.synchronize()
     assert int(st.item()) & dsa.DEV_GROUP
     assert torch.all(torch.isneginf(sc[1]))     # the offending row is empty
+
+
+def test_bad_scales_are_reported_and_left_out():
+    """Scales that are not positive finite numbers.  In the index-key cache
+    (negative, zero, NaN): the indexer sets DSA_DEV_SCALE, scores those tokens
+    -inf and writes every other score as a clean call does.  In the MLA cache
+    (negative, NaN, +inf) at selected slots: the attention sets the bit and
+    leaves those tokens out; the row attends the others, which the oracle
+    computes from the filtered list."""
+    from dataclasses import replace
+    inp = W.to(W.make("c0"), "cuda")
+    good = run_step(inp, 1, 4)
+    pt = inp.page_table.cpu()
+    p = inp.page_size
+
+    def at(b, t):
+        return int(pt[b, t // p]), t % p
+
+    ks = inp.k_scale.clone()
+    planted = {(1, 100): -0.5, (1, 4000): float("nan"), (1, 2000): 0.0, (0, 7): -1e-30}
+    for (b, t), val in planted.items():
+        ks[at(b, t)] = val
+    st = dsa.new_status()
+    sc, _ = dsa.index_scores(inp.q_idx, inp.head_w, inp.k_code, ks, inp.page_table, inp.kv_lens,
+                             inp.row_req, inp.row_vis, score_stride=good.score_stride, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == dsa.DEV_SCALE
+    want = good.scores.clone()
+    for (b, t) in planted:
+        want[b, t] = -float("inf")
+    assert torch.equal(sc, want)
+
+    # MLA rows: bad scales at selected slots of both rows.
+    idx = good.topk_idx.cpu().numpy()
+    cnt = good.topk_count.cpu().numpy()
+    kv = inp.kv_cache.clone()
+    kvs = W.kv_scale_view(kv)
+    bad_slots = {0: [int(idx[0, 3]), int(idx[0, 1499])], 1: [int(idx[1, 0]), int(idx[1, 1000])]}
+    vals = [-2.0, float("nan"), float("inf"), -0.0]
+    for j, (b, t) in enumerate((b, t) for b, ts in bad_slots.items() for t in ts):
+        kvs[at(b, t)] = vals[j]
+    st = dsa.new_status()
+    po, pl, _ = dsa.sparse_mla_decode(inp.q_mla, kv, inp.page_table, inp.row_req, inp.row_vis,
+                                      good.topk_idx, good.topk_count, 4, inp.sm_scale, status=st)
+    out, lse = dsa.lse_merge(po, pl)
+    torch.cuda.synchronize()
+    assert int(st.item()) == dsa.DEV_SCALE
+    n = W.as_numpy(W.subset(inp, range(inp.n_rows)))
+    k = idx.shape[1]
+    f_idx = np.full((inp.n_rows, k), -1, dtype=np.int64)
+    f_cnt = np.zeros(inp.n_rows, dtype=np.int64)
+    for i in range(inp.n_rows):
+        keep = [t for t in idx[i, :cnt[i]] if t not in bad_slots[i]]
+        f_idx[i, :len(keep)] = keep
+        f_cnt[i] = len(keep)
+    r_po, r_pl = O.sparse_mla(n["q_mla"], n["kv_code"], n["kv_scale"], n["page_table"], n["row_req"], f_idx,
+                              f_cnt, inp.sm_scale, 1, inp.page_size)
+    r_out, r_lse = O.lse_merge(r_po, r_pl)
+    check_out(bf16_to_f64(out), lse.cpu().double().numpy(), r_out, r_lse)
