@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 6
+#define DSA_ABI_VERSION 7
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -72,7 +72,8 @@ enum {
     DSA_ERR_SHAPE = -2,       /* a size, stride or count is out of range or inconsistent */
     DSA_ERR_UNSUPPORTED = -3, /* valid but not built: head count, head dim, page size */
     DSA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the size query */
-    DSA_ERR_LAUNCH = -5       /* the HIP runtime refused a launch */
+    DSA_ERR_LAUNCH = -5,      /* the HIP runtime refused a launch */
+    DSA_ERR_SCRATCH = -6      /* dsa_topk_noalloc: the call needs more than DSA_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Bits ORed by kernels into the caller's device status word. */
@@ -234,6 +235,27 @@ size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits);
 int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
              int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes,
              int32_t* topk_idx, int32_t* topk_count, int32_t* status, hipStream_t stream);
+
+/*
+ * dsa_topk_noalloc -- dsa_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, rules and results as dsa_topk, without the
+ * workspace: the candidates of a split call (n_splits > 1) live in a fixed
+ * array of DSA_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
+ * one per GPU, from the first call on that GPU until the process ends.  The
+ * call allocates nothing.
+ * Limit: dsa_topk_workspace_size(n_rows, top_k, n_splits) must not exceed
+ * DSA_NOALLOC_SCRATCH_BYTES, else DSA_ERR_SCRATCH and nothing is enqueued
+ * (16 MiB holds n_rows * n_splits * top_k up to 2^21 candidates).  The array
+ * keeps the last call's contents; nothing in it needs to start at zero.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the caller.
+ * DSA_ERR_LAUNCH if the array's device address cannot be looked up.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dsa_topk_noalloc(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
+                     int32_t top_k, int32_t n_splits, int32_t* topk_idx, int32_t* topk_count,
+                     int32_t* status, hipStream_t stream);
 
 /*
  * dsa_sparse_mla_decode -- split-K absorbed-MLA attention over each row's

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["dsa_api.cpp", "quantize_q.hip", "index_scores.hip", "topk.hip",
+SOURCES = ["dsa_api.cpp", "quantize_q.hip", "index_scores.hip", "topk.hip", "topk_noalloc.hip",
            "sparse_mla.hip", "lse_merge.hip", "cache_write.hip", "merge_project.hip"]
 
 

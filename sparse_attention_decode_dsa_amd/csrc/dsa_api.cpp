@@ -52,6 +52,8 @@ const char* dsa_status_string(int status) {
         case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: head count, head dim or page size not built";
         case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
         case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH: the HIP runtime refused a launch";
+        case DSA_ERR_SCRATCH:
+            return "DSA_ERR_SCRATCH: the call needs more scratch than the library's fixed buffer holds";
         default: return "unknown";
     }
 }
@@ -148,27 +150,11 @@ size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits) 
 int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
              int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes,
              int32_t* topk_idx, int32_t* topk_count, int32_t* status, hipStream_t stream) {
-    if (n_rows < 0 || n_rows > kMaxRows || score_stride < 1) return DSA_ERR_SHAPE;
-    if (top_k < 1 || top_k > dsa::kTopkMaxK) return DSA_ERR_SHAPE;
-    if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
-    if (((int64_t)score_stride + n_splits - 1) / n_splits > dsa::kTopkMaxList) return DSA_ERR_SHAPE;
-    if (n_splits > 1 && (int64_t)n_splits * top_k > dsa::kTopkMaxList) return DSA_ERR_SHAPE;
-    if (!scores || !row_vis || !topk_idx || !topk_count || !status) return DSA_ERR_NULL;
-    if (n_rows == 0) return DSA_OK;
-    dsa::TopkArgs a;
-    a.scores = scores; a.score_stride = score_stride; a.row_vis = row_vis;
-    a.n_rows = n_rows; a.top_k = top_k; a.n_splits = n_splits;
-    a.cand_key = nullptr; a.cand_slot = nullptr;
-    if (n_splits > 1) {
-        const size_t need = dsa_topk_workspace_size(n_rows, top_k, n_splits);
-        if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
-        char* ws = static_cast<char*>(workspace);
-        const size_t kb = topk_ws_keys(n_rows, top_k, n_splits);
-        a.cand_key = reinterpret_cast<uint32_t*>(ws);
-        a.cand_slot = reinterpret_cast<int32_t*>(ws + kb);
-    }
-    a.topk_idx = topk_idx; a.topk_count = topk_count; a.status = status;
-    return launch_status(dsa::launch_topk(a, stream));
+    const int rc = dsa::topk_validate(scores, score_stride, row_vis, n_rows, top_k, n_splits, topk_idx,
+                                      topk_count, status);
+    if (rc != DSA_OK || n_rows == 0) return rc;
+    return dsa::topk_launch(scores, score_stride, row_vis, n_rows, top_k, n_splits, workspace, workspace_bytes,
+                            topk_idx, topk_count, status, stream);
 }
 
 int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
@@ -215,3 +201,38 @@ int dsa_lse_merge(const float* part_o, const float* part_lse, int32_t n_rows, in
 }
 
 }  // extern "C"
+
+namespace dsa {
+
+int topk_validate(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
+                  int32_t top_k, int32_t n_splits, const int32_t* topk_idx, const int32_t* topk_count,
+                  const int32_t* status) {
+    if (n_rows < 0 || n_rows > kMaxRows || score_stride < 1) return DSA_ERR_SHAPE;
+    if (top_k < 1 || top_k > kTopkMaxK) return DSA_ERR_SHAPE;
+    if (n_splits < 1 || n_splits > kMaxSplits) return DSA_ERR_SHAPE;
+    if (((int64_t)score_stride + n_splits - 1) / n_splits > kTopkMaxList) return DSA_ERR_SHAPE;
+    if (n_splits > 1 && (int64_t)n_splits * top_k > kTopkMaxList) return DSA_ERR_SHAPE;
+    if (!scores || !row_vis || !topk_idx || !topk_count || !status) return DSA_ERR_NULL;
+    return DSA_OK;
+}
+
+int topk_launch(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
+                int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes, int32_t* topk_idx,
+                int32_t* topk_count, int32_t* status, hipStream_t stream) {
+    TopkArgs a;
+    a.scores = scores; a.score_stride = score_stride; a.row_vis = row_vis;
+    a.n_rows = n_rows; a.top_k = top_k; a.n_splits = n_splits;
+    a.cand_key = nullptr; a.cand_slot = nullptr;
+    if (n_splits > 1) {
+        const size_t need = dsa_topk_workspace_size(n_rows, top_k, n_splits);
+        if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+        char* ws = static_cast<char*>(workspace);
+        const size_t kb = topk_ws_keys(n_rows, top_k, n_splits);
+        a.cand_key = reinterpret_cast<uint32_t*>(ws);
+        a.cand_slot = reinterpret_cast<int32_t*>(ws + kb);
+    }
+    a.topk_idx = topk_idx; a.topk_count = topk_count; a.status = status;
+    return launch_status(launch_topk(a, stream));
+}
+
+}  // namespace dsa

@@ -92,6 +92,16 @@ constexpr int kTopkMaxList = 32768;
 constexpr int kTopkMaxK = 8192;
 constexpr int kMaxSplits = 64;
 
+// Host validation of a top-k call (the rules of dsa_topk, without the
+// workspace), and its launch with a given workspace (checked against the
+// size dsa_topk_workspace_size gives).  Both return DSA_OK or a DSA_ERR_*.
+int topk_validate(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
+                  int32_t top_k, int32_t n_splits, const int32_t* topk_idx, const int32_t* topk_count,
+                  const int32_t* status);
+int topk_launch(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
+                int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes, int32_t* topk_idx,
+                int32_t* topk_count, int32_t* status, hipStream_t stream);
+
 hipError_t launch_quantize_q(const uint16_t* q, int32_t n_pairs, uint8_t* code, float* scale,
                              hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);

@@ -17,7 +17,7 @@ import os
 
 import torch
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE", 64: "SCALE"}
@@ -39,6 +39,7 @@ _SIGS = {
                           _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
     "dsa_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
     "dsa_topk": ([_p, _i32, _p, _i32, _i32, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p], ctypes.c_int),
+    "dsa_topk_noalloc": ([_p, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p], ctypes.c_int),
     "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "dsa_lse_merge": ([_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
@@ -176,6 +177,26 @@ def topk(scores, row_vis, top_k: int, n_splits: int = 1, workspace=None, topk_id
                           _ptr(topk_idx, torch.int32, "topk_idx"),
                           _ptr(topk_count, torch.int32, "topk_count"),
                           _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_topk")
+    return topk_idx, topk_count, status
+
+
+def topk_noalloc(scores, row_vis, top_k: int, n_splits: int = 1, topk_idx=None, topk_count=None,
+                 status=None, stream=None):
+    """topk() with the candidates in the library's fixed device array instead
+    of a workspace (dsa_topk_noalloc); the same results."""
+    r, stride = scores.shape
+    dev = scores.device
+    if topk_idx is None:
+        topk_idx = torch.empty((r, top_k), dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty((r,), dtype=torch.int32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    _check(lib().dsa_topk_noalloc(_ptr(scores, torch.float32, "scores"), stride,
+                                  _ptr(row_vis, torch.int32, "row_vis"), r, top_k, n_splits,
+                                  _ptr(topk_idx, torch.int32, "topk_idx"),
+                                  _ptr(topk_count, torch.int32, "topk_count"),
+                                  _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_topk_noalloc")
     return topk_idx, topk_count, status
 
 

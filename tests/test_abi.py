@@ -12,7 +12,7 @@ from sparse_attention_decode_dsa_amd import dsa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsa.h")
 
-OK, NULL, SHAPE, UNSUP, WS = 0, -1, -2, -3, -4
+OK, NULL, SHAPE, UNSUP, WS, SCRATCH = 0, -1, -2, -3, -4, -6
 P = 0x1000  # a non-NULL dummy device pointer; never dereferenced on these paths
 
 
@@ -44,7 +44,7 @@ def test_abi_version_and_status_strings(L):
     assert L.dsa_abi_version() == dsa.ABI_VERSION
     hdr = open(HEADER).read()
     assert f"#define DSA_ABI_VERSION {dsa.ABI_VERSION}" in hdr
-    for code in (OK, NULL, SHAPE, UNSUP, WS, -5):
+    for code in (OK, NULL, SHAPE, UNSUP, WS, -5, SCRATCH):
         assert dsa.status_string(code).startswith("DSA_")
     assert dsa.status_string(12345) == "unknown"
 
@@ -177,3 +177,22 @@ def test_lse_merge_project_validation(L):
     assert _mp(L, part_o=P + 4) == SHAPE        # 16-byte aligned partials
     assert _mp(L, w_uv=P + 8) == SHAPE          # 16-byte aligned weights
     assert _mp(L, n_rows=0) == OK
+
+
+def test_topk_noalloc_validation(L):
+    """The no-allocation top-k applies dsa_topk's rules, then rejects a call
+    whose candidates exceed its fixed array, all before any HIP call."""
+    def call(**kw):
+        a = dict(scores=P, score_stride=4096, row_vis=P, n_rows=8, top_k=2048, n_splits=4,
+                 topk_idx=P, topk_count=P, status=P, stream=None)
+        a.update(kw)
+        return L.dsa_topk_noalloc(*a.values())
+    assert call(n_rows=-1) == SHAPE
+    assert call(top_k=0) == SHAPE
+    assert call(n_splits=65) == SHAPE
+    assert call(scores=None) == NULL
+    assert call(n_rows=0) == OK
+    # 1024 rows x 16 splits x 2048 candidates x 8 bytes = 256 MiB > 16 MiB
+    assert call(n_rows=1024, n_splits=16, score_stride=64) == SCRATCH
+    hdr = open(HEADER).read()
+    assert "#define DSA_NOALLOC_SCRATCH_BYTES (16u << 20)" in hdr
