@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch kernels directly, no HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--cpu-seconds-1t", type=float, default=4.0, help="budget of the one-thread oracle sample")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the bandwidth kernels and the MTP-verify indexer measurement")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--seed", type=int, default=None)
@@ -97,22 +100,28 @@ def algorithmic_bytes(inp) -> dict:
     return {"step": idx + mla, "index_kernel": idx, "index_flops": sum(2 * 64 * 128 * v for v in vis)}
 
 
-def cpu_baseline(inps, seconds: float) -> dict:
-    """The oracle, as it stands, on rows of the same workload (the rotated
-    input sets in turn) until the time budget is spent; scaled to steps/s of
-    the full batch."""
-    import numpy as np  # noqa: F401
-    from threadpoolctl import threadpool_info
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def _time_oracle_rows(inps, seconds: float):
+    """The oracle on one row at a time of the workload (every 8th row first,
+    then the rest, input set after input set) until `seconds` of CPU work are
+    done; returns (rows, seconds)."""
     from oracle import dsa_oracle as O
     from sparse_attention_decode_dsa_amd import workload as W
 
     n_rows = inps[0].n_rows
     rows = list(range(n_rows))
-    # deterministic order: every 8th row first, then the rest
     order = rows[::8] + [r for r in rows if r % 8]
-    done = 0
-    t_total = 0.0
+    done, t_total = 0, 0.0
     for inp in inps:
         for r in order:
             sub = W.as_numpy(W.subset(inp, [r]))
@@ -121,15 +130,140 @@ def cpu_baseline(inps, seconds: float) -> dict:
             t_total += time.perf_counter() - t0
             done += 1
             if t_total >= seconds:
-                break
-        if t_total >= seconds:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": done / t_total / n_rows, "unit": "steps/s", "cores": int(threads),
-            "kind": "oracle",
+                return done, t_total
+    return done, t_total
+
+
+def cpu_baseline(inps, seconds: float, one_thread_seconds: float) -> dict:
+    """The oracle, as it stands, on rows of the same workload (the rotated
+    input sets in turn) until the time budget is spent, with its BLAS pool
+    pinned to every core this process may run on; then again with one
+    thread.  Scaled to steps/s of the full batch."""
+    from threadpoolctl import threadpool_limits
+
+    n_rows = inps[0].n_rows
+    affinity = len(os.sched_getaffinity(0))
+    # The host's share of cores: OMP_NUM_THREADS where the environment sets
+    # one (the GPU boxes do), else every core the process may run on.
+    cores = min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity) or affinity))
+    with threadpool_limits(limits=cores):
+        done, t_total = _time_oracle_rows(inps, seconds)
+    with threadpool_limits(limits=1):
+        done1, t1 = _time_oracle_rows(inps, one_thread_seconds)
+    return {"value": done / t_total / n_rows, "unit": "steps/s", "cores": cores,
+            "affinity_cores": affinity, "cpu_model": _cpu_model(), "kind": "oracle",
             "sample": f"{done} rows ({done / n_rows:.2f} steps of {n_rows} rows, over "
-                      f"{len(inps)} input sets), timed one row at a time ({t_total:.1f} s), "
-                      f"scaled to whole steps"}
+                      f"{len(inps)} input sets), timed one row at a time ({t_total:.1f} s) with "
+                      f"{cores} BLAS threads, scaled to whole steps",
+            "one_thread": {"value": done1 / t1 / n_rows, "unit": "steps/s",
+                           "sample": f"{done1} rows timed one at a time ({t1:.1f} s), 1 thread"}}
+
+
+def measure_bandwidth(dev, nbytes: int, reps: int = 20) -> dict:
+    """Plain streaming-read and copy kernels (libdsa_bw.so) over `nbytes`,
+    cycling through four buffers (more than the chip's 256 MB memory-side
+    cache holds in total), timed like the step's kernels: a graph of `reps`
+    launches replayed between two HIP events on the launch stream.  Copy
+    counts the bytes read plus the bytes written."""
+    import ctypes
+
+    import torch
+
+    from sparse_attention_decode_dsa_amd import build as B
+
+    L = ctypes.CDLL(B.BW_LIB)
+    L.dsa_bw_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    L.dsa_bw_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(4)]
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for j in range(4):
+                fn(j, side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = torch.cuda.current_stream().cuda_stream
+            for j in range(reps):
+                fn(j % 4, st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        e0.record(stream)
+        for _ in range(3):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / (3 * reps)
+
+    best_read, best_copy = 0.0, 0.0
+    for wgs in (512, 1024, 2048):
+        us = timed(lambda j, st: L.dsa_bw_stream_read(bufs[j].data_ptr(), nbytes, wgs, sink.data_ptr(), st))
+        best_read = max(best_read, nbytes / us / 1e3)
+        us = timed(lambda j, st: L.dsa_bw_copy(bufs[j].data_ptr(), bufs[(j + 1) % 4].data_ptr(), nbytes, wgs, st))
+        best_copy = max(best_copy, 2 * nbytes / us / 1e3)
+    del bufs, sink
+    torch.cuda.synchronize()
+    return {"stream_read_GBps": round(best_read, 1), "copy_GBps": round(best_copy, 1), "bytes": nbytes,
+            "how": "libdsa_bw.so kernels, 256-thread workgroups, best of 512/1024/2048 workgroups, "
+                   "four buffers in turn; copy counts bytes read + written"}
+
+
+def c3_indexer(dev, seed: int, reps: int = 20) -> dict:
+    """The multi-row indexer at the MTP-verify workload (32 requests x 6
+    causal rows, kv_len U[16384, 65536], groups of 6 rows), timed like the
+    step's kernels over two input sets, against the dense fp8 MFMA peak."""
+    import torch
+
+    from sparse_attention_decode_dsa_amd import dsa
+    from sparse_attention_decode_dsa_amd import workload as W
+
+    inps = [W.make("c3", seed=seed + k, device=dev) for k in range(2)]
+    steps = [dsa.DecodeStep(x) for x in inps]
+    fns = [lambda i=i, st=st: dsa.index_scores(
+        i.q_idx, i.head_w, i.k_code, i.k_scale, i.page_table, i.kv_lens, i.row_req, i.row_vis,
+        group_rows=st.group_rows, score_stride=st.score_stride, scores=st.scores, status=st.status)
+        for i, st in zip(inps, steps)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in range(reps):
+            fns[j % 2]()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        g.replay()
+    e1.record(stream)
+    e1.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / (3 * reps)
+    for st in steps:
+        dsa.check_status(st.status)
+    flops = sum(algorithmic_bytes(x)["index_flops"] for x in inps) / 2
+    tflops = flops / (us * 1e-6) / 1e12
+    out = {"workload": "c3: 32 requests x 6 causal MTP rows, kv_len U[16384, 65536], rows scored in groups of 6",
+           "us_per_launch": round(us, 2), "fp8_flops_per_launch": flops, "achieved_TFLOPs": round(tflops, 1),
+           "peak_TFLOPs": FP8_PEAK_TFLOPS, "frac": round(tflops / FP8_PEAK_TFLOPS, 4)}
+    del inps, steps
+    torch.cuda.synchronize()
+    return out
 
 
 def main():
@@ -373,8 +507,16 @@ def main():
             "bound": "latency",
         },
     }
+    if not args.no_extras:
+        bw = measure_bandwidth(dev, ab["index_kernel"])
+        line["roofline"]["measured"] = bw
+        if line["roofline"]["unit"] == "GB/s":
+            line["roofline"]["frac_of_measured_read"] = round(achieved / bw["stream_read_GBps"], 4)
+        line["step_frac_of_measured_read"] = round(ab["step"] / (ms * 1e-3) / (bw["stream_read_GBps"] * 1e9), 4)
+        if args.config != "c3":
+            line["c3_indexer_mfma"] = c3_indexer(dev, base_seed + 100)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inps, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inps, args.cpu_seconds, args.cpu_seconds_1t)
     print(json.dumps(line), flush=True)
 
 

@@ -23,6 +23,9 @@ LIB = os.path.join(PKG, "libdsa.so")
 
 SOURCES = ["dsa_api.cpp", "quantize_q.hip", "index_scores.hip", "topk.hip", "topk_noalloc.hip",
            "sparse_mla.hip", "lse_merge.hip", "cache_write.hip", "merge_project.hip"]
+# The benchmark's plain bandwidth kernels, in a library of their own.
+BW_SOURCES = ["bandwidth.hip"]
+BW_LIB = os.path.join(PKG, "libdsa_bw.so")
 
 
 def hipcc() -> str:
@@ -58,22 +61,29 @@ def _compile(src: str) -> tuple[str, str]:
     return obj, err
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source for gfx950 and link libdsa.so; returns its path."""
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for obj, msg in results:
-        if verbose and msg.strip():
-            print(msg, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
-        raise RuntimeError(f"linking libdsa.so failed:\n{' '.join(cmd)}\n{p.stdout}{p.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{' '.join(cmd)}\n{p.stdout}{p.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source for gfx950 and link libdsa.so (and the benchmark's
+    libdsa_bw.so); returns the path of libdsa.so."""
+    srcs = SOURCES + BW_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        results = dict(zip(srcs, ex.map(_compile, srcs)))
+    for obj, msg in results.values():
+        if verbose and msg.strip():
+            print(msg, file=sys.stderr)
+    _link([results[s][0] for s in SOURCES], LIB)
+    _link([results[s][0] for s in BW_SOURCES], BW_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BW_LIB}")
     return LIB
 
 

@@ -196,3 +196,21 @@ def test_topk_noalloc_validation(L):
     assert call(n_rows=1024, n_splits=16, score_stride=64) == SCRATCH
     hdr = open(HEADER).read()
     assert "#define DSA_NOALLOC_SCRATCH_BYTES (16u << 20)" in hdr
+
+
+def test_bandwidth_library_exports_its_header():
+    """libdsa_bw.so (the benchmark's plain read and copy kernels) exports what
+    include/dsa_bw.h declares and rejects bad arguments before any launch."""
+    from sparse_attention_decode_dsa_amd import build as B
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "dsa_bw.h")).read(), flags=re.S)
+    names = set(re.findall(r"^\s*int\s+(dsa_bw_\w+)\s*\(", src, flags=re.M))
+    assert names == {"dsa_bw_stream_read", "dsa_bw_copy"}
+    L = ctypes.CDLL(B.BW_LIB)
+    for n in names:
+        assert hasattr(L, n)
+    L.dsa_bw_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    L.dsa_bw_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+    assert L.dsa_bw_stream_read(None, 4096, 8, P, None) == -1
+    assert L.dsa_bw_stream_read(P, 4095, 8, P, None) == -1
+    assert L.dsa_bw_copy(P, P + 8, 4096, 8, None) == -1
