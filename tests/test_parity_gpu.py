@@ -157,6 +157,35 @@ def test_topk_bit_exact_on_synthetic_scores(k, n_splits):
         np.testing.assert_array_equal(idx[i], ri)
 
 
+@pytest.mark.parametrize("n_splits", [1, 3])
+def test_topk_with_infinities_matches_oracle(n_splits):
+    """Rows with -inf inside the visible span (tokens on invalid pages, keys
+    with bad scales), fewer finite scores than k, and +inf scores: the
+    selection still follows (score desc, slot asc)."""
+    rng = np.random.default_rng(31 + n_splits)
+    r, stride, k = 6, 12000, 2048
+    s = rng.normal(size=(r, stride)).astype(np.float32)
+    vis = [12000, 12000, 9000, 12000, 5000, 3000]
+    s[0, rng.random(stride) < 0.95] = -np.inf      # ~600 finite scores < k
+    s[1, rng.random(stride) < 0.5] = -np.inf       # ~6000 finite scores > k
+    s[2, :4000] = -np.inf
+    s[3, [5, 77, 11000]] = np.inf                  # +inf at the top
+    s[4, rng.random(stride) < 0.7] = -np.inf
+    s[4, [10, 20]] = np.inf
+    s[5] = -np.inf                                 # nothing finite at all
+    for i, v in enumerate(vis):
+        s[i, v:] = -np.inf
+    idx, cnt, st = dsa.topk(torch.from_numpy(s).cuda(), torch.tensor(vis, dtype=torch.int32).cuda(), k,
+                            n_splits)
+    torch.cuda.synchronize()
+    dsa.check_status(st)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for i, v in enumerate(vis):
+        ri, rc = O.topk_global(s[i].astype(np.float64), v, k)
+        assert cnt[i] == rc, (i, v)
+        np.testing.assert_array_equal(idx[i], ri)
+
+
 def test_topk_all_equal_scores_keep_lowest_slots():
     s = np.zeros((2, 9000), dtype=np.float32)
     vis = [9000, 4097]
