@@ -29,6 +29,10 @@ context parallel (DCP) for GLM-5 / DeepSeek-V3.2" (sgl-project/sglang PR
 * The step after the path: Future work, projecting V (W_UV) before the LSE
   merge; here the merge is followed by the projection, which is the same
   linear map applied once.
+* MTP IndexShare: Modifications, "MTP / EAGLE", and the chain-EAGLE commit
+  note name an option that shares the index across MTP iterations; read here
+  as one top-k list, selected for a chain's first draft row, attended by every
+  row of the chain (``decode_step_index_share``).
 
 The pages never print the formulas.  The readings taken here are the plainest
 ones consistent with the configurations: indexer score
@@ -564,6 +568,46 @@ def decode_step(inp: dict, n_index_splits: int = 1, n_attn_splits: int = 1,
     return {"q_code": q_code, "q_scale": q_scale, "scores": scores,
             "topk_idx": idx, "topk_count": cnt, "part_o": part_o,
             "part_lse": part_lse, "out": out, "lse": lse}
+
+
+def decode_step_index_share(inp: dict, chain: int, n_index_splits: int = 1, n_attn_splits: int = 1) -> dict:
+    """MTP IndexShare: one top-k list for a chain of draft rows.
+
+    Subject page, Modifications, "MTP / EAGLE" and the chain-EAGLE commit
+    note: the draft runs five steps with six draft tokens, and the option
+    that shares the index across MTP iterations is named (it is switched off
+    under DCP only because a rank there holds just its owned share of the
+    top-k).  The page does not spell out what is shared; the reading taken
+    here is the plainest one: the rows of one request's chain (``chain``
+    consecutive rows, the chain's draft iterations in order, each seeing
+    one more slot than the one before) run the indexer and the top-k once,
+    for the chain's first row, and every row of the chain attends that one
+    list with its own query.  The first row sees the fewest slots, so every
+    entry of its list lies inside every later row's span.
+
+    Returns the leads' scores and selection, the list each row attends
+    (``row_list``, an index into the leads) and every row's merged output.
+    """
+    row_req = np.asarray(inp["row_req"], dtype=np.int64)
+    row_vis = np.asarray(inp["row_vis"], dtype=np.int64)
+    n_rows = len(row_req)
+    if chain < 1 or n_rows % chain != 0:
+        raise ValueError("the rows must form whole chains")
+    lead = np.arange(0, n_rows, chain)
+    row_list = np.arange(n_rows) // chain
+    if np.any(row_req != row_req[lead][row_list]):
+        raise ValueError("every row of a chain must belong to the chain's request")
+    if np.any(row_vis < row_vis[lead][row_list]):
+        raise ValueError("no row of a chain may see fewer slots than its first row")
+    sel = decode_step(inp, n_index_splits, n_attn_splits, rows=lead)
+    idx = sel["topk_idx"][row_list]
+    cnt = sel["topk_count"][row_list]
+    part_o, part_lse = sparse_mla(inp["q_mla"], inp["kv_code"], inp["kv_scale"], inp["page_table"], row_req,
+                                  idx, cnt, float(inp["sm_scale"]), n_attn_splits, int(inp["page_size"]))
+    out, lse = lse_merge(part_o, part_lse)
+    return {"lead_rows": lead, "row_list": row_list, "q_code": sel["q_code"], "q_scale": sel["q_scale"],
+            "scores": sel["scores"], "topk_idx": sel["topk_idx"], "topk_count": sel["topk_count"],
+            "out": out, "lse": lse}
 
 
 def sm_scale_default() -> float:
