@@ -94,6 +94,15 @@ def algorithmic_bytes(inp) -> dict:
     """
     vis = inp.row_vis.cpu().tolist()
     p, k, h, g = inp.page_size, inp.top_k, inp.mla_heads, inp.cfg.group_rows
+    c = inp.cfg.index_share
+    if c > 1:
+        # MTP IndexShare: only each chain's first row is scored, and the
+        # chain's rows attend one list, whose rows count once per chain.
+        lead = vis[::c]
+        keys = sum(132 * m + 4 * math.ceil(m / p) for m in lead)
+        idx = keys + len(lead) * (64 * 128 * 2 + 64 * 4)
+        mla = sum(580 * min(v, k) for v in lead) + len(vis) * (h * 576 * 2 + h * 512 * 2 + h * 4)
+        return {"step": idx + mla, "index_kernel": idx, "index_flops": sum(2 * 64 * 128 * v for v in lead)}
     keys = sum(132 * m + 4 * math.ceil(m / p) for m in (max(vis[i:i + g]) for i in range(0, len(vis), g)))
     idx = keys + len(vis) * (64 * 128 * 2 + 64 * 4)
     mla = sum(580 * min(v, k) + h * 576 * 2 + h * 512 * 2 + h * 4 for v in vis)
@@ -354,14 +363,22 @@ def main():
     def kernel_launches(i, st):
         fns = {
             "index_scores": lambda: dsa.index_scores(
-                i.q_idx, i.head_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
-                i.row_req, i.row_vis, group_rows=st.group_rows, score_stride=st.score_stride,
+                st.lead_q, st.lead_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
+                st.lead_req, st.lead_vis, group_rows=st.group_rows, score_stride=st.score_stride,
                 scores=st.scores, status=st.status),
-            "topk": lambda: dsa.topk(st.scores, i.row_vis, i.top_k, st.index_splits,
+            "topk": lambda: dsa.topk(st.scores, st.lead_vis, i.top_k, st.index_splits,
                                      workspace=st.workspace, topk_idx=st.topk_idx,
                                      topk_count=st.topk_count, status=st.status),
         }
-        if st.attn_splits == 1:
+        if st.row_list is not None:
+            s_ = st.attn_splits
+            fns["sparse_mla"] = lambda: dsa.sparse_mla_decode_shared(
+                i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis, st.row_list, st.topk_idx,
+                st.topk_count, s_, i.sm_scale, part_o=st.part_o, part_lse=st.part_lse, out=st.out,
+                out_lse=st.out_lse, status=st.status)
+            if s_ > 1:
+                fns["lse_merge"] = lambda: dsa.lse_merge(st.part_o, st.part_lse, out=st.out, out_lse=st.out_lse)
+        elif st.attn_splits == 1:
             fns["sparse_mla"] = lambda: dsa.sparse_mla_decode(
                 i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
                 st.topk_idx, st.topk_count, 1, i.sm_scale, out=st.out, out_lse=st.out_lse,

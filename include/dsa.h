@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 7
+#define DSA_ABI_VERSION 8
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -290,6 +290,32 @@ int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int3
                           int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
                           float* part_o, float* part_lse, uint16_t* out, float* out_lse,
                           int32_t* status, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_decode_shared -- dsa_sparse_mla_decode where rows share
+ * selected lists (subject page, Modifications, "MTP / EAGLE", and the
+ * chain-EAGLE commit note: the index can be shared across MTP iterations,
+ * an option the page switches off only under DCP).  The chain of draft rows
+ * of one request runs the indexer and the top-k once, for its first row,
+ * and every row of the chain attends that list with its own query.
+ * Row r attends list l = row_list[r]: the first topk_count[l] entries of
+ * topk_idx[l], exactly as dsa_sparse_mla_decode attends row r's own list
+ * (same splits, outputs, checks).  An entry outside row r's span is left out
+ * (DSA_DEV_TOPK_OOB); a list count above row r's span, or l outside
+ * [0, n_lists), writes row r empty (DSA_DEV_TOPK_OOB / DSA_DEV_ROW_RANGE).
+ *   row_list [n_rows] i32; topk_idx [n_lists, top_k] i32; topk_count
+ *   [n_lists] i32; every other argument as dsa_sparse_mla_decode.
+ * When n_lists divides n_rows into chains of 2..16 consecutive rows, each
+ * chain's work runs on one XCD of the chip, so the rows it shares are read
+ * from HBM about once; any row_list gives the same results.
+ */
+int dsa_sparse_mla_decode_shared(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
+                                 const int32_t* row_req, const int32_t* row_vis, const int32_t* row_list,
+                                 const int32_t* topk_idx, const int32_t* topk_count, int32_t n_lists,
+                                 int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
+                                 int32_t page_size, int32_t n_heads, int32_t top_k, int32_t n_splits,
+                                 float sm_scale, float* part_o, float* part_lse, uint16_t* out, float* out_lse,
+                                 int32_t* status, hipStream_t stream);
 
 /*
  * dsa_lse_merge -- merge split partials by their natural-log LSE (subject

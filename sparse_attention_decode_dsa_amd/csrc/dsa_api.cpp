@@ -38,6 +38,43 @@ size_t topk_ws_keys(int32_t n_rows, int32_t top_k, int32_t n_splits) {
     return (size_t)n_rows * n_splits * top_k * sizeof(uint32_t);
 }
 
+// Validation and launch shared by the attention entry points: row r attends
+// list row_list[r] of [n_lists, top_k] (row_list NULL: list r, n_lists ==
+// n_rows).
+int mla_checked(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table, const int32_t* row_req,
+                const int32_t* row_vis, const int32_t* row_list, const int32_t* topk_idx,
+                const int32_t* topk_count, int32_t n_lists, int32_t n_rows, int32_t batch, int32_t num_pages,
+                int32_t max_pages, int32_t page_size, int32_t n_heads, int32_t top_k, int32_t n_splits,
+                float sm_scale, float* part_o, float* part_lse, uint16_t* out, float* out_lse, int32_t* status,
+                hipStream_t stream) {
+    if (n_rows < 0 || n_rows > kMaxRows || n_heads < 1) return DSA_ERR_SHAPE;
+    if (top_k < 1 || top_k > dsa::kTopkMaxK) return DSA_ERR_SHAPE;
+    if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
+    if (!isfinite(sm_scale)) return DSA_ERR_SHAPE;
+    if (n_heads != 16 && n_heads != 32) return DSA_ERR_UNSUPPORTED;
+    int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
+    if (rc != DSA_OK) return rc;
+    if (!q || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx ||
+        !topk_count || !status)
+        return DSA_ERR_NULL;
+    if (n_splits == 1 ? !out : (!part_o || !part_lse)) return DSA_ERR_NULL;
+    if (n_rows == 0) return DSA_OK;
+    dsa::MlaArgs a;
+    a.q = q; a.kv_cache = kv_cache; a.page_table = page_table;
+    a.row_req = row_req; a.row_vis = row_vis; a.topk_idx = topk_idx; a.topk_count = topk_count;
+    a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
+    a.page_size = page_size; a.log2_page = log2i(page_size); a.n_heads = n_heads;
+    a.top_k = top_k; a.n_splits = n_splits; a.sm_scale = sm_scale;
+    a.part_o = part_o; a.part_lse = part_lse; a.out = out; a.out_lse = out_lse; a.status = status;
+    a.row_list = row_list;
+    a.n_lists = n_lists;
+    // Chains of consecutive rows that share a list go to one XCD each (a
+    // placement only: every row reads its own list index).
+    const int32_t per = n_lists > 0 ? n_rows / n_lists : 0;
+    a.chain = (row_list != nullptr && per > 1 && per <= 16 && n_rows % n_lists == 0) ? per : 1;
+    return launch_status(dsa::launch_sparse_mla(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,26 +201,23 @@ int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int3
                           int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
                           float* part_o, float* part_lse, uint16_t* out, float* out_lse,
                           int32_t* status, hipStream_t stream) {
-    if (n_rows < 0 || n_rows > kMaxRows || n_heads < 1) return DSA_ERR_SHAPE;
-    if (top_k < 1 || top_k > dsa::kTopkMaxK) return DSA_ERR_SHAPE;
-    if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
-    if (!isfinite(sm_scale)) return DSA_ERR_SHAPE;
-    if (n_heads != 16 && n_heads != 32) return DSA_ERR_UNSUPPORTED;
-    int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
-    if (rc != DSA_OK) return rc;
-    if (!q || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx ||
-        !topk_count || !status)
-        return DSA_ERR_NULL;
-    if (n_splits == 1 ? !out : (!part_o || !part_lse)) return DSA_ERR_NULL;
-    if (n_rows == 0) return DSA_OK;
-    dsa::MlaArgs a;
-    a.q = q; a.kv_cache = kv_cache; a.page_table = page_table;
-    a.row_req = row_req; a.row_vis = row_vis; a.topk_idx = topk_idx; a.topk_count = topk_count;
-    a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
-    a.page_size = page_size; a.log2_page = log2i(page_size); a.n_heads = n_heads;
-    a.top_k = top_k; a.n_splits = n_splits; a.sm_scale = sm_scale;
-    a.part_o = part_o; a.part_lse = part_lse; a.out = out; a.out_lse = out_lse; a.status = status;
-    return launch_status(dsa::launch_sparse_mla(a, stream));
+    return mla_checked(q, kv_cache, page_table, row_req, row_vis, nullptr, topk_idx, topk_count, n_rows, n_rows,
+                       batch, num_pages, max_pages, page_size, n_heads, top_k, n_splits, sm_scale, part_o,
+                       part_lse, out, out_lse, status, stream);
+}
+
+int dsa_sparse_mla_decode_shared(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
+                                 const int32_t* row_req, const int32_t* row_vis, const int32_t* row_list,
+                                 const int32_t* topk_idx, const int32_t* topk_count, int32_t n_lists,
+                                 int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
+                                 int32_t page_size, int32_t n_heads, int32_t top_k, int32_t n_splits,
+                                 float sm_scale, float* part_o, float* part_lse, uint16_t* out, float* out_lse,
+                                 int32_t* status, hipStream_t stream) {
+    if (n_lists < 1 || n_lists > kMaxRows) return DSA_ERR_SHAPE;
+    if (!row_list) return DSA_ERR_NULL;
+    return mla_checked(q, kv_cache, page_table, row_req, row_vis, row_list, topk_idx, topk_count, n_lists, n_rows,
+                       batch, num_pages, max_pages, page_size, n_heads, top_k, n_splits, sm_scale, part_o,
+                       part_lse, out, out_lse, status, stream);
 }
 
 int dsa_lse_merge(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,

@@ -155,9 +155,26 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     const int g = lane >> 4;
     const int hb = wv % HB;         // head block of this wavefront in QK
     const int tbk = wv / HB;        // its token block: tokens [16 tbk, 16 tbk + 16) of a tile
-    const int r = blockIdx.y;
-    const int sp = blockIdx.x;
-    const int ns = gridDim.x;
+    const int ns = a.n_splits;
+    int r, sp;
+    if (a.chain > 1) {
+        // Chains on XCDs: workgroup L runs on XCD L % 8 (the dispatcher deals
+        // workgroups out to the XCDs in turn); XCD x takes chains x, x + 8,
+        // ... one after the other, all (row, split) units of a chain in a
+        // row, so the chain's shared rows are fetched into that XCD's L2
+        // once.  Padding units past the last chain do nothing.
+        const int L = blockIdx.x;
+        const int per_chain = a.chain * ns;
+        const int j = L >> 3;
+        const int c = ((j / per_chain) << 3) | (L & 7);
+        const int u = j % per_chain;
+        if (c * a.chain >= a.n_rows) return;
+        r = c * a.chain + u / ns;
+        sp = u % ns;
+    } else {
+        r = blockIdx.y;
+        sp = blockIdx.x;
+    }
 
     // The bf16 query of the row, gathered like a tile (lane i of load j
     // fills chunk 64 j + i of the staging rows; the pad chunk rereads chunk
@@ -179,11 +196,15 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     // loaded together with the metadata.
     const int b_raw = a.row_req[r];
     const int v_raw = a.row_vis[r];
-    const int c_raw = a.topk_count[r];
+    // The list this row attends: its own, or the shared one row_list names.
+    const int list_raw = a.row_list != nullptr ? a.row_list[r] : r;
+    const bool list_ok = list_raw >= 0 && list_raw < a.n_lists;
+    const int list = list_ok ? list_raw : 0;
+    const int c_raw = a.topk_count[list];
     const int chunk = (a.top_k + ns - 1) / ns;
     const int lo = min(a.top_k, sp * chunk);
     const int hi_list = min(a.top_k, lo + chunk);
-    const int32_t* sel = a.topk_idx + (size_t)r * a.top_k;
+    const int32_t* sel = a.topk_idx + (size_t)list * a.top_k;
 
     // First batch of list entries (8 per thread), issued before anything
     // else; indexes are clamped into the list.
@@ -196,7 +217,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     };
     load_slots(lo);
 
-    bool ok = b_raw >= 0 && b_raw < a.batch && v_raw >= 0 && v_raw <= a.max_pages * a.page_size;
+    bool ok = b_raw >= 0 && b_raw < a.batch && v_raw >= 0 && v_raw <= a.max_pages * a.page_size && list_ok;
     if (!ok && tid == 0) flag(a.status, DSA_DEV_ROW_RANGE);
     if (ok && (c_raw < 0 || c_raw > a.top_k || c_raw > v_raw)) {
         if (tid == 0) flag(a.status, DSA_DEV_TOPK_OOB);
@@ -490,7 +511,15 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
 
 template <int HB, int NB>
 hipError_t launch_hb(const MlaArgs& a, hipStream_t stream) {
-    sparse_mla_kernel<HB, NB><<<dim3(a.n_splits, a.n_rows), 256 * HB, 0, stream>>>(a);
+    if (a.chain > 1) {
+        // Whole groups of eight chains (one per XCD), padded.
+        const int64_t chains = (a.n_rows / a.chain + 7) / 8 * 8;
+        const int64_t wgs = chains * a.chain * a.n_splits;
+        if (wgs > INT32_MAX) return hipErrorInvalidValue;
+        sparse_mla_kernel<HB, NB><<<(unsigned)wgs, 256 * HB, 0, stream>>>(a);
+    } else {
+        sparse_mla_kernel<HB, NB><<<dim3(a.n_splits, a.n_rows), 256 * HB, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

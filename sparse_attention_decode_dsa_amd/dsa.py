@@ -17,7 +17,7 @@ import os
 
 import torch
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE", 64: "SCALE"}
@@ -42,6 +42,8 @@ _SIGS = {
     "dsa_topk_noalloc": ([_p, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p], ctypes.c_int),
     "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
+    "dsa_sparse_mla_decode_shared": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "dsa_lse_merge": ([_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_lse_merge_project": ([_p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_cache_write": ([_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
@@ -242,6 +244,47 @@ def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_
     return part_o, part_lse, status
 
 
+def sparse_mla_decode_shared(q, kv_cache, page_table, row_req, row_vis, row_list, topk_idx, topk_count,
+                             n_splits: int = 1, sm_scale: float = 1.0 / 24.0, part_o=None, part_lse=None,
+                             out=None, out_lse=None, status=None, stream=None):
+    """sparse_mla_decode where row r attends list row_list[r] of topk_idx
+    [n_lists, k] / topk_count [n_lists] (MTP IndexShare).  Returns as
+    sparse_mla_decode."""
+    r, h, dq = q.shape
+    n_pages, p, row_bytes = kv_cache.shape
+    if row_bytes != 640:
+        raise DsaError(f"kv_cache rows must be 640 bytes, got {row_bytes}")
+    batch, max_pages = page_table.shape
+    n_lists, top_k = topk_idx.shape
+    dev = q.device
+    if status is None:
+        status = new_status(dev)
+    if n_splits == 1:
+        if out is None:
+            out = torch.empty((r, h, 512), dtype=torch.bfloat16, device=dev)
+        if out_lse is None:
+            out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
+    else:
+        if part_o is None:
+            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
+    _check(lib().dsa_sparse_mla_decode_shared(
+        _ptr(q, _BF16, "q"), _ptr(kv_cache, torch.uint8, "kv_cache"),
+        _ptr(page_table, torch.int32, "page_table"), _ptr(row_req, torch.int32, "row_req"),
+        _ptr(row_vis, torch.int32, "row_vis"), _ptr(row_list, torch.int32, "row_list"),
+        _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_count, torch.int32, "topk_count"), n_lists,
+        r, batch, n_pages, max_pages, p, h, top_k, n_splits, float(sm_scale),
+        _ptr(part_o, torch.float32, "part_o") if n_splits > 1 else None,
+        _ptr(part_lse, torch.float32, "part_lse") if n_splits > 1 else None,
+        _ptr(out, _BF16, "out") if n_splits == 1 else None,
+        _ptr(out_lse, torch.float32, "out_lse") if n_splits == 1 else None,
+        _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_sparse_mla_decode_shared")
+    if n_splits == 1:
+        return out, out_lse, status
+    return part_o, part_lse, status
+
+
 def lse_merge(part_o, part_lse, out=None, out_lse=None, stream=None):
     """Merge split partials -> (out bf16 [R,H,512], out_lse f32 [R,H])."""
     r, h, s, dv = part_o.shape
@@ -303,23 +346,41 @@ class DecodeStep:
     (else the current) stream without allocating or synchronising."""
 
     def __init__(self, inp, index_splits: int | None = None, attn_splits: int | None = None,
-                 group_rows: int | None = None, score_stride: int | None = None):
+                 group_rows: int | None = None, score_stride: int | None = None,
+                 index_share: int | None = None):
         self.inp = inp
         cfg = inp.cfg
         self.index_splits = index_splits or cfg.index_splits
         self.attn_splits = attn_splits or cfg.attn_splits
         self.group_rows = group_rows or cfg.group_rows
+        # MTP IndexShare: chains of `index_share` consecutive rows; only each
+        # chain's first row is scored and selected, and every row attends
+        # that list.  The first rows' inputs are gathered once, here.
+        self.index_share = index_share if index_share is not None else cfg.index_share
         dev = inp.q_idx.device
         r = inp.n_rows
         h = inp.mla_heads
         k = inp.top_k
+        if self.index_share > 1:
+            c = self.index_share
+            if r % c or self.group_rows != 1:
+                raise DsaError("index sharing needs whole chains and one row per scoring group")
+            self.lead_q = inp.q_idx[::c].contiguous()
+            self.lead_w = inp.head_w[::c].contiguous()
+            self.lead_req = inp.row_req[::c].contiguous()
+            self.lead_vis = inp.row_vis[::c].contiguous()
+            self.row_list = (torch.arange(r, device=dev, dtype=torch.int32) // c).contiguous()
+        else:
+            self.lead_q, self.lead_w, self.lead_req, self.lead_vis = inp.q_idx, inp.head_w, inp.row_req, inp.row_vis
+            self.row_list = None
+        n_sel = self.lead_q.shape[0]
         # Rows start 16-byte aligned (the top-k then reads them in 16-byte loads).
-        self.score_stride = score_stride or max(64, (inp.max_vis() + 63) // 64 * 64)
-        self.scores = torch.empty((r, self.score_stride), dtype=torch.float32, device=dev)
-        need = topk_workspace_size(r, k, self.index_splits)
+        self.score_stride = score_stride or max(64, (int(self.lead_vis.max()) + 63) // 64 * 64)
+        self.scores = torch.empty((n_sel, self.score_stride), dtype=torch.float32, device=dev)
+        need = topk_workspace_size(n_sel, k, self.index_splits)
         self.workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-        self.topk_idx = torch.empty((r, k), dtype=torch.int32, device=dev)
-        self.topk_count = torch.empty((r,), dtype=torch.int32, device=dev)
+        self.topk_idx = torch.empty((n_sel, k), dtype=torch.int32, device=dev)
+        self.topk_count = torch.empty((n_sel,), dtype=torch.int32, device=dev)
         s = self.attn_splits
         self.part_o = torch.empty((r, h, s, 512), dtype=torch.float32, device=dev) if s > 1 else None
         self.part_lse = torch.empty((r, h, s), dtype=torch.float32, device=dev) if s > 1 else None
@@ -329,12 +390,21 @@ class DecodeStep:
 
     def run(self, stream=None):
         i = self.inp
-        index_scores(i.q_idx, i.head_w, i.k_code, i.k_scale, i.page_table,
-                     i.kv_lens, i.row_req, i.row_vis, group_rows=self.group_rows,
+        index_scores(self.lead_q, self.lead_w, i.k_code, i.k_scale, i.page_table,
+                     i.kv_lens, self.lead_req, self.lead_vis, group_rows=self.group_rows,
                      score_stride=self.score_stride, scores=self.scores, status=self.status,
                      stream=stream)
-        topk(self.scores, i.row_vis, i.top_k, self.index_splits, workspace=self.workspace,
+        topk(self.scores, self.lead_vis, i.top_k, self.index_splits, workspace=self.workspace,
              topk_idx=self.topk_idx, topk_count=self.topk_count, status=self.status, stream=stream)
+        if self.row_list is not None:
+            s = self.attn_splits
+            sparse_mla_decode_shared(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
+                                           self.row_list, self.topk_idx, self.topk_count, s, i.sm_scale,
+                                           part_o=self.part_o, part_lse=self.part_lse, out=self.out,
+                                           out_lse=self.out_lse, status=self.status, stream=stream)
+            if s > 1:
+                lse_merge(self.part_o, self.part_lse, out=self.out, out_lse=self.out_lse, stream=stream)
+            return self.out, self.out_lse
         if self.attn_splits == 1:
             sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req,
                               i.row_vis, self.topk_idx, self.topk_count, 1, i.sm_scale, out=self.out,

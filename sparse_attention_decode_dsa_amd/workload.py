@@ -71,6 +71,7 @@ class Config:
     planted: int = 0                      # boosted slots per request
     planted_factor: float = 8.0
     group_rows: int = 1                   # rows scored together against one key stream
+    index_share: int = 0                  # MTP IndexShare: rows per chain sharing one top-k list
 
 
 CONFIGS = {
@@ -89,6 +90,11 @@ CONFIGS = {
     # MTP verify: 6 causal rows per request.
     "c3": Config("c3", batch=32, kv_range=(16384, 65536), rows_per_req=6, causal="mtp",
                  mla_heads=32, index_splits=2, attn_splits=1, group_rows=6),
+    # MTP draft chains with IndexShare: the MTP-verify geometry (32 requests x
+    # 6 causal rows), the indexer and top-k run on each chain's first row
+    # only, and all six rows attend that row's list.
+    "c3s": Config("c3s", batch=32, kv_range=(16384, 65536), rows_per_req=6, causal="mtp",
+                  mla_heads=32, index_splits=2, attn_splits=1, index_share=6),
     # Long-prefix prefill on the owned top-k path: 4096 new rows after 65536.
     # Five index splits keep each split's list (69632 / 5 scores) within 16
     # keys a thread.

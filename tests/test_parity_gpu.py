@@ -609,3 +609,126 @@ def test_bad_scales_are_reported_and_left_out():
                               f_cnt, inp.sm_scale, 1, inp.page_size)
     r_out, r_lse = O.lse_merge(r_po, r_pl)
     check_out(bf16_to_f64(out), lse.cpu().double().numpy(), r_out, r_lse)
+
+
+# ------------------------------------------------------------------ MTP IndexShare
+
+def compare_index_share(inp, step, chains):
+    """Oracle IndexShare step on whole chains `chains` vs the GPU step: the
+    chains' first rows' scores and selections, then every row's output.  A
+    chain whose selection differs inside the tie band is compared with the
+    oracle's attention over the GPU's selection."""
+    c = step.index_share
+    rows = [ch * c + i for ch in chains for i in range(c)]
+    sub = W.subset(inp, rows)
+    sub_np = W.as_numpy(sub)
+    ref = O.decode_step_index_share(sub_np, c, step.index_splits, step.attn_splits)
+    lead_vis = sub.row_vis.numpy()[::c]
+    g_scores = step.scores[chains].cpu().double().numpy()
+    r_scores = np.full_like(g_scores, -np.inf)
+    r_scores[:, :ref["scores"].shape[1]] = ref["scores"]
+    lead_np = dict(sub_np, row_req=sub_np["row_req"][::c], row_vis=sub_np["row_vis"][::c],
+                   head_w=sub_np["head_w"][::c])
+    mags = score_magnitudes(lead_np, ref["q_code"], ref["q_scale"])
+    ulps = check_scores(g_scores, r_scores, lead_vis, mags, 128 + 64 + 2)
+    say(f"  lead scores: max err {ulps:.2f} u*A")
+    g_idx = step.topk_idx[chains].cpu().numpy()
+    g_cnt = step.topk_count[chains].cpu().numpy()
+    out_cmp, lse_cmp = ref["out"].copy(), ref["lse"].copy()
+    swapped = []
+    for j in range(len(chains)):
+        if check_topk_row(g_idx[j], g_cnt[j], ref["topk_idx"][j], ref["topk_count"][j], ref["scores"][j],
+                          lead_vis[j], inp.top_k):
+            swapped.append(chains[j])
+            ch_rows = list(range(j * c, (j + 1) * c))
+            o, l = oracle_on_selection(sub_np, ch_rows, np.repeat(g_idx, c, 0), np.repeat(g_cnt, c, 0),
+                                       step.attn_splits)
+            out_cmp[ch_rows], lse_cmp[ch_rows] = o, l
+    g_out = bf16_to_f64(step.out[rows])
+    g_lse = step.out_lse[rows].cpu().double().numpy()
+    for i in range(len(rows)):
+        check_out(g_out[i], g_lse[i], out_cmp[i], lse_cmp[i])
+    return swapped
+
+
+@pytest.mark.parametrize("splits", [None, (4, 3)])
+def test_index_share_chains_match_oracle(splits):
+    """32 requests x 6 causal draft rows: the indexer and top-k run on each
+    chain's first row, every row attends that list (chains placed on one
+    XCD each); sampled chains 0, 13 and 31 against the oracle."""
+    inp = W.make("c3s", device="cuda")
+    step = dsa.DecodeStep(inp, *(splits or (None, None)))
+    step.run()
+    torch.cuda.synchronize()
+    dsa.check_status(step.status)
+    say(f"c3s: R={inp.n_rows} chains={inp.n_rows // step.index_share} splits=({step.index_splits},{step.attn_splits})")
+    swapped = compare_index_share(inp, step, [0, 13, 31])
+    say(f"c3s: swapped {swapped}")
+
+
+def test_index_share_edge_chains_match_oracle():
+    """Short chains on small pages: spans from 2 tokens, k above the first
+    row's span, 16 heads, chains of 3, one and four attention splits."""
+    cfg = W.Config("edge_share", batch=5, kv_lens=(3, 40, 300, 2100, 2500), rows_per_req=3, causal="mtp",
+                   page_size=16, mla_heads=16, index_splits=1, attn_splits=4, index_share=3)
+    inp = W.to(W.make(cfg), "cuda")
+    for splits in ((1, 4), (2, 1)):
+        step = dsa.DecodeStep(inp, *splits)
+        step.run()
+        torch.cuda.synchronize()
+        dsa.check_status(step.status)
+        compare_index_share(inp, step, list(range(inp.n_rows // 3)))
+
+
+def test_shared_lists_in_any_order_and_bad_list_ids():
+    """row_list in an arbitrary order (no chains: the plain grid) gives each
+    row the oracle's attention over its list; a list id out of range writes
+    the row empty with DSA_DEV_ROW_RANGE; a list whose entries reach past a
+    shorter row's span leaves those entries out with DSA_DEV_TOPK_OOB."""
+    inp = W.to(W.make("c0"), "cuda")
+    good = run_step(inp, 1, 1)
+    # Lists: row 0's and row 1's own, in a shuffled map over 5 query rows of
+    # request 1 (each row sees all of request 1's slots).
+    rr = torch.tensor([1, 1, 1, 1, 1], dtype=torch.int32, device="cuda")
+    rv = torch.full((5,), int(inp.kv_lens[1]), dtype=torch.int32, device="cuda")
+    q = inp.q_mla[torch.tensor([1, 0, 1, 0, 1], device="cuda")].contiguous()
+    row_list = torch.tensor([1, 0, 1, 1, 0], dtype=torch.int32, device="cuda")
+    st = dsa.new_status()
+    out, lse, _ = dsa.sparse_mla_decode_shared(q, inp.kv_cache, inp.page_table, rr, rv, row_list, good.topk_idx,
+                                               good.topk_count, 1, inp.sm_scale, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    n = W.as_numpy(W.subset(inp, [0, 1]))
+    rl = row_list.cpu().numpy()
+    idx = good.topk_idx.cpu().numpy()[rl]
+    cnt = good.topk_count.cpu().numpy()[rl]
+    # request 1 is the subset's request 1; row 0's list (slots < 1500) lies inside its span
+    qn = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    r_po, r_pl = O.sparse_mla(qn, n["kv_code"], n["kv_scale"], n["page_table"], np.ones(5, dtype=np.int64), idx,
+                              cnt, inp.sm_scale, 1, inp.page_size)
+    r_out, r_lse = O.lse_merge(r_po, r_pl)
+    check_out(bf16_to_f64(out), lse.cpu().double().numpy(), r_out, r_lse)
+    # A list id out of range: that row only is empty.
+    bad_list = torch.tensor([1, 0, 7, 1, -1], dtype=torch.int32, device="cuda")
+    st = dsa.new_status()
+    out2, lse2, _ = dsa.sparse_mla_decode_shared(q, inp.kv_cache, inp.page_table, rr, rv, bad_list,
+                                                 good.topk_idx, good.topk_count, 1, inp.sm_scale, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == dsa.DEV_ROW_RANGE
+    for i in (2, 4):
+        assert torch.all(out2[i] == 0) and torch.all(torch.isneginf(lse2[i]))
+    for i in (0, 1, 3):
+        assert torch.equal(out2[i], out[i])
+    # Request 0's rows (span 1500) attending request 1's list (2048 slots of
+    # 5000): the count exceeds the span, so the row is written empty.
+    rr0 = torch.zeros(2, dtype=torch.int32, device="cuda")
+    rv0 = torch.full((2,), 1500, dtype=torch.int32, device="cuda")
+    st = dsa.new_status()
+    out3, lse3, _ = dsa.sparse_mla_decode_shared(inp.q_mla[:1].repeat(2, 1, 1).contiguous(), inp.kv_cache,
+                                                 inp.page_table, rr0, rv0,
+                                                 torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
+                                                 good.topk_idx, good.topk_count, 1, inp.sm_scale, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & dsa.DEV_TOPK_OOB
+    assert torch.equal(out3[0], good.out[0])
+    assert torch.all(out3[1] == 0) and torch.all(torch.isneginf(lse3[1]))
