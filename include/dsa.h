@@ -205,8 +205,9 @@ int dsa_index_scores(const uint16_t* q, const float* head_w,
                      float* scores, int32_t score_stride, int32_t* status, hipStream_t stream);
 
 /*
- * Workspace bytes dsa_topk needs for n_splits > 1: candidate keys and slots,
- * n_splits * top_k of each per row.  0 when n_splits == 1.  The caller
+ * Workspace bytes dsa_topk needs for n_splits > 1: room for top_k candidate
+ * keys and slots per split and row, and one count per split and row.  0 when
+ * n_splits == 1.  The caller
  * reserves the workspace once, up front, and a call with a smaller one is
  * rejected (DSA_ERR_WORKSPACE) rather than served by an allocation (page
  * "Harden DeepSeek V4 DSpark DP2 serving", section 6.3: workspaces reserved
@@ -219,10 +220,16 @@ size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits);
  * slot ascending), so equal scores keep the lower slot (subject page,
  * Motivation: the top 2048 of the whole sequence; Modifications, indexer
  * decode: local top-k per shard merged into the exact global top-k).
- * Row r's slots [0, row_vis[r]) are cut into n_splits contiguous ranges of
+ * n_splits == 1 selects directly, one workgroup per row.  n_splits > 1 cuts
+ * row r's slots [0, row_vis[r]) into n_splits contiguous ranges of
  * ceil(row_vis/n_splits) rounded up to a multiple of 4 (the last ranges may
- * be short or empty); each keeps its top-min(top_k, len) candidates and one
- * merge keeps the top-k of their union.  n_splits == 1 selects directly.
+ * be short or empty), one workgroup each.  Each range keeps its candidates:
+ * the scores at or above one cut that every range of the row derives alike
+ * from a strided sample of the whole row, or its own top top_k when more
+ * than top_k of its scores pass the cut.  One merge per row selects the top
+ * top_k of the candidates, which is the row's top top_k whenever at least
+ * top_k are kept; when the cut kept fewer, the merge selects from the row's
+ * scores directly (slower, same result).
  * Score rows whose start is 16-byte aligned (score_stride a multiple of 4)
  * are read in 16-byte loads; nothing outside [0, row_vis) of a row is used,
  * and nothing past the row's score_stride entries is read.

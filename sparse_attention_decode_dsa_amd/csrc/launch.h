@@ -29,8 +29,11 @@ struct TopkArgs {
     int32_t score_stride;
     const int32_t* row_vis;
     int32_t n_rows, top_k, n_splits;
-    uint32_t* cand_key;   // [n_rows, n_splits * top_k]: a row's candidates, first to last split
-    int32_t* cand_slot;   // [n_rows, n_splits * top_k]
+    uint32_t* cand_key;   // [n_rows, n_splits, top_k]: each split's kept keys, at the front of its block
+    int32_t* cand_slot;   // [n_rows, n_splits, top_k]: their slots
+    int32_t* cand_count;  // [n_rows, n_splits]: how many each split kept
+    int32_t* cand_cut;    // [n_rows, n_splits]: the row's cut key, as each split used it
+    int32_t* cand_hist;   // [n_rows, n_splits, 512]: histogram of each split's kept keys
     int32_t* topk_idx;
     int32_t* topk_count;
     int32_t* status;

@@ -68,6 +68,11 @@ struct TopkSmem {
         } sel;
     } u;
     uint32_t h0[kBins0];   // sample histogram, cleared before the list is staged
+    uint32_t khist[512];   // filter pass: histogram of the kept keys above the cut
+    uint32_t bkey[kWave];  // merge: the keys of the threshold bin, and the threshold found among them
+    uint32_t bcount;
+    uint32_t sel_thr;
+    uint32_t sel_need_eq;
     uint32_t scan[2][kThreads / kWave + 1];
     uint32_t sel_digit;
     uint32_t sel_digit2;
@@ -514,52 +519,21 @@ __device__ __forceinline__ SplitRange split_range(int v, int ns, int j) {
     return {lo, min(v, lo + c)};
 }
 
-// Candidates that the splits before split j of a row put in the workspace
-// (each keeps min(its length, k)); with j = n_splits, the row's total.
-__device__ __forceinline__ int candidates_before(int v, int ns, int j, int k) {
-    int o = 0;
-    for (int i = 0; i < j; ++i) {
-        const SplitRange sr = split_range(v, ns, i);
-        o += min(sr.hi - sr.lo, k);
-    }
-    return o;
-}
-
-// One split, or the whole row: grid (n_splits, n_rows); no list is longer
-// than P keys per thread.
+// Whole row, one split: grid (1, n_rows); no row is longer than P keys per
+// thread.
 template <int P>
-__global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kThreads) void topk_direct_kernel(TopkArgs a) {
     __shared__ TopkSmem s;
     const int r = blockIdx.y;
-    const int j = blockIdx.x;
-    const int v = checked_vis(a, r);
-    const SplitRange sr = split_range(v, a.n_splits, j);
-    const int lo = sr.lo;
-    const int n = sr.hi - sr.lo;
+    const int n = checked_vis(a, r);
     const int k = a.top_k;
-    const bool direct = a.n_splits == 1;
-    // Output pointers are formed where they are used, so that they are not
-    // held across the selection.
-    auto cand_at = [&]() { return (size_t)r * a.n_splits * k + candidates_before(v, a.n_splits, j, k); };
-    if (direct && threadIdx.x == 0) a.topk_count[r] = min(n, k);
-    const float* src = a.scores + (size_t)r * a.score_stride + lo;
+    if (threadIdx.x == 0) a.topk_count[r] = min(n, k);
+    const float* src = a.scores + (size_t)r * a.score_stride;
+    int32_t* out_idx = a.topk_idx + (size_t)r * k;
     if (n <= k) {
-        // Everything in the range is selected.
-        if (direct) {
-            int32_t* out_idx = a.topk_idx + (size_t)r * k;
-            for (int i = threadIdx.x; i < n; i += kThreads) out_idx[i] = lo + i;
-            pad_tail(out_idx, n, k);
-        } else {
-            const size_t at = cand_at();
-            bool nan = false;
-            for (int i = threadIdx.x; i < n; i += kThreads) {
-                const float f = src[i];
-                nan |= (f != f);
-                a.cand_slot[at + i] = lo + i;
-                a.cand_key[at + i] = monotone_key(f);
-            }
-            if (__ballot(nan) != 0ull && (threadIdx.x & 63) == 0) flag(a.status, DSA_DEV_NAN);
-        }
+        // Everything visible is selected.
+        for (int i = threadIdx.x; i < n; i += kThreads) out_idx[i] = i;
+        pad_tail(out_idx, n, k);
         return;
     }
     const int per = keys_per_thread(n);
@@ -574,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
     for (int i = threadIdx.x; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
     // 16-byte loads read whole chunks, so the last one may reach up to three
     // floats past the list: taken only where those stay inside the row.
-    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && lo + ((n + 3) & ~3) <= a.score_stride) {
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && ((n + 3) & ~3) <= a.score_stride) {
         load_list_vec<P, true>(s, src, n, base, mine, key, nan);
     } else {
         load_list<P>(s, n, base, mine, key, [&](int i) {
@@ -589,60 +563,438 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a) {
     select_kth<P>(s, key, mine, n, k, &thr, &need, tog);
     // A right selection takes exactly k keys; ranks are clamped below k so
     // that a wrong one could not write past the buffers.
-    if (direct) {
-        emit_direct<P>(s, key, base, thr, need, k, a.topk_idx + (size_t)r * k, lo, tog);
-    } else {
-        emit_to_lds<P>(s, key, base, thr, need, k, tog);
-        __syncthreads();
-        const size_t at = cand_at();
-        for (int i = threadIdx.x; i < k; i += kThreads) {
-            a.cand_slot[at + i] = lo + (int)s.u.stage[kEmitPos + i];
-            a.cand_key[at + i] = s.u.stage[kEmitKey + i];
-        }
-    }
+    emit_direct<P>(s, key, base, thr, need, k, out_idx, 0, tog);
 }
 
-// Merge of the split candidates of one row: grid (n_rows).  The row's
-// candidates are the first n entries of its workspace block, in split order
-// (n <= n_splits * k, at most P keys per thread).
+// ---------------------------------------------------------------------------
+// Several workgroups per row: a filter pass and an exact merge.
+//
+// A row's top k is a small part of it, so each split of the row keeps only
+// the keys at or above one row-wide cut, estimated from a strided sample of
+// the whole row that every split of the row reads alike: sample position
+// t_i = floor(i * v / S) for i < S = min(512, v).  With rho = k S / v the
+// expected number of sample keys in the top k and sigma = sqrt(rho (1 -
+// rho / S)), the cut is the floor of the 12-bit key bin holding the sample
+// key of rank R = ceil(rho + 4 sigma + 4) from the top (no cut when R > S),
+// so about R v / S keys of the row pass.  A split with more than k keys at
+// or above the cut keeps its exact top k instead.  Every kept key is then
+// at or above the cut, and every dropped key is below it or below k kept
+// keys of its own split, so once at least k keys are kept in total, the top
+// k of the kept keys is the row's top k.  The merge checks that count; when
+// the cut was too high (fewer than k kept) it selects from the whole row,
+// streamed in passes.
+// ---------------------------------------------------------------------------
+
+constexpr int kSample = 512;
+
+// The filter's histogram of its kept keys: bins of 2^16 key values (1/16 of
+// an octave of scores), counted from the cut's bin, the last bin also
+// holding everything above.  Every kept key is at or above the cut.
+constexpr int kHistBins = 512;
+__device__ __forceinline__ int kept_bin(uint32_t key, uint32_t cut) {
+    return (int)min((key >> 16) - (cut >> 16), (uint32_t)(kHistBins - 1));
+}
+
+// R of the cut above, or kSample + 1 for "no cut".
+__device__ __forceinline__ int cut_rank(int v, int k, int S) {
+    if (S <= 0) return kSample + 1;
+    const float rho = (float)k * (float)S / (float)v;
+    const float sigma = sqrtf(fmaxf(rho * (1.0f - rho / (float)S), 0.0f));
+    const int R = (int)ceilf(rho + 4.0f * sigma + 4.0f);
+    return R > S ? kSample + 1 : R;
+}
+
+// Filter pass: grid (n_splits, n_rows).  Split j of row r writes its kept
+// keys and slots, in slot order, at the front of its own block of k entries
+// of the workspace, and their number to cand_count[r][j].
 template <int P>
-__global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
     __shared__ TopkSmem s;
-    const int r = blockIdx.x;
+    const int r = blockIdx.y;
+    const int j = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int v = checked_vis(a, r);
+    const SplitRange sr = split_range(v, a.n_splits, j);
+    const int lo = sr.lo;
+    const int n = sr.hi - sr.lo;
     const int k = a.top_k;
-    const int ns = a.n_splits;
-    int32_t* out_idx = a.topk_idx + (size_t)r * k;
-    const int n = candidates_before(checked_vis(a, r), ns, ns, k);
-    if (threadIdx.x == 0) a.topk_count[r] = min(n, k);
-    const int32_t* cslot = a.cand_slot + (size_t)r * ns * k;
-    const uint32_t* ckey = a.cand_key + (size_t)r * ns * k;
-    if (n <= k) {
-        // Every candidate is selected, in list order.
-        for (int i = threadIdx.x; i < n; i += kThreads) out_idx[i] = cslot[i];
-        pad_tail(out_idx, n, k);
-        return;
-    }
+    const size_t seg = ((size_t)r * a.n_splits + j) * k;
+    const size_t rj = (size_t)r * a.n_splits + j;
+    uint32_t* hist_out = reinterpret_cast<uint32_t*>(a.cand_hist) + rj * kHistBins;
+    const float* row = a.scores + (size_t)r * a.score_stride;
     const int per = keys_per_thread(n);
-    if (per > P) {   // cannot happen: n <= n_splits * k, which the launch bounds
-        if (threadIdx.x == 0) flag(a.status, DSA_DEV_ROW_RANGE);
+    if (n <= 0 || per > P) {   // an empty split (per > P cannot happen: the launch bounds the length)
+        if (per > P && n > 0 && tid == 0) flag(a.status, DSA_DEV_ROW_RANGE);
+        if (tid == 0) {
+            a.cand_count[rj] = 0;
+            a.cand_cut[rj] = 0;
+        }
+        for (int b = tid; b < kHistBins; b += kThreads) hist_out[b] = 0u;
         return;
     }
-    const int base = threadIdx.x * per;
+    // The row sample goes out first.
+    const int S = min(kSample, v);
+    float sf = 0.0f;
+    if (tid < S) sf = row[(int)((int64_t)tid * v / S)];
+    const int base = tid * per;
     const int mine = max(0, min(per, n - base));
     uint32_t key[P];
-    for (int i = threadIdx.x; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
-    if ((reinterpret_cast<uintptr_t>(ckey) & 15) == 0) {
-        bool unused = false;
-        load_list_vec<P, false>(s, ckey, n, base, mine, key, unused);
+    bool nan = false;
+    const float* src = row + lo;
+    for (int i = tid; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
+    for (int i = tid; i < kHistBins; i += kThreads) s.khist[i] = 0u;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && lo + ((n + 3) & ~3) <= a.score_stride) {
+        load_list_vec<P, true>(s, src, n, base, mine, key, nan);
     } else {
-        load_list<P>(s, n, base, mine, key, [&](int i) { return ckey[i]; });
+        load_list<P>(s, n, base, mine, key, [&](int i) {
+            const float f = src[i];
+            nan |= (f != f);
+            return monotone_key(f);
+        });
     }
-    uint32_t thr, need;
+    if (__ballot(nan) != 0ull && (tid & 63) == 0) flag(a.status, DSA_DEV_NAN);
+    // The cut: bin of the sample key of rank R.
     int tog = 0;
+    const int R = cut_rank(v, k, S);
+    uint32_t cut = 0u;
+    if (R <= S) {
+        if (tid < S) atomicAdd(&s.h0[bin0(monotone_key(sf))], 1u);
+        __syncthreads();
+        find_digit<kBins0>(s, s.h0, (uint32_t)R, tog);
+        cut = s.sel_digit << 20;
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) c += (i < mine && key[i] >= cut) ? 1u : 0u;
+    uint32_t total;
+    uint32_t at = scan2(s, c, &total, tog);
+    int32_t* cslot = a.cand_slot + seg;
+    uint32_t* ckey = a.cand_key + seg;
+    if (total <= (uint32_t)k) {
+        // Kept keys in list order into the staging buffer (free: the keys
+        // are in registers), then out in one coalesced pass.
+        pin(cut);
+        const uint32_t dummy = (uint32_t)k + (uint32_t)(tid & (kWave - 1));
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const bool in = i < mine && key[i] >= cut;
+            const uint32_t d = in ? at : dummy;
+            s.u.stage[kEmitPos + d] = (uint32_t)(base + i);
+            s.u.stage[kEmitKey + d] = key[i];
+            if (in) atomicAdd(&s.khist[kept_bin(key[i], cut)], 1u);
+            at += in ? 1u : 0u;
+        }
+        __syncthreads();
+        for (int i = tid; i < (int)total; i += kThreads) {
+            cslot[i] = lo + (int)s.u.stage[kEmitPos + i];
+            ckey[i] = s.u.stage[kEmitKey + i];
+        }
+        for (int b = tid; b < kHistBins; b += kThreads) hist_out[b] = s.khist[b];
+        if (tid == 0) {
+            a.cand_count[rj] = (int)total;
+            a.cand_cut[rj] = (int)cut;
+        }
+        return;
+    }
+    // More than k keys of this split at or above the cut: its exact top k.
+    for (int i = tid; i < kBins0; i += kThreads) s.h0[i] = 0u;
+    __syncthreads();
+    uint32_t thr, need;
     select_kth<P>(s, key, mine, n, k, &thr, &need, tog);
     emit_to_lds<P>(s, key, base, thr, need, k, tog);
     __syncthreads();
-    for (int i = threadIdx.x; i < k; i += kThreads) out_idx[i] = cslot[s.u.stage[kEmitPos + i]];
+    for (int i = tid; i < k; i += kThreads) {
+        const uint32_t kk = s.u.stage[kEmitKey + i];
+        cslot[i] = lo + (int)s.u.stage[kEmitPos + i];
+        ckey[i] = kk;
+        atomicAdd(&s.khist[kept_bin(kk, cut)], 1u);
+    }
+    __syncthreads();
+    for (int b = tid; b < kHistBins; b += kThreads) hist_out[b] = s.khist[b];
+    if (tid == 0) {
+        a.cand_count[rj] = k;
+        a.cand_cut[rj] = (int)cut;
+    }
+}
+
+// Row r's exact top k straight from its scores [0, v), v > k, when the kept
+// keys do not hold it: three radix passes of 12, 10 and 10 bits over the
+// whole row, then the emission in rounds of kThreads positions, each round
+// one scan.  Slow, and only for the rows whose cut missed.
+__device__ void topk_row_streamed(TopkSmem& s, const float* row, int v, int k, int32_t* out, int& tog) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0u, mask = 0u, kk = (uint32_t)k;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 20 : pass == 1 ? 10 : 0;
+        const int nb = pass == 0 ? kBins0 : kBins1;
+        __syncthreads();
+        for (int i = tid; i < nb; i += kThreads) s.u.sel.hist[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < v; i += kThreads) {
+            const uint32_t key = monotone_key(row[i]);
+            if ((key & mask) == prefix) atomicAdd(&s.u.sel.hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        if (pass == 0) find_digit<kBins0>(s, s.u.sel.hist, kk, tog);
+        else find_digit<kBins1>(s, s.u.sel.hist, kk, tog);
+        prefix |= s.sel_digit << shift;
+        mask |= (uint32_t)(nb - 1) << shift;
+        kk = s.sel_need;
+    }
+    const uint32_t thr = prefix, need_eq = kk;
+    const bool eq_ok = thr != 0u;   // a zero threshold means NaN scores, reported elsewhere
+    uint32_t taken_before = 0u, eq_before_round = 0u;
+#pragma unroll 1
+    for (int i0 = 0; i0 < v; i0 += kThreads) {
+        const int i = i0 + tid;
+        const uint32_t key = i < v ? monotone_key(row[i]) : 0u;
+        const uint32_t gt = key > thr ? 1u : 0u;
+        const uint32_t eq = (i < v && eq_ok && key == thr) ? 1u : 0u;
+        uint32_t tot;
+        const uint32_t both = scan2(s, (gt << 16) | eq, &tot, tog);
+        const uint32_t eq_before = eq_before_round + (both & 0xFFFFu);
+        const uint32_t eq_quota = need_eq > eq_before_round ? need_eq - eq_before_round : 0u;
+        const bool take = gt || (eq && eq_before < need_eq);
+        const uint32_t rank = taken_before + (both >> 16) + min(both & 0xFFFFu, eq_quota);
+        if (take && rank < (uint32_t)k) out[rank] = i;
+        taken_before += (tot >> 16) + min(tot & 0xFFFFu, eq_quota);
+        eq_before_round += tot & 0xFFFFu;
+    }
+}
+
+// Merge pass: grid (n_rows).  The row's kept keys, split after split, form
+// one list in slot order; its top k (the row's top k, see above) is emitted
+// in that order.  The list is gathered into the staging buffer and selected
+// with as few keys per thread (4, 8, 16 or 32) as its length allows.
+template <int P>
+__device__ __forceinline__ void merge_select(const TopkArgs& a, TopkSmem& s, const int* off, int ns, int nc, int k,
+                                             int32_t* out_idx, int& tog) {
+    const int tid = threadIdx.x;
+    const int per = keys_per_thread(nc);
+    const int base = tid * per;
+    const int mine = max(0, min(per, nc - base));
+    uint32_t key[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const uint32_t x = s.u.stage[stage_index(min(base + i, kTopkMaxList - 1))];
+        key[i] = i < mine ? x : 0u;
+    }
+    __syncthreads();
+    for (int i = tid; i < kBins0; i += kThreads) s.h0[i] = 0u;
+    __syncthreads();
+    uint32_t thr, need;
+    select_kth<P>(s, key, mine, nc, k, &thr, &need, tog);
+    emit_to_lds<P>(s, key, base, thr, need, k, tog);
+    __syncthreads();
+    const size_t row_base = (size_t)blockIdx.x * ns * k;
+    for (int i = tid; i < k; i += kThreads) {
+        const int pos = min(max((int)s.u.stage[kEmitPos + i], 0), nc - 1);
+        int lo_j = 0, hi_j = ns - 1;   // the split holding list position pos
+        while (lo_j < hi_j) {
+            const int mid = (lo_j + hi_j + 1) >> 1;
+            if (off[mid] <= pos) lo_j = mid;
+            else hi_j = mid - 1;
+        }
+        out_idx[i] = a.cand_slot[row_base + (size_t)lo_j * k + (pos - off[lo_j])];
+    }
+}
+
+// Words of the staging buffer where the merge keeps the kept keys' slots
+// (the keys sit at stage_index([0, nc)), which stays below kSlotBase when
+// nc <= kSlotBase); the fast merge needs nc <= kSlotBase.
+constexpr int kSlotBase = kTopkMaxList / 2;
+
+// Fast merge, given the threshold bin b of the summed kept-key histograms
+// (need = how many keys of bin b belong to the top k, m = keys in bin b <=
+// 64): thread t holds list positions [t*per, t*per + per) of the kept keys
+// (in the staging buffer, slots at kSlotBase); one wavefront ranks bin b's
+// keys exactly and the selection is emitted in list order.
+template <int P>
+__device__ __forceinline__ void merge_fast(TopkSmem& s, int nc, int k, uint32_t cut, int bstar, uint32_t need,
+                                           uint32_t m, int32_t* out_idx, int& tog) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int per = keys_per_thread(nc);
+    const int base = tid * per;
+    const int mine = max(0, min(per, nc - base));
+    uint32_t key[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const uint32_t x = s.u.stage[stage_index(min(base + i, kSlotBase - 1))];
+        key[i] = i < mine ? x : 0u;
+    }
+    if (tid == 0) s.bcount = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        if (i < mine && kept_bin(key[i], cut) == bstar) {
+            const uint32_t at = atomicAdd(&s.bcount, 1u);
+            s.bkey[min(at, (uint32_t)kWave - 1)] = key[i];
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        const uint32_t mk = lane < (int)m ? s.bkey[lane] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t j = 0; j < m; ++j) {
+            const uint32_t x = s.bkey[j];
+            gt += x > mk ? 1u : 0u;
+            ge += x >= mk ? 1u : 0u;
+        }
+        if (lane < (int)m && gt < need && need <= ge) {
+            s.sel_thr = mk;
+            s.sel_need_eq = need - gt;
+        }
+    }
+    __syncthreads();
+    const uint32_t thr = s.sel_thr, need_eq = s.sel_need_eq;
+    // Emission as in the direct selection, each position's slot from LDS.
+    uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        gtm |= (i < mine && key[i] > thr ? 1u : 0u) << i;
+        eqm |= (i < mine && key[i] == thr ? 1u : 0u) << i;
+    }
+    uint32_t tot;
+    const uint32_t both = scan2(s, ((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm), &tot, tog);
+    const uint32_t eq_before = both & 0xFFFFu;
+    uint32_t take_eq = min((uint32_t)__popc(eqm), need_eq > eq_before ? need_eq - eq_before : 0u);
+    uint32_t tm = gtm;
+    for (uint32_t em = eqm; take_eq > 0; --take_eq) {
+        tm |= em & (0u - em);
+        em &= em - 1u;
+    }
+    uint32_t rank = (both >> 16) + min(eq_before, need_eq);
+    while (tm != 0u) {
+        const int i = __ffs(tm) - 1;
+        tm &= tm - 1u;
+        if (rank < (uint32_t)k) out_idx[rank] = (int32_t)s.u.stage[kSlotBase + base + i];
+        ++rank;
+    }
+}
+
+// Merge pass: grid (n_rows).  The row's kept keys, split after split, form
+// one list in slot order, gathered into the staging buffer; its top k is
+// the row's top k (see above).  The splits' histograms, summed, give the bin
+// of the k-th largest kept key, and one wavefront ranks that bin's keys;
+// rows whose bin holds more than 64 keys (or without a cut) take the general
+// selection instead.
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
+    __shared__ TopkSmem s;
+    __shared__ int off[kMaxSplits + 1];
+    __shared__ uint32_t hsum[kHistBins];
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int k = a.top_k;
+    const int ns = a.n_splits;
+    int32_t* out_idx = a.topk_idx + (size_t)r * k;
+    const size_t rb = (size_t)r * ns;
+    const int v = checked_vis(a, r);
+    const int want = min(v, k);
+    if (tid == 0) a.topk_count[r] = want;
+    // Everything this row needs goes out at once: the splits' counts, the
+    // cut, the summed histograms, and the first kSpec entries of each
+    // split's kept list (kept lists are usually that short).
+    const int tps = kThreads / ns;            // threads per split for the speculative loads
+    constexpr int kSpec = 8;
+    const int sj = tid / tps, si = tid - sj * tps;
+    int cnt_lane = 0;
+    if (tid < kWave) cnt_lane = tid < ns ? min(max(a.cand_count[rb + tid], 0), k) : 0;
+    const uint32_t cut = (uint32_t)a.cand_cut[rb];
+    uint32_t hs = 0u;
+    if (tid < kHistBins) {
+        const uint32_t* h = reinterpret_cast<const uint32_t*>(a.cand_hist) + rb * kHistBins + tid;
+        for (int j = 0; j < ns; ++j) hs += h[(size_t)j * kHistBins];
+    }
+    uint32_t sk[kSpec];
+    int32_t ss[kSpec];
+#pragma unroll
+    for (int q = 0; q < kSpec; ++q) {
+        const int i = si + q * tps;
+        const bool ok = sj < ns && i < k;
+        const size_t at = (rb + (size_t)(ok ? sj : 0)) * k + (size_t)(ok ? i : 0);
+        sk[q] = a.cand_key[at];
+        ss[q] = a.cand_slot[at];
+    }
+    if (tid < kWave) {
+        const uint32_t inc = wave_inclusive_scan((uint32_t)cnt_lane);
+        if (tid < ns) off[tid + 1] = (int)inc;
+        if (tid == 0) off[0] = 0;
+    }
+    if (tid < kHistBins) hsum[tid] = hs;
+    __syncthreads();
+    const int nc = off[ns];
+    int tog = 0;
+    if (nc < want) {
+        // The cut kept fewer than k keys: select from the whole row.
+        topk_row_streamed(s, a.scores + (size_t)r * a.score_stride, v, k, out_idx, tog);
+        return;
+    }
+    // The kept keys (and, when they fit, their slots) into the staging
+    // buffer at their list positions.
+    const bool slots_fit = nc <= kSlotBase;
+    if (sj < ns) {
+        const int c = off[sj + 1] - off[sj];
+#pragma unroll
+        for (int q = 0; q < kSpec; ++q) {
+            const int i = si + q * tps;
+            if (i < c) {
+                s.u.stage[stage_index(off[sj] + i)] = sk[q];
+                if (slots_fit) s.u.stage[kSlotBase + off[sj] + i] = (uint32_t)ss[q];
+            }
+        }
+        for (int i = si + kSpec * tps; i < c; i += tps) {   // longer kept lists
+            s.u.stage[stage_index(off[sj] + i)] = a.cand_key[(rb + sj) * k + i];
+            if (slots_fit) s.u.stage[kSlotBase + off[sj] + i] = (uint32_t)a.cand_slot[(rb + sj) * k + i];
+        }
+    }
+    __syncthreads();
+    if (nc <= k) {
+        // Every kept key is selected (nc == want), in list order.
+        for (int i = tid; i < nc; i += kThreads) {
+            if (slots_fit) {
+                out_idx[i] = (int32_t)s.u.stage[kSlotBase + i];
+            } else {
+                int lo_j = 0, hi_j = ns - 1;
+                while (lo_j < hi_j) {
+                    const int mid = (lo_j + hi_j + 1) >> 1;
+                    if (off[mid] <= i) lo_j = mid;
+                    else hi_j = mid - 1;
+                }
+                out_idx[i] = a.cand_slot[(rb + lo_j) * k + (i - off[lo_j])];
+            }
+        }
+        pad_tail(out_idx, nc, k);
+        return;
+    }
+    // Threshold bin: thread t holds bin kHistBins - 1 - t, so its exclusive
+    // prefix counts the keys in the bins above.
+    const uint32_t hb = tid < kHistBins ? hsum[kHistBins - 1 - tid] : 0u;
+    if (tid == 0) {
+        s.sel_digit = 0u;
+        s.sel_need = 0u;
+    }
+    uint32_t total;
+    const uint32_t above = scan2(s, hb, &total, tog);
+    if (tid < kHistBins && above < (uint32_t)k && above + hb >= (uint32_t)k) {
+        s.sel_digit = (uint32_t)(kHistBins - 1 - tid);
+        s.sel_need = (uint32_t)k - above;
+    }
+    __syncthreads();
+    const int bstar = min((int)s.sel_digit, kHistBins - 1);
+    const uint32_t need = s.sel_need;
+    const uint32_t m = hsum[bstar];
+    if (cut != 0u && slots_fit && total == (uint32_t)nc && m <= (uint32_t)kWave && need >= 1u) {
+        if (nc <= 4 * kThreads) merge_fast<4>(s, nc, k, cut, bstar, need, m, out_idx, tog);
+        else if (nc <= 8 * kThreads) merge_fast<8>(s, nc, k, cut, bstar, need, m, out_idx, tog);
+        else merge_fast<16>(s, nc, k, cut, bstar, need, m, out_idx, tog);
+        return;
+    }
+    if (nc <= 4 * kThreads) merge_select<4>(a, s, off, ns, nc, k, out_idx, tog);
+    else if (nc <= 8 * kThreads) merge_select<8>(a, s, off, ns, nc, k, out_idx, tog);
+    else if (nc <= 16 * kThreads) merge_select<16>(a, s, off, ns, nc, k, out_idx, tog);
+    else merge_select<32>(a, s, off, ns, nc, k, out_idx, tog);
 }
 
 }  // namespace
@@ -673,15 +1025,19 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     // Longest split: ceil(score_stride / n_splits) rounded up to whole chunks
     // (row_vis <= score_stride is checked on the device).
     const int64_t split_max = (((int64_t)a.score_stride + a.n_splits - 1) / a.n_splits + 3) & ~int64_t{3};
+    if (a.n_splits == 1) {
+        return by_class(keys_class(split_max), [&](auto pc) {
+            topk_direct_kernel<decltype(pc)::value><<<dim3(1, a.n_rows), kThreads, 0, stream>>>(a);
+            return hipGetLastError();
+        });
+    }
     hipError_t e = by_class(keys_class(split_max), [&](auto pc) {
-        topk_split_kernel<decltype(pc)::value><<<dim3(a.n_splits, a.n_rows), kThreads, 0, stream>>>(a);
+        topk_filter_kernel<decltype(pc)::value><<<dim3(a.n_splits, a.n_rows), kThreads, 0, stream>>>(a);
         return hipGetLastError();
     });
-    if (e != hipSuccess || a.n_splits == 1) return e;
-    return by_class(keys_class((int64_t)a.n_splits * a.top_k), [&](auto pc) {
-        topk_merge_kernel<decltype(pc)::value><<<a.n_rows, kThreads, 0, stream>>>(a);
-        return hipGetLastError();
-    });
+    if (e != hipSuccess) return e;
+    topk_merge_kernel<<<a.n_rows, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -89,12 +89,12 @@ CONFIGS = {
                  index_splits=16, attn_splits=32, planted=4),
     # MTP verify: 6 causal rows per request.
     "c3": Config("c3", batch=32, kv_range=(16384, 65536), rows_per_req=6, causal="mtp",
-                 mla_heads=32, index_splits=2, attn_splits=1, group_rows=6),
+                 mla_heads=32, index_splits=4, attn_splits=1, group_rows=6),
     # MTP draft chains with IndexShare: the MTP-verify geometry (32 requests x
     # 6 causal rows), the indexer and top-k run on each chain's first row
     # only, and all six rows attend that row's list.
     "c3s": Config("c3s", batch=32, kv_range=(16384, 65536), rows_per_req=6, causal="mtp",
-                  mla_heads=32, index_splits=2, attn_splits=1, index_share=6),
+                  mla_heads=32, index_splits=4, attn_splits=1, index_share=6),
     # Long-prefix prefill on the owned top-k path: 4096 new rows after 65536.
     # Five index splits keep each split's list (69632 / 5 scores) within 16
     # keys a thread.

@@ -186,6 +186,29 @@ def test_topk_with_infinities_matches_oracle(n_splits):
         np.testing.assert_array_equal(idx[i], ri)
 
 
+@pytest.mark.parametrize("n_splits", [2, 4])
+def test_topk_cut_that_misses_falls_back_to_the_whole_row(n_splits):
+    """Scores planted at the row sample's positions (floor(i * v / 512))
+    make every split's cut too high, so fewer than k keys pass it; the merge
+    then selects from the whole row, with the same result as the oracle."""
+    rng = np.random.default_rng(60 + n_splits)
+    r, stride, k = 3, 32768, 2048
+    vis = [32768, 20000, 9000]
+    s = rng.normal(size=(r, stride)).astype(np.float32)
+    for i, v in enumerate(vis):
+        pos = (np.arange(512, dtype=np.int64) * v) // 512
+        s[i, pos] = 50.0 + rng.random(512).astype(np.float32)
+        s[i, v:] = -np.inf
+    idx, cnt, st = dsa.topk(torch.from_numpy(s).cuda(), torch.tensor(vis, dtype=torch.int32).cuda(), k, n_splits)
+    torch.cuda.synchronize()
+    dsa.check_status(st)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for i, v in enumerate(vis):
+        ri, rc = O.topk_global(s[i].astype(np.float64), v, k)
+        assert cnt[i] == rc
+        np.testing.assert_array_equal(idx[i], ri)
+
+
 def test_topk_all_equal_scores_keep_lowest_slots():
     s = np.zeros((2, 9000), dtype=np.float32)
     vis = [9000, 4097]
