@@ -51,6 +51,7 @@
 // conflict-free as it is.
 #include "device_common.h"
 #include "launch.h"
+#include "query_quant.h"
 
 namespace dsa {
 
@@ -275,19 +276,6 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) any_bad |= s_bad[w] != 0;
 
-    // The query operand of this lane (head 16 hb + nn, lane group g) for the
-    // whole split: for the i-th key chunk of lane group g (chunk ch), the
-    // query elements [16 ch, 16 ch + 16) as two 8-element K steps.
-    v8bf qb[18];
-    {
-        const uint8_t* qr = s_x[NB - 1] + (16 * hb + nn) * kQRow;
-#pragma unroll
-        for (int i = 0; i < 9; ++i) {
-            const int ch = i < 8 ? qk_chunk(i >> 1, i & 1, g) : 32 + g;
-            qb[2 * i] = *reinterpret_cast<const v8bf*>(qr + 32 * ch);
-            qb[2 * i + 1] = *reinterpret_cast<const v8bf*>(qr + 32 * ch + 16);
-        }
-    }
     const float cq = a.sm_scale;
 
     // Row of tile-local token t of the tile starting at split entry `base`.
@@ -341,6 +329,89 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     for (int j = 0; j < NB - 1; ++j)
         if (j < n_tiles) issue(j, lo + j * kT);
 
+    // The query as two E4M3 terms, while those tiles load.  Head h's bf16
+    // values q (exact fp32) are scaled by 2^-e_h, e_h the smallest exponent
+    // with max|q| <= 448 * 2^e_h (the indexer query's rule); hi = RNE(q 2^-e)
+    // in E4M3, lo = RNE(q 2^-e - hi).  A bf16 value has 8 significant bits and
+    // hi keeps the top 4, so lo is exact except where it falls below E4M3's
+    // smallest subnormal (values under 2^-7 of the head's largest, where the
+    // lost part is at most 2^-10 of the scaled unit): q . k = 2^e (hi . k +
+    // lo . k) with every fp8 product exact, on fp8 matrix cores with the
+    // keys' codes as they are stored.  Sixteen threads per head (36 values
+    // each) split the query in place in its staging buffer: each head's row
+    // becomes 576 hi codes then 576 lo codes.
+    __shared__ float s_qs[H];   // 2^e per head
+    {
+        constexpr int kPart = kRowBytes / 16;   // 36 values per thread
+        static_assert(NT == 16 * H, "sixteen threads per head");
+        const int qh = tid >> 4, part = tid & 15;
+        uint8_t* hrow = s_x[NB - 1] + qh * kQRow;
+        float v[kPart];
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kPart / 4; ++k) {
+            const uint2 w = *reinterpret_cast<const uint2*>(hrow + 2 * (kPart * part + 4 * k));
+            v[4 * k + 0] = __uint_as_float(w.x << 16);
+            v[4 * k + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+            v[4 * k + 2] = __uint_as_float(w.y << 16);
+            v[4 * k + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int k = 0; k < kPart; ++k) amax = fmaxf(amax, fabsf(v[k]));
+        amax = row16_max(amax);   // the head's sixteen threads are one 16-lane row
+        const int e = idx_q_exponent(amax);
+        uint32_t hw[kPart / 4], lw[kPart / 4];
+#pragma unroll
+        for (int k = 0; k < kPart / 4; ++k) {
+            float y[4], rr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = __builtin_amdgcn_ldexpf(v[4 * k + j], -e);
+            const int h01 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            const int h23 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], h01, true);
+            const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(h23, false);
+            const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(h23, true);
+            rr[0] = y[0] - d01[0];
+            rr[1] = y[1] - d01[1];
+            rr[2] = y[2] - d23[0];
+            rr[3] = y[3] - d23[1];
+            const int l01 = __builtin_amdgcn_cvt_pk_fp8_f32(rr[0], rr[1], 0, false);
+            hw[k] = (uint32_t)h23;
+            lw[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rr[2], rr[3], l01, true);
+        }
+        __syncthreads();   // every bf16 value of the buffer has been read
+#pragma unroll
+        for (int k = 0; k < kPart / 4; ++k) {
+            *reinterpret_cast<uint32_t*>(hrow + kPart * part + 4 * k) = hw[k];
+            *reinterpret_cast<uint32_t*>(hrow + kRowBytes + kPart * part + 4 * k) = lw[k];
+        }
+        if (part == 0) s_qs[qh] = __builtin_amdgcn_ldexpf(1.0f, e);
+        __syncthreads();
+    }
+    // This lane's operands (head 16 hb + nn, lane group g) for the whole
+    // split: for 128-element MFMA step m the 32 codes at elements
+    // [16 c, 16 c + 32), c = qk_chunk(m, 0, g), the same 32 bytes of every
+    // key row; for the rope, the 16 codes [512 + 16 g, +16) as two 8-code
+    // steps.  Both terms.
+    v8i qh8[4], ql8[4];
+    v4i qrh, qrl;
+    float qsc;
+    {
+        const uint8_t* hr = s_x[NB - 1] + (16 * hb + nn) * kQRow;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int c = qk_chunk(m, 0, g);
+            const v4i h0 = *reinterpret_cast<const v4i*>(hr + 16 * c);
+            const v4i h1 = *reinterpret_cast<const v4i*>(hr + 16 * c + 16);
+            const v4i l0 = *reinterpret_cast<const v4i*>(hr + kRowBytes + 16 * c);
+            const v4i l1 = *reinterpret_cast<const v4i*>(hr + kRowBytes + 16 * c + 16);
+            qh8[m] = v8i{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+            ql8[m] = v8i{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        }
+        qrh = *reinterpret_cast<const v4i*>(hr + 16 * (32 + g));
+        qrl = *reinterpret_cast<const v4i*>(hr + kRowBytes + 16 * (32 + g));
+        qsc = cq * s_qs[16 * hb + nn];
+    }
+
     // Softmax state: in the QK layout a lane owns head 16 hb + nn (m_run,
     // and l_run: this wavefront's share of the denominator); in the PV
     // layout accumulator row i of lane group g is head 16 h2 + 4g + i.
@@ -365,18 +436,27 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
             lds_sync();
         }
 
-        // QK: token block tbk (A, rows), head block hb (B), in bf16: each
-        // 16-byte key chunk of the lane's row is two 8-element K steps.
-        v4f a0 = v4f{0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+        // QK: token block tbk (A, rows), head block hb (B), on fp8 matrix
+        // cores: the keys' codes as stored against the two query terms, the
+        // 512 latent values in four 128-deep steps, the 64 rope values in two
+        // 32-deep steps.
+        v4f ah = v4f{0.0f, 0.0f, 0.0f, 0.0f}, al = ah;
         {
             const uint8_t* xr = xb + (16 * tbk + nn) * kXStride;
 #pragma unroll
-            for (int i = 0; i < 9; ++i) {
-                const int ch = i < 8 ? qk_chunk(i >> 1, i & 1, g) : 32 + g;
-                const v4i x = *reinterpret_cast<const v4i*>(xr + 16 * ch);
-                a0 = mfma_bf16_16x16x32(fp8x8_to_bf16x8((uint32_t)x.x, (uint32_t)x.y), qb[2 * i], a0);
-                a1 = mfma_bf16_16x16x32(fp8x8_to_bf16x8((uint32_t)x.z, (uint32_t)x.w), qb[2 * i + 1], a1);
+            for (int m = 0; m < 4; ++m) {
+                const int c = qk_chunk(m, 0, g);
+                const v4i x0 = *reinterpret_cast<const v4i*>(xr + 16 * c);
+                const v4i x1 = *reinterpret_cast<const v4i*>(xr + 16 * c + 16);
+                const v8i ka = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                ah = mfma_fp8_16x16x128(ka, qh8[m], ah);
+                al = mfma_fp8_16x16x128(ka, ql8[m], al);
             }
+            const v4i xq = *reinterpret_cast<const v4i*>(xr + 16 * (32 + g));
+            ah = mfma_fp8_16x16x32(v2i{xq.x, xq.y}, v2i{qrh.x, qrh.y}, ah);
+            al = mfma_fp8_16x16x32(v2i{xq.x, xq.y}, v2i{qrl.x, qrl.y}, al);
+            ah = mfma_fp8_16x16x32(v2i{xq.z, xq.w}, v2i{qrh.z, qrh.w}, ah);
+            al = mfma_fp8_16x16x32(v2i{xq.z, xq.w}, v2i{qrl.z, qrl.w}, al);
         }
 
         // Logits of this lane's tokens tk0 + i (tk0 = 16 tbk + 4g) for head
@@ -408,7 +488,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            lg[i] = live[i] ? (a0[i] + a1[i]) * (cq * ts[i]) : -INFINITY;
+            lg[i] = live[i] ? (ah[i] + al[i]) * (qsc * ts[i]) : -INFINITY;
             mx = fmaxf(mx, lg[i]);
         }
         mx = rows4_max(mx);
