@@ -361,15 +361,26 @@ def main():
     # replayed K/4 times on the launch stream between two HIP events,
     # averaged per launch.
     def kernel_launches(i, st):
-        fns = {
-            "index_scores": lambda: dsa.index_scores(
-                st.lead_q, st.lead_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
-                st.lead_req, st.lead_vis, group_rows=st.group_rows, score_stride=st.score_stride,
-                scores=st.scores, status=st.status),
-            "topk": lambda: dsa.topk(st.scores, st.lead_vis, i.top_k, st.index_splits,
-                                     workspace=st.workspace, topk_idx=st.topk_idx,
-                                     topk_count=st.topk_count, status=st.status),
-        }
+        if st.index_topk:
+            # The step's own two kernels: the indexer with its candidate
+            # epilogue, then the merge (dsa_index_topk's two phases).
+            def fused(phases):
+                return lambda: dsa.index_topk(
+                    st.lead_q, st.lead_w, i.k_code, i.k_scale, i.page_table, i.kv_lens, st.lead_req,
+                    st.lead_vis, i.top_k, score_stride=st.score_stride, scores=st.scores,
+                    workspace=st.workspace, topk_idx=st.topk_idx, topk_count=st.topk_count,
+                    status=st.status, phases=phases)
+            fns = {"index_scores": fused(dsa.PHASE_SCORE), "topk": fused(dsa.PHASE_SELECT)}
+        else:
+            fns = {
+                "index_scores": lambda: dsa.index_scores(
+                    st.lead_q, st.lead_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
+                    st.lead_req, st.lead_vis, group_rows=st.group_rows, score_stride=st.score_stride,
+                    scores=st.scores, status=st.status),
+                "topk": lambda: dsa.topk(st.scores, st.lead_vis, i.top_k, st.index_splits,
+                                         workspace=st.workspace, topk_idx=st.topk_idx,
+                                         topk_count=st.topk_count, status=st.status),
+            }
         if st.row_list is not None:
             s_ = st.attn_splits
             fns["sparse_mla"] = lambda: dsa.sparse_mla_decode_shared(
@@ -481,7 +492,8 @@ def main():
                         f"indexer 64x128 fp8, MLA {inp.mla_heads} heads x 576 fp8, page {inp.page_size}",
             "batch": inp.n_rows, "kv_len_max": int(inp.row_vis.max()), "top_k": inp.top_k,
             "page_size": inp.page_size, "mla_heads": inp.mla_heads,
-            "index_splits": step.index_splits, "attn_splits": step.attn_splits,
+            "index_splits": "in the indexer's chunks" if step.index_topk else step.index_splits,
+            "attn_splits": step.attn_splits,
             "launch": "eager" if round_graph is None else "hipgraph",
             "input_sets": n_sets,
         },

@@ -12,6 +12,8 @@
  *                            rows, split along the selected list into
  *                            (partial output, natural-log LSE) pairs
  *   4. dsa_lse_merge         merge of the split partials by their LSE
+ * dsa_index_topk runs steps 1 and 2 for decode rows with the top-k's
+ * candidate filter in the indexer's epilogue (same results as the two calls).
  * dsa_quantize_q exposes the query quantization of step 1 on its own.
  * dsa_cache_write is the step before the path: it stores new tokens' MLA rows
  * and index keys in the paged caches the four steps read.
@@ -63,7 +65,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 8
+#define DSA_ABI_VERSION 9
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -203,6 +205,47 @@ int dsa_index_scores(const uint16_t* q, const float* head_w,
                      int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
                      int32_t page_size, int32_t n_heads, int32_t head_dim, int32_t group_rows,
                      float* scores, int32_t score_stride, int32_t* status, hipStream_t stream);
+
+/*
+ * dsa_index_topk -- steps 1 and 2 for decode rows (one row per scoring
+ * group): the scores of dsa_index_scores with group_rows = 1, and the top-k
+ * of dsa_topk over them, bit for bit (subject page, Modifications, indexer
+ * decode: local top-k per shard merged into the exact global top-k).
+ * The indexer scores each row in chunks of tokens, one workgroup each; while
+ * a chunk's scores are still on chip, the workgroup keeps its candidates:
+ * every visible score at or above a cut of its own, placed near the rank of
+ * the chunk's expected share of the row's top top_k plus four standard
+ * deviations.  A merge per row then selects the top top_k of the
+ * candidates, after checking that at least top_k of them lie at or above the
+ * highest chunk cut, which makes them hold the row's top top_k; a row that
+ * fails the check (scores far from exchangeable across chunks, many equal
+ * scores) is selected from its scores instead (slower, same result).
+ *   arguments as dsa_index_scores (group_rows fixed to 1) and dsa_topk;
+ *   scores [n_rows, score_stride] f32 out (as dsa_index_scores)
+ *   topk_idx [n_rows, top_k] i32 out, topk_count [n_rows] i32 out (as dsa_topk)
+ *   workspace: dsa_index_topk_workspace_size(n_rows, score_stride, top_k)
+ *   bytes of device memory, 4-byte aligned, else DSA_ERR_WORKSPACE; its
+ *   contents need no initialisation and are not results.
+ * phases: DSA_PHASE_SCORE | DSA_PHASE_SELECT runs both (the normal call);
+ * DSA_PHASE_SCORE alone writes the scores and the candidates in the
+ * workspace; DSA_PHASE_SELECT alone runs the merge over the candidates and
+ * scores a previous DSA_PHASE_SCORE call with the same arguments left there
+ * (the two halves can be timed or scheduled apart).  Other values:
+ * DSA_ERR_SHAPE.
+ * Device status bits: those of dsa_index_scores and dsa_topk (DSA_DEV_NAN
+ * for a NaN score inside a row's span).
+ * Limits: 1 <= top_k <= 8192; the indexer's chunks per row (score_stride
+ * over its chunk length of 1024 to 8192 tokens) at most 1024.
+ */
+#define DSA_PHASE_SCORE 1
+#define DSA_PHASE_SELECT 2
+size_t dsa_index_topk_workspace_size(int32_t n_rows, int32_t score_stride, int32_t top_k);
+int dsa_index_topk(const uint16_t* q, const float* head_w, const uint8_t* k_code, const float* k_scale,
+                   const int32_t* page_table, const int32_t* kv_lens, const int32_t* row_req,
+                   const int32_t* row_vis, int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
+                   int32_t page_size, int32_t n_heads, int32_t head_dim, float* scores, int32_t score_stride,
+                   int32_t top_k, int32_t phases, void* workspace, size_t workspace_bytes,
+                   int32_t* topk_idx, int32_t* topk_count, int32_t* status, hipStream_t stream);
 
 /*
  * Workspace bytes dsa_topk needs for n_splits > 1: room for top_k candidate

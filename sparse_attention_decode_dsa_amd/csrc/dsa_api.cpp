@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "dsa.h"
 #include "launch.h"
 
@@ -75,6 +77,45 @@ int mla_checked(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_
     return launch_status(dsa::launch_sparse_mla(a, stream));
 }
 
+// Validation of an indexer call (the rules of dsa_index_scores) and its
+// arguments, filled into `a`; nothing is launched.
+int index_checked(const uint16_t* q, const float* head_w, const uint8_t* k_code, const float* k_scale,
+                  const int32_t* page_table, const int32_t* kv_lens, const int32_t* row_req,
+                  const int32_t* row_vis, int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
+                  int32_t page_size, int32_t n_heads, int32_t head_dim, int32_t group_rows, float* scores,
+                  int32_t score_stride, int32_t* status, dsa::IndexArgs& a) {
+    if (n_rows < 0 || n_rows > kMaxRows || score_stride < 1) return DSA_ERR_SHAPE;
+    if (n_heads < 1 || head_dim < 1) return DSA_ERR_SHAPE;
+    if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
+    int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
+    if (rc != DSA_OK) return rc;
+    if (group_rows < 1 || group_rows > 8) return DSA_ERR_SHAPE;
+    if (n_rows % group_rows != 0) return DSA_ERR_SHAPE;
+    if (!q || !head_w || !k_code || !k_scale || !page_table || !kv_lens ||
+        !row_req || !row_vis || !scores || !status)
+        return DSA_ERR_NULL;
+    a.q = q; a.head_w = head_w;
+    a.k_code = k_code; a.k_scale = k_scale; a.page_table = page_table; a.kv_lens = kv_lens;
+    a.row_req = row_req; a.row_vis = row_vis;
+    a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
+    a.page_size = page_size; a.log2_page = log2i(page_size); a.group_rows = group_rows;
+    a.scores = scores; a.score_stride = score_stride; a.status = status;
+    a.cand_key = nullptr;
+    return DSA_OK;
+}
+
+// Chunks per row of the decode indexer launch and the candidates' block
+// length per chunk (a chunk keeps at most min(chunk, top_k) of them).
+constexpr int32_t kMaxIndexChunks = 1024;
+struct IndexTopkGeometry {
+    int64_t n_chunks;
+    int32_t cap;
+};
+IndexTopkGeometry index_topk_geometry(int32_t n_rows, int32_t score_stride, int32_t top_k) {
+    const int chunk = dsa::index_chunk(n_rows, score_stride);
+    return {((int64_t)score_stride + chunk - 1) / chunk, std::min(chunk, top_k)};
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,25 +152,60 @@ int dsa_index_scores(const uint16_t* q, const float* head_w,
                      int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
                      int32_t page_size, int32_t n_heads, int32_t head_dim, int32_t group_rows,
                      float* scores, int32_t score_stride, int32_t* status, hipStream_t stream) {
-    if (n_rows < 0 || n_rows > kMaxRows || score_stride < 1) return DSA_ERR_SHAPE;
-    if (n_heads < 1 || head_dim < 1) return DSA_ERR_SHAPE;
-    if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
-    int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
-    if (rc != DSA_OK) return rc;
-    if (group_rows < 1 || group_rows > 8) return DSA_ERR_SHAPE;
-    if (n_rows % group_rows != 0) return DSA_ERR_SHAPE;
-    if (!q || !head_w || !k_code || !k_scale || !page_table || !kv_lens ||
-        !row_req || !row_vis || !scores || !status)
-        return DSA_ERR_NULL;
-    if (n_rows == 0) return DSA_OK;
-    dsa::IndexArgs a;
-    a.q = q; a.head_w = head_w;
-    a.k_code = k_code; a.k_scale = k_scale; a.page_table = page_table; a.kv_lens = kv_lens;
-    a.row_req = row_req; a.row_vis = row_vis;
-    a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
-    a.page_size = page_size; a.log2_page = log2i(page_size); a.group_rows = group_rows;
-    a.scores = scores; a.score_stride = score_stride; a.status = status;
+    dsa::IndexArgs a{};
+    const int rc = index_checked(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis, n_rows, batch,
+                                 num_pages, max_pages, page_size, n_heads, head_dim, group_rows, scores,
+                                 score_stride, status, a);
+    if (rc != DSA_OK || n_rows == 0) return rc;
     return launch_status(dsa::launch_index_scores(a, stream));
+}
+
+size_t dsa_index_topk_workspace_size(int32_t n_rows, int32_t score_stride, int32_t top_k) {
+    if (n_rows <= 0 || score_stride < 1 || top_k < 1) return 0;
+    const IndexTopkGeometry g = index_topk_geometry(n_rows, score_stride, top_k);
+    // keys and slots [n_rows, n_chunks, cap]; counts and cuts [n_rows, n_chunks]
+    return (size_t)n_rows * g.n_chunks * (2 * (size_t)g.cap + 2) * sizeof(int32_t);
+}
+
+int dsa_index_topk(const uint16_t* q, const float* head_w, const uint8_t* k_code, const float* k_scale,
+                   const int32_t* page_table, const int32_t* kv_lens, const int32_t* row_req,
+                   const int32_t* row_vis, int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
+                   int32_t page_size, int32_t n_heads, int32_t head_dim, float* scores, int32_t score_stride,
+                   int32_t top_k, int32_t phases, void* workspace, size_t workspace_bytes, int32_t* topk_idx,
+                   int32_t* topk_count, int32_t* status, hipStream_t stream) {
+    if (phases < 1 || phases > (DSA_PHASE_SCORE | DSA_PHASE_SELECT)) return DSA_ERR_SHAPE;
+    dsa::IndexArgs a{};
+    int rc = index_checked(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis, n_rows, batch,
+                           num_pages, max_pages, page_size, n_heads, head_dim, 1, scores, score_stride, status, a);
+    if (rc != DSA_OK) return rc;
+    if (top_k < 1 || top_k > dsa::kTopkMaxK) return DSA_ERR_SHAPE;
+    const IndexTopkGeometry g = index_topk_geometry(std::max(n_rows, 1), score_stride, top_k);
+    if (g.n_chunks > kMaxIndexChunks) return DSA_ERR_SHAPE;
+    if (!topk_idx || !topk_count) return DSA_ERR_NULL;
+    if (n_rows == 0) return DSA_OK;
+    const size_t need = dsa_index_topk_workspace_size(n_rows, score_stride, top_k);
+    if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3) != 0) return DSA_ERR_WORKSPACE;
+    const size_t blocks = (size_t)n_rows * g.n_chunks;
+    char* ws = static_cast<char*>(workspace);
+    a.cand_key = reinterpret_cast<uint32_t*>(ws);
+    a.cand_slot = reinterpret_cast<int32_t*>(ws + blocks * g.cap * sizeof(uint32_t));
+    a.cand_count = a.cand_slot + blocks * g.cap;
+    a.cand_cut = a.cand_count + blocks;
+    a.top_k = top_k;
+    a.cand_cap = g.cap;
+    dsa::TopkArgs t{};
+    t.scores = scores; t.score_stride = score_stride; t.row_vis = row_vis;
+    t.n_rows = n_rows; t.top_k = top_k; t.n_splits = g.n_chunks;
+    t.cand_key = a.cand_key; t.cand_slot = a.cand_slot; t.cand_count = a.cand_count; t.cand_cut = a.cand_cut;
+    t.cand_hist = nullptr; t.cand_cap = g.cap;
+    t.topk_idx = topk_idx; t.topk_count = topk_count; t.status = status;
+    if (phases & DSA_PHASE_SCORE) {
+        rc = launch_status(dsa::launch_index_scores(a, stream));
+        if (rc != DSA_OK) return rc;
+    }
+    if (phases & DSA_PHASE_SELECT) rc = launch_status(dsa::launch_topk_merge_cuts(t, stream));
+    return rc;
 }
 
 int dsa_cache_write(const uint16_t* latent, const uint16_t* rope, const uint16_t* index_k,
@@ -255,7 +331,7 @@ int topk_validate(const float* scores, int32_t score_stride, const int32_t* row_
 int topk_launch(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
                 int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes, int32_t* topk_idx,
                 int32_t* topk_count, int32_t* status, hipStream_t stream) {
-    TopkArgs a;
+    TopkArgs a{};
     a.scores = scores; a.score_stride = score_stride; a.row_vis = row_vis;
     a.n_rows = n_rows; a.top_k = top_k; a.n_splits = n_splits;
     a.cand_key = nullptr; a.cand_slot = nullptr; a.cand_count = nullptr; a.cand_cut = nullptr;

@@ -450,6 +450,130 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
     }
 }
 
+// ---------------------------------------------------------------------------
+// Top-k candidates in the decode epilogue (dsa_index_topk).
+//
+// The row's top k is a small part of it, and a chunk's scores are still in
+// LDS when they have gone out, so the chunk keeps its likely share of the top
+// k right there: every visible score at or above a cut of its own, as keys
+// and slots in slot order, for a merge that selects the row's top k from them.
+// Thread t holds the chunk's positions [t L, t L + L) in registers, and its
+// first key is one of S evenly spaced samples.  The chunk holds n of the
+// row's v visible tokens, so about mu = k S / v samples fall in the row's top
+// k; the cut is the sample of rank rho = ceil(mu + 4 sqrt(mu) + 4) from the
+// top, rounded down to 22 key bits, or 0 (keep all) when rho > S, and about
+// rho n / S keys pass it.  Keeping more than cand_cap
+// keys (only when many scores are equal) is reported as a count of -1.  None
+// of this decides the result: the merge checks that the candidates hold the
+// row's top k and otherwise selects from the scores.
+// ---------------------------------------------------------------------------
+
+constexpr int kKeepMax = kMaxChunk / 256;   // most keys per thread
+
+// Chunk j = [t0, t0 + cnt) of row r: its candidates into the workspace
+// block of (r, j).  Called by every thread after score_range, whose scores
+// stay in s.sc; the query codes are no longer needed, and their LDS holds the
+// samples.
+template <int NT>
+__device__ void keep_candidates(const IndexArgs& a, IndexSmem<1, NT>& s, int r, int j, int t0, int cnt) {
+    static_assert(NT == 256 && sizeof(s.q) >= NT * sizeof(uint32_t), "the samples fit the query codes' LDS");
+    constexpr int NW = NT / kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int v = s.vok[0];
+    const int n = min(max(v - t0, 0), cnt);   // the chunk's visible tokens
+    const size_t rj = (size_t)r * gridDim.x + j;
+    uint32_t* smp = reinterpret_cast<uint32_t*>(s.q);
+    int* tab = s.pre;   // kept keys per wavefront
+
+    // Keys per thread: a multiple of 4 (whole 16-byte LDS reads), so that
+    // NT L covers the chunk (L <= kKeepMax since cnt <= kMaxChunk).
+    const int L = (((cnt + NT - 1) / NT) + 3) & ~3;
+    const int base = tid * L;
+    const int mine = max(0, min(L, n - base));
+    uint32_t key[kKeepMax];
+    bool nan = false;
+#pragma unroll
+    for (int m = 0; m < kKeepMax / 4; ++m) {
+        float4 f = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (4 * m < mine) f = *reinterpret_cast<const float4*>(&s.sc[base + 4 * m]);
+        const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            nan |= (fv[e] != fv[e]) && 4 * m + e < mine;
+            key[4 * m + e] = monotone_key(fv[e]);
+        }
+    }
+    if (__ballot(nan) != 0ull && lane == 0) flag(a.status, DSA_DEV_NAN);
+    // Samples: thread t's first key, for the S threads that hold any; the
+    // rest read as key 0, which never rises above a real sample.
+    const int S = (n + L - 1) / L;
+    smp[tid] = mine > 0 ? key[0] : 0u;
+    __syncthreads();
+    const float mu = n > 0 ? (float)a.top_k * (float)S / (float)v : 0.0f;
+    const int rho = (int)ceilf(mu + 4.0f * sqrtf(mu) + 4.0f);
+    uint32_t cut = 0u;
+    if (rho <= S) {
+        // Every wavefront finds the rho-th largest sample on its own (no
+        // barrier): a radix select over the 22 top key bits, counting with
+        // ballots, lane l holding samples l + 64 i.  The cut is that sample
+        // with its low 10 bits cleared, so at least rho samples pass it.
+        uint32_t x[NT / kWave];
+#pragma unroll
+        for (int i = 0; i < NT / kWave; ++i) x[i] = smp[lane + kWave * i];
+        uint32_t need = (uint32_t)rho;
+#pragma unroll 1
+        for (int b = 31; b >= 10; --b) {
+            const uint32_t hi = ~0u << b;
+            const uint32_t cand = cut | (1u << b);
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < NT / kWave; ++i) c += (uint32_t)__popcll(__ballot((x[i] & hi) == cand));
+            if (c >= need) cut = cand;
+            else need -= c;
+        }
+    }
+
+    // Kept keys in slot order: a mask per thread, one wavefront scan, and the
+    // wavefronts' totals in LDS.
+    uint32_t km = 0u;
+#pragma unroll
+    for (int i = 0; i < kKeepMax; ++i) km |= (i < mine && key[i] >= cut ? 1u : 0u) << i;
+    const uint32_t c = (uint32_t)__popc(km);
+    const uint32_t inc = wave_inclusive_scan(c);
+    if (lane == kWave - 1) tab[w] = (int)inc;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+        before += q < w ? tab[q] : 0;
+        total += tab[q];
+    }
+    if (total > a.cand_cap) {
+        if (tid == 0) {
+            a.cand_count[rj] = -1;
+            a.cand_cut[rj] = (int)cut;
+        }
+        return;
+    }
+    uint32_t* ckey = a.cand_key + rj * a.cand_cap;
+    int32_t* cslot = a.cand_slot + rj * a.cand_cap;
+    uint32_t at = (uint32_t)before + inc - c;
+#pragma unroll
+    for (int i = 0; i < kKeepMax; ++i) {
+        if ((km >> i) & 1u) {
+            ckey[at] = key[i];
+            cslot[at] = t0 + base + i;
+            ++at;
+        }
+    }
+    if (tid == 0) {
+        a.cand_count[rj] = total;
+        a.cand_cut[rj] = (int)cut;
+    }
+}
+
 // Two launch shapes:
 //   chunked:  grid (chunks, groups) of 256-thread workgroups; a workgroup
 //             scores one chunk of a.chunk tokens of one group of G rows;
@@ -472,12 +596,14 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
 // long tail in which the younger one ran alone, one wavefront per SIMD; one
 // workgroup whose wavefronts claim tiles as they go ends them together, and
 // quantizes each group's queries once per unit instead of twice.
-template <int G>
+// kKeep (one row a group): the chunk's top-k candidates are kept as well.
+template <int G, bool kKeep>
 __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     __shared__ IndexSmem<G, 256> s;
     const int t0 = blockIdx.x * a.chunk;
-    score_range<G, 256, false>(a, s, blockIdx.y * G, t0, min(t0 + a.chunk, a.score_stride), 0, 0, blockIdx.x == 0,
-                               true);
+    const int t_end = min(t0 + a.chunk, a.score_stride);
+    score_range<G, 256, false>(a, s, blockIdx.y * G, t0, t_end, 0, 0, blockIdx.x == 0, true);
+    if constexpr (kKeep) keep_candidates<256>(a, s, blockIdx.y, blockIdx.x, t0, t_end - t0);
 }
 
 constexpr int kBalancedThreads = 768;
@@ -606,16 +732,25 @@ hipError_t launch_g(IndexArgs a, hipStream_t stream) {
             return hipGetLastError();
         }
     }
-    const int per_group = max(1, kResidentWgs / groups);
-    int chunk = (a.score_stride + per_group - 1) / per_group;
-    chunk = min(kMaxChunk, max(kMinChunk, (chunk + 255) & ~255));
-    a.chunk = chunk;
-    dim3 grid((a.score_stride + chunk - 1) / chunk, groups);
-    index_scores_kernel<G><<<grid, 256, 0, stream>>>(a);
+    a.chunk = index_chunk(groups, a.score_stride);
+    dim3 grid((a.score_stride + a.chunk - 1) / a.chunk, groups);
+    if constexpr (G == 1) {
+        if (a.cand_key != nullptr) {
+            index_scores_kernel<1, true><<<grid, 256, 0, stream>>>(a);
+            return hipGetLastError();
+        }
+    }
+    index_scores_kernel<G, false><<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int index_chunk(int groups, int score_stride) {
+    const int per_group = max(1, kResidentWgs / max(groups, 1));
+    const int chunk = (int)(((int64_t)score_stride + per_group - 1) / per_group);
+    return min(kMaxChunk, max(kMinChunk, (chunk + 255) & ~255));
+}
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
     if (a.n_rows == 0) return hipSuccess;

@@ -22,6 +22,15 @@ struct IndexArgs {
     int32_t score_stride;
     int32_t* status;
     int32_t chunk;     // chunked launch: tokens per workgroup (set by the launcher)
+    // Top-k candidates kept by the decode launch (one row a group), or
+    // cand_key == nullptr for scores only.  Chunk j of row r writes to block
+    // r * n_chunks + j: up to cand_cap keys and slots, their count (-1: more
+    // than cand_cap) and its cut.
+    uint32_t* cand_key;
+    int32_t* cand_slot;
+    int32_t* cand_count;
+    int32_t* cand_cut;
+    int32_t top_k, cand_cap;
 };
 
 struct TopkArgs {
@@ -34,6 +43,7 @@ struct TopkArgs {
     int32_t* cand_count;  // [n_rows, n_splits]: how many each split kept
     int32_t* cand_cut;    // [n_rows, n_splits]: the row's cut key, as each split used it
     int32_t* cand_hist;   // [n_rows, n_splits, 512]: histogram of each split's kept keys
+    int32_t cand_cap;     // candidates' block length per split (the merge of the indexer's candidates)
     int32_t* topk_idx;
     int32_t* topk_count;
     int32_t* status;
@@ -115,7 +125,12 @@ int topk_launch(const float* scores, int32_t score_stride, const int32_t* row_vi
 hipError_t launch_quantize_q(const uint16_t* q, int32_t n_pairs, uint8_t* code, float* scale,
                              hipStream_t stream);
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
+// Tokens per workgroup of the chunked indexer launch for `groups` row groups.
+int index_chunk(int groups, int score_stride);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+// Merge of the candidates the decode indexer kept (a.n_splits = its chunks
+// per row, a.cand_cap their block length; no histograms).
+hipError_t launch_topk_merge_cuts(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);

@@ -805,30 +805,38 @@ __device__ __forceinline__ void merge_select(const TopkArgs& a, TopkSmem& s, con
 // nc <= kSlotBase); the fast merge needs nc <= kSlotBase.
 constexpr int kSlotBase = kTopkMaxList / 2;
 
-// Fast merge, given the threshold bin b of the summed kept-key histograms
-// (need = how many keys of bin b belong to the top k, m = keys in bin b <=
-// 64): thread t holds list positions [t*per, t*per + per) of the kept keys
-// (in the staging buffer, slots at kSlotBase); one wavefront ranks bin b's
-// keys exactly and the selection is emitted in list order.
 template <int P>
-__device__ __forceinline__ void merge_fast(TopkSmem& s, int nc, int k, uint32_t cut, int bstar, uint32_t need,
-                                           uint32_t m, int32_t* out_idx, int& tog) {
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
+__device__ __forceinline__ void emit_slots(TopkSmem& s, const uint32_t (&key)[P], int base, int mine, uint32_t thr,
+                                           uint32_t need_eq, int k, int32_t* out_idx, int& tog);
+
+// Keys of list positions [base, base + mine) of the staged candidates (keys
+// at stage_index) into registers; per = keys_per_thread(nc).
+template <int P>
+__device__ __forceinline__ void load_staged(const TopkSmem& s, int nc, uint32_t (&key)[P], int& base, int& mine) {
     const int per = keys_per_thread(nc);
-    const int base = tid * per;
-    const int mine = max(0, min(per, nc - base));
-    uint32_t key[P];
+    base = (int)threadIdx.x * per;
+    mine = max(0, min(per, nc - base));
 #pragma unroll
     for (int i = 0; i < P; ++i) {
         const uint32_t x = s.u.stage[stage_index(min(base + i, kSlotBase - 1))];
         key[i] = i < mine ? x : 0u;
     }
+}
+
+// The top k of the staged candidates, given a set of them (the keys for
+// which inb holds, m <= 64 of them) that holds the k-th largest key as its
+// need-th largest: one wavefront ranks the set exactly, then the selection
+// is emitted in list order.
+template <int P, typename InBin>
+__device__ __forceinline__ void rank_bin_emit(TopkSmem& s, const uint32_t (&key)[P], int base, int mine, int k,
+                                              uint32_t need, uint32_t m, InBin inb, int32_t* out_idx, int& tog) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
     if (tid == 0) s.bcount = 0u;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-        if (i < mine && kept_bin(key[i], cut) == bstar) {
+        if (i < mine && inb(key[i])) {
             const uint32_t at = atomicAdd(&s.bcount, 1u);
             s.bkey[min(at, (uint32_t)kWave - 1)] = key[i];
         }
@@ -848,8 +856,30 @@ __device__ __forceinline__ void merge_fast(TopkSmem& s, int nc, int k, uint32_t 
         }
     }
     __syncthreads();
-    const uint32_t thr = s.sel_thr, need_eq = s.sel_need_eq;
-    // Emission as in the direct selection, each position's slot from LDS.
+    emit_slots<P>(s, key, base, mine, s.sel_thr, s.sel_need_eq, k, out_idx, tog);
+}
+
+// Fast merge, given the threshold bin b of the summed kept-key histograms
+// (need = how many keys of bin b belong to the top k, m = keys in bin b <=
+// 64): thread t holds list positions [t*per, t*per + per) of the kept keys
+// (in the staging buffer, slots at kSlotBase); one wavefront ranks bin b's
+// keys exactly and the selection is emitted in list order.
+template <int P>
+__device__ __forceinline__ void merge_fast(TopkSmem& s, int nc, int k, uint32_t cut, int bstar, uint32_t need,
+                                           uint32_t m, int32_t* out_idx, int& tog) {
+    uint32_t key[P];
+    int base, mine;
+    load_staged<P>(s, nc, key, base, mine);
+    rank_bin_emit<P>(s, key, base, mine, k, need, m,
+                     [&](uint32_t x) { return x >= cut && kept_bin(x, cut) == bstar; }, out_idx, tog);
+}
+
+// Emission as in the direct selection (keys above thr, then the first
+// need_eq keys equal to it, in list order), each position's slot read from
+// the staging buffer at kSlotBase.
+template <int P>
+__device__ __forceinline__ void emit_slots(TopkSmem& s, const uint32_t (&key)[P], int base, int mine, uint32_t thr,
+                                           uint32_t need_eq, int k, int32_t* out_idx, int& tog) {
     uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
@@ -997,6 +1027,191 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     else merge_select<32>(a, s, off, ns, nc, k, out_idx, tog);
 }
 
+
+// Merge of the candidates that the decode indexer kept (dsa_index_topk):
+// grid (n_rows).  Chunk j of the row kept every visible key at or above its
+// own cut c_j (up to cand_cap of them, else count -1).  With C = max_j c_j,
+// every key of the row at or above C is a candidate; so when at least k
+// candidates are >= C, the row's k-th largest key T is >= C, every key >= T
+// is a candidate, and the top k of the candidates (in slot order, ties to
+// the lower slot) is the row's top k.  Rows where that does not hold, or
+// whose candidates do not fit the staging buffer, are selected from their
+// scores.  Candidates at or above C are binned by their top 16 key bits
+// relative to C; the bin of the k-th largest is ranked by one wavefront when
+// it holds at most 64 keys, else the general selection runs over all
+// candidates.
+constexpr int kMaxCutSplits = 1024;
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    return v;
+}
+
+// The bin of 512 (scanned from the largest) that holds the need-th largest
+// counted key: s.sel_digit, and s.sel_need = need minus the keys in the bins
+// above (0 and 0 when fewer than need keys are counted); *total = all counted.
+__device__ __forceinline__ void find_bin512(TopkSmem& s, const uint32_t* hist, uint32_t need, uint32_t* total,
+                                            int& tog) {
+    const int tid = threadIdx.x;
+    const uint32_t h = tid < kHistBins ? hist[kHistBins - 1 - tid] : 0u;
+    if (tid == 0) {
+        s.sel_digit = 0u;
+        s.sel_need = 0u;
+    }
+    const uint32_t above = scan2(s, h, total, tog);
+    if (tid < kHistBins && above < need && above + h >= need) {
+        s.sel_digit = (uint32_t)(kHistBins - 1 - tid);
+        s.sel_need = need - above;
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) void topk_merge_cuts_kernel(TopkArgs a) {
+    __shared__ TopkSmem s;
+    __shared__ int off[kMaxCutSplits + 1];
+    __shared__ uint32_t kmax_s;   // the largest candidate
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int k = a.top_k;
+    const int ns = a.n_splits;
+    const int cap = a.cand_cap;
+    int32_t* out_idx = a.topk_idx + (size_t)r * k;
+    const size_t rb = (size_t)r * ns;
+    const int v = checked_vis(a, r);
+    if (tid == 0) a.topk_count[r] = min(v, k);
+    if (v <= k) {
+        for (int i = tid; i < v; i += kThreads) out_idx[i] = i;
+        pad_tail(out_idx, v, k);
+        return;
+    }
+    // Counts, cuts and the first kSpec candidates of every chunk go out at
+    // once (kept lists are usually that short).
+    const int tps = kThreads / ns;   // threads per chunk for the speculative loads (ns <= kThreads)
+    constexpr int kSpec = 8;
+    const int sj = tid / tps, si = tid - sj * tps;
+    int cnt = 0;
+    uint32_t cut = 0u;
+    if (tid < ns) {
+        cnt = a.cand_count[rb + tid];
+        cut = (uint32_t)a.cand_cut[rb + tid];
+    }
+    uint32_t sk[kSpec];
+    int32_t ss[kSpec];
+#pragma unroll
+    for (int q = 0; q < kSpec; ++q) {
+        const int i = si + q * tps;
+        const bool ok = sj < ns && i < cap;
+        const size_t at = (rb + (size_t)(ok ? sj : 0)) * cap + (size_t)(ok ? i : 0);
+        sk[q] = a.cand_key[at];
+        ss[q] = a.cand_slot[at];
+    }
+    for (int b = tid; b < kHistBins; b += kThreads) s.khist[b] = 0u;
+    for (int b = tid; b < kBins0; b += kThreads) s.h0[b] = 0u;
+    if (tid == 0) {
+        s.sel_thr = 0u;   // C
+        s.bcount = 0u;    // a chunk overflowed
+        kmax_s = 0u;
+    }
+    __syncthreads();
+    const bool over = tid < ns && (cnt < 0 || cnt > cap);
+    if (tid < ns) atomicMax(&s.sel_thr, cut);
+    if (over) s.bcount = 1u;
+    int tog = 0;
+    uint32_t nc_u;
+    const uint32_t ex = scan2(s, over ? 0u : (uint32_t)max(cnt, 0), &nc_u, tog);
+    if (tid < ns) off[tid] = (int)ex;
+    if (tid == 0) off[ns] = (int)nc_u;
+    const uint32_t C = s.sel_thr;
+    const bool fall = s.bcount != 0u || nc_u < (uint32_t)k || nc_u > (uint32_t)kSlotBase;
+    __syncthreads();
+    const float* row = a.scores + (size_t)r * a.score_stride;
+    if (fall) {
+        topk_row_streamed(s, row, v, k, out_idx, tog);
+        return;
+    }
+    const int nc = (int)nc_u;
+    // Candidates (keys at stage_index, slots at kSlotBase) in list order, and
+    // the largest of them.
+    uint32_t kmax = 0u;
+    auto put = [&](int at, uint32_t key, int32_t slot) {
+        s.u.stage[stage_index(at)] = key;
+        s.u.stage[kSlotBase + at] = (uint32_t)slot;
+        kmax = max(kmax, key);
+    };
+    if (sj < ns) {
+        const int o = off[sj];
+        const int c = off[sj + 1] - o;
+#pragma unroll
+        for (int q = 0; q < kSpec; ++q) {
+            const int i = si + q * tps;
+            if (i < c) put(o + i, sk[q], ss[q]);
+        }
+        for (int i = si + kSpec * tps; i < c; i += tps)
+            put(o + i, a.cand_key[(rb + sj) * cap + i], a.cand_slot[(rb + sj) * cap + i]);
+    }
+    kmax = wave_max_u32(kmax);
+    if ((tid & (kWave - 1)) == 0) atomicMax(&kmax_s, kmax);
+    __syncthreads();
+    // Keys >= C in 512 bins of 2^s1 key values from C up, s1 the smallest
+    // shift that fits the largest candidate; the bin of the k-th largest;
+    // inside it, if it holds more than 64 keys, 512 bins of 2^s2 values.
+    const uint32_t range = kmax_s >= C ? kmax_s - C : 0u;
+    const int s1 = range == 0u ? 0 : max(0, 32 - __clz(range) - 9);
+    const int s2 = max(0, s1 - 9);
+    auto select = [&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        uint32_t key[P];
+        int base, mine;
+        load_staged<P>(s, nc, key, base, mine);
+        auto in_b0 = [&](uint32_t x) { return x >= C; };
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            if (i < mine && in_b0(key[i])) atomicAdd(&s.khist[(key[i] - C) >> s1], 1u);
+        __syncthreads();
+        uint32_t ge_c;
+        find_bin512(s, s.khist, (uint32_t)k, &ge_c, tog);
+        if (ge_c < (uint32_t)k) {   // fewer than k candidates >= C: the row's top k may lie below C
+            topk_row_streamed(s, row, v, k, out_idx, tog);
+            return;
+        }
+        if (nc == k) {   // every candidate is >= C and selected
+            for (int i = tid; i < nc; i += kThreads) out_idx[i] = (int32_t)s.u.stage[kSlotBase + i];
+            return;
+        }
+        const uint32_t bstar = s.sel_digit, need = s.sel_need, m = s.khist[bstar];
+        auto in_b = [&](uint32_t x) { return x >= C && ((x - C) >> s1) == bstar; };
+        if (m <= (uint32_t)kWave) {
+            rank_bin_emit<P>(s, key, base, mine, k, need, m, in_b, out_idx, tog);
+            return;
+        }
+        if (s1 > 0) {
+            // s.h0 is still zero.
+#pragma unroll
+            for (int i = 0; i < P; ++i)
+                if (i < mine && in_b(key[i])) atomicAdd(&s.h0[((key[i] - C) >> s2) & (kHistBins - 1)], 1u);
+            __syncthreads();
+            uint32_t tot;
+            find_bin512(s, s.h0, need, &tot, tog);
+            const uint32_t sb = s.sel_digit, need2 = s.sel_need, m2 = s.h0[sb];
+            if (tot == m && m2 <= (uint32_t)kWave) {
+                rank_bin_emit<P>(s, key, base, mine, k, need2, m2,
+                                 [&](uint32_t x) { return in_b(x) && (((x - C) >> s2) & (kHistBins - 1)) == sb; },
+                                 out_idx, tog);
+                return;
+            }
+            for (int b = tid; b < kHistBins; b += kThreads) s.h0[b] = 0u;
+        }
+        // General selection over every candidate (many equal keys).
+        __syncthreads();   // its histograms overwrite the staged keys (not the slots); s.h0 is zero
+        uint32_t thr, need_eq;
+        select_kth<P>(s, key, mine, nc, k, &thr, &need_eq, tog);
+        emit_slots<P>(s, key, base, mine, thr, need_eq, k, out_idx, tog);
+    };
+    if (nc <= 4 * kThreads) select(std::integral_constant<int, 4>{});
+    else if (nc <= 8 * kThreads) select(std::integral_constant<int, 8>{});
+    else select(std::integral_constant<int, 16>{});
+}
 }  // namespace
 
 namespace {
@@ -1037,6 +1252,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     });
     if (e != hipSuccess) return e;
     topk_merge_kernel<<<a.n_rows, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_merge_cuts(const TopkArgs& a, hipStream_t stream) {
+    if (a.n_rows == 0) return hipSuccess;
+    if (a.n_splits < 1 || a.n_splits > kMaxCutSplits || a.cand_cap < 1) return hipErrorInvalidValue;
+    topk_merge_cuts_kernel<<<a.n_rows, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

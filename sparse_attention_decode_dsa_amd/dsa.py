@@ -17,11 +17,12 @@ import os
 
 import torch
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE", 64: "SCALE"}
 DEV_PAGE_OOB, DEV_TOPK_OOB, DEV_ROW_RANGE, DEV_GROUP, DEV_NAN, DEV_WRITE, DEV_SCALE = 1, 2, 4, 8, 16, 32, 64
+PHASE_SCORE, PHASE_SELECT = 1, 2   # dsa_index_topk's halves
 
 
 class DsaError(RuntimeError):
@@ -37,6 +38,9 @@ _SIGS = {
     "dsa_quantize_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_index_scores": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
+    "dsa_index_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
+    "dsa_index_topk": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                        _p, _i32, _i32, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p], ctypes.c_int),
     "dsa_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
     "dsa_topk": ([_p, _i32, _p, _i32, _i32, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p], ctypes.c_int),
     "dsa_topk_noalloc": ([_p, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p], ctypes.c_int),
@@ -152,6 +156,46 @@ def index_scores(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_v
         _ptr(scores, torch.float32, "scores"), score_stride, _ptr(status, torch.int32, "status"),
         _stream(stream)), "dsa_index_scores")
     return scores, status
+
+
+def index_topk_workspace_size(n_rows: int, score_stride: int, top_k: int) -> int:
+    return int(lib().dsa_index_topk_workspace_size(n_rows, score_stride, top_k))
+
+
+def index_topk(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis, top_k: int,
+               score_stride: int | None = None, scores=None, workspace=None, topk_idx=None, topk_count=None,
+               status=None, stream=None, phases: int = 3):
+    """Decode rows' indexer scores and their exact top-k in one call
+    (dsa_index_topk) -> (scores, topk_idx, topk_count, status), the same
+    results as index_scores (one row a group) followed by topk.  phases:
+    PHASE_SCORE | PHASE_SELECT (both), or one of them on its own."""
+    r, h, d = q.shape
+    n_pages, p, dk = k_code.shape
+    batch, max_pages = page_table.shape
+    dev = q.device
+    if score_stride is None:
+        score_stride = scores.shape[1] if scores is not None else max_pages * p
+    if scores is None:
+        scores = torch.empty((r, score_stride), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((r, top_k), dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty((r,), dtype=torch.int32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    if workspace is None:
+        workspace = torch.empty((max(index_topk_workspace_size(r, score_stride, top_k), 1),),
+                                dtype=torch.uint8, device=dev)
+    _check(lib().dsa_index_topk(
+        _ptr(q, _BF16, "q"), _ptr(head_w, torch.float32, "head_w"), _ptr(k_code, _FP8, "k_code"),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(page_table, torch.int32, "page_table"),
+        _ptr(kv_lens, torch.int32, "kv_lens"), _ptr(row_req, torch.int32, "row_req"),
+        _ptr(row_vis, torch.int32, "row_vis"), r, batch, n_pages, max_pages, p, h, d,
+        _ptr(scores, torch.float32, "scores"), score_stride, top_k, phases, _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_count, torch.int32, "topk_count"), _ptr(status, torch.int32, "status"), _stream(stream)),
+        "dsa_index_topk")
+    return scores, topk_idx, topk_count, status
 
 
 def topk_workspace_size(n_rows: int, top_k: int, n_splits: int) -> int:
@@ -347,12 +391,17 @@ class DecodeStep:
 
     def __init__(self, inp, index_splits: int | None = None, attn_splits: int | None = None,
                  group_rows: int | None = None, score_stride: int | None = None,
-                 index_share: int | None = None):
+                 index_share: int | None = None, index_topk: bool | None = None):
         self.inp = inp
         cfg = inp.cfg
         self.index_splits = index_splits or cfg.index_splits
         self.attn_splits = attn_splits or cfg.attn_splits
         self.group_rows = group_rows or cfg.group_rows
+        # Rows scored one at a time take scores and top-k in one call
+        # (dsa_index_topk) unless a split count for dsa_topk is asked for.
+        if index_topk is None:
+            index_topk = index_splits is None and cfg.index_topk
+        self.index_topk = bool(index_topk) and self.group_rows == 1
         # MTP IndexShare: chains of `index_share` consecutive rows; only each
         # chain's first row is scored and selected, and every row attends
         # that list.  The first rows' inputs are gathered once, here.
@@ -377,7 +426,10 @@ class DecodeStep:
         # Rows start 16-byte aligned (the top-k then reads them in 16-byte loads).
         self.score_stride = score_stride or max(64, (int(self.lead_vis.max()) + 63) // 64 * 64)
         self.scores = torch.empty((n_sel, self.score_stride), dtype=torch.float32, device=dev)
-        need = topk_workspace_size(n_sel, k, self.index_splits)
+        if self.index_topk:
+            need = index_topk_workspace_size(n_sel, self.score_stride, k)
+        else:
+            need = topk_workspace_size(n_sel, k, self.index_splits)
         self.workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
         self.topk_idx = torch.empty((n_sel, k), dtype=torch.int32, device=dev)
         self.topk_count = torch.empty((n_sel,), dtype=torch.int32, device=dev)
@@ -390,12 +442,18 @@ class DecodeStep:
 
     def run(self, stream=None):
         i = self.inp
-        index_scores(self.lead_q, self.lead_w, i.k_code, i.k_scale, i.page_table,
-                     i.kv_lens, self.lead_req, self.lead_vis, group_rows=self.group_rows,
-                     score_stride=self.score_stride, scores=self.scores, status=self.status,
-                     stream=stream)
-        topk(self.scores, self.lead_vis, i.top_k, self.index_splits, workspace=self.workspace,
-             topk_idx=self.topk_idx, topk_count=self.topk_count, status=self.status, stream=stream)
+        if self.index_topk:
+            index_topk(self.lead_q, self.lead_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
+                       self.lead_req, self.lead_vis, i.top_k, score_stride=self.score_stride,
+                       scores=self.scores, workspace=self.workspace, topk_idx=self.topk_idx,
+                       topk_count=self.topk_count, status=self.status, stream=stream)
+        else:
+            index_scores(self.lead_q, self.lead_w, i.k_code, i.k_scale, i.page_table,
+                         i.kv_lens, self.lead_req, self.lead_vis, group_rows=self.group_rows,
+                         score_stride=self.score_stride, scores=self.scores, status=self.status,
+                         stream=stream)
+            topk(self.scores, self.lead_vis, i.top_k, self.index_splits, workspace=self.workspace,
+                 topk_idx=self.topk_idx, topk_count=self.topk_count, status=self.status, stream=stream)
         if self.row_list is not None:
             s = self.attn_splits
             sparse_mla_decode_shared(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,

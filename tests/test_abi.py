@@ -215,3 +215,42 @@ def test_bandwidth_library_exports_its_header():
     assert L.dsa_bw_stream_read(None, 4096, 8, P, None) == -1
     assert L.dsa_bw_stream_read(P, 4095, 8, P, None) == -1
     assert L.dsa_bw_copy(P, P + 8, 4096, 8, None) == -1
+
+
+def _itk(L, **kw):
+    a = dict(q=P, head_w=P, k_code=P, k_scale=P, page_table=P, kv_lens=P, row_req=P, row_vis=P, n_rows=4,
+             batch=2, num_pages=200, max_pages=128, page_size=256, n_heads=64, head_dim=128, scores=P,
+             score_stride=32768, top_k=2048, phases=3, workspace=P, workspace_bytes=1 << 30, topk_idx=P,
+             topk_count=P, status=P, stream=None)
+    a.update(kw)
+    return L.dsa_index_topk(*a.values())
+
+
+def test_index_topk_validation_and_workspace(L):
+    """dsa_index_topk applies dsa_index_scores' rules, the top-k's, its own
+    phase and chunk-count rules, then checks the workspace, all before any
+    HIP call."""
+    # 4 rows x 32768 slots: 1024-token chunks (the indexer's smallest), 32 a
+    # row, each holding up to min(1024, k) candidate keys and slots, a count
+    # and a cut.
+    assert L.dsa_index_topk_workspace_size(4, 32768, 2048) == 4 * 32 * (2 * 1024 + 2) * 4
+    # 64 rows x 32768 slots: 4096-token chunks, 8 a row, k = 2048 candidates each.
+    assert L.dsa_index_topk_workspace_size(64, 32768, 2048) == 64 * 8 * (2 * 2048 + 2) * 4
+    assert L.dsa_index_topk_workspace_size(0, 32768, 2048) == 0
+    need = L.dsa_index_topk_workspace_size(4, 32768, 2048)
+    assert _itk(L, n_heads=32) == UNSUP
+    assert _itk(L, page_size=100) == UNSUP
+    assert _itk(L, n_rows=-1) == SHAPE
+    assert _itk(L, top_k=0) == SHAPE
+    assert _itk(L, top_k=8193) == SHAPE
+    assert _itk(L, phases=0) == SHAPE
+    assert _itk(L, phases=4) == SHAPE
+    assert _itk(L, n_rows=1, score_stride=8192 * 1024 + 1, max_pages=40000) == SHAPE   # 1025 chunks
+    assert _itk(L, q=None) == NULL
+    assert _itk(L, scores=None) == NULL
+    assert _itk(L, topk_idx=None) == NULL
+    assert _itk(L, topk_count=None) == NULL
+    assert _itk(L, workspace=None) == WS
+    assert _itk(L, workspace_bytes=need - 1) == WS
+    assert _itk(L, workspace=P + 2) == WS
+    assert _itk(L, n_rows=0) == OK
