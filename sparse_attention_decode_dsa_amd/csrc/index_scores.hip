@@ -461,8 +461,8 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
 // first key is one of S evenly spaced samples.  The chunk holds n of the
 // row's v visible tokens, so about mu = k S / v samples fall in the row's top
 // k; the cut is the sample of rank rho = ceil(mu + 4 sqrt(mu) + 4) from the
-// top, rounded down to 22 key bits, or 0 (keep all) when rho > S, and about
-// rho n / S keys pass it.  Keeping more than cand_cap
+// top, rounded down to 14 bits below the highest bit in which the samples
+// differ, or 0 (keep all) when rho > S, and about rho n / S keys pass it.  Keeping more than cand_cap
 // keys (only when many scores are equal) is reported as a count of -1.  None
 // of this decides the result: the merge checks that the candidates hold the
 // row's top k and otherwise selects from the scores.
@@ -478,6 +478,9 @@ template <int NT>
 __device__ void keep_candidates(const IndexArgs& a, IndexSmem<1, NT>& s, int r, int j, int t0, int cnt) {
     static_assert(NT == 256 && sizeof(s.q) >= NT * sizeof(uint32_t), "the samples fit the query codes' LDS");
     constexpr int NW = NT / kWave;
+    // The compute unit's other workgroup is usually still in its main loop;
+    // this short tail goes first.
+    __builtin_amdgcn_s_setprio(3);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
@@ -516,22 +519,38 @@ __device__ void keep_candidates(const IndexArgs& a, IndexSmem<1, NT>& s, int r, 
     uint32_t cut = 0u;
     if (rho <= S) {
         // Every wavefront finds the rho-th largest sample on its own (no
-        // barrier): a radix select over the 22 top key bits, counting with
-        // ballots, lane l holding samples l + 64 i.  The cut is that sample
-        // with its low 10 bits cleared, so at least rho samples pass it.
+        // barrier), lane l holding samples l + 64 i.  Below the bits that
+        // all samples share, two bits a step: the largest t on the step's
+        // grid with at least rho samples >= t (counted with ballots) becomes
+        // the cut.  Fourteen bits below the first one that differs, the cut
+        // sits at or below the rho-th largest sample, so at least rho
+        // samples pass it.
         uint32_t x[NT / kWave];
+        uint32_t hi = 0u, lo = ~0u;
 #pragma unroll
-        for (int i = 0; i < NT / kWave; ++i) x[i] = smp[lane + kWave * i];
-        uint32_t need = (uint32_t)rho;
-#pragma unroll 1
-        for (int b = 31; b >= 10; --b) {
-            const uint32_t hi = ~0u << b;
-            const uint32_t cand = cut | (1u << b);
+        for (int i = 0; i < NT / kWave; ++i) {
+            x[i] = smp[lane + kWave * i];
+            hi = max(hi, x[i]);
+            lo = min(lo, x[i]);
+        }
+        hi = wave_max_u32(hi);
+        lo = wave_min_u32(lo);
+        const int top = hi == lo ? -1 : 31 - __clz(hi ^ lo);   // highest bit the samples differ in
+        cut = top < 0 ? hi : hi & ~((2u << top) - 1u);
+        auto count_ge = [&](uint32_t t) {
             uint32_t c = 0;
 #pragma unroll
-            for (int i = 0; i < NT / kWave; ++i) c += (uint32_t)__popcll(__ballot((x[i] & hi) == cand));
-            if (c >= need) cut = cand;
-            else need -= c;
+            for (int i = 0; i < NT / kWave; ++i) c += (uint32_t)__popcll(__ballot(x[i] >= t));
+            return c;
+        };
+#pragma unroll 1
+        for (int b = top; b >= max(top - 13, 0); b -= 2) {
+            const int sh = max(b - 1, 0);   // the step's lowest bit (one bit when b == 0)
+            const uint32_t t3 = cut | (3u << sh), t2 = cut | (2u << sh), t1 = cut | (1u << sh);
+            const uint32_t c3 = b > 0 ? count_ge(t3) : 0u;
+            const uint32_t c2 = b > 0 ? count_ge(t2) : 0u;
+            const uint32_t c1 = count_ge(t1);
+            cut = c3 >= (uint32_t)rho ? t3 : c2 >= (uint32_t)rho ? t2 : c1 >= (uint32_t)rho ? t1 : cut;
         }
     }
 
@@ -557,15 +576,33 @@ __device__ void keep_candidates(const IndexArgs& a, IndexSmem<1, NT>& s, int r, 
         }
         return;
     }
+    // The kept keys and their positions go to LDS in order (the scores there
+    // are in registers by now), then out in coalesced stores; a list too
+    // long for that goes out directly.
     uint32_t* ckey = a.cand_key + rj * a.cand_cap;
     int32_t* cslot = a.cand_slot + rj * a.cand_cap;
+    uint32_t* stk = reinterpret_cast<uint32_t*>(s.sc);
+    constexpr int kHalf = kMaxChunk / 2;
+    const bool staged = total <= kHalf;
     uint32_t at = (uint32_t)before + inc - c;
 #pragma unroll
     for (int i = 0; i < kKeepMax; ++i) {
         if ((km >> i) & 1u) {
-            ckey[at] = key[i];
-            cslot[at] = t0 + base + i;
+            if (staged) {
+                stk[at] = key[i];
+                stk[kHalf + at] = (uint32_t)(base + i);
+            } else {
+                ckey[at] = key[i];
+                cslot[at] = t0 + base + i;
+            }
             ++at;
+        }
+    }
+    if (staged) {
+        __syncthreads();
+        for (int i = tid; i < total; i += NT) {
+            ckey[i] = stk[i];
+            cslot[i] = t0 + (int)stk[kHalf + i];
         }
     }
     if (tid == 0) {

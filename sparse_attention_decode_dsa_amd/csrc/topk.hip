@@ -1042,12 +1042,6 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
 // candidates.
 constexpr int kMaxCutSplits = 1024;
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-    return v;
-}
-
 // The bin of 512 (scanned from the largest) that holds the need-th largest
 // counted key: s.sel_digit, and s.sel_need = need minus the keys in the bins
 // above (0 and 0 when fewer than need keys are counted); *total = all counted.
