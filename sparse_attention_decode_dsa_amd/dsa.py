@@ -397,8 +397,9 @@ class DecodeStep:
         self.index_splits = index_splits or cfg.index_splits
         self.attn_splits = attn_splits or cfg.attn_splits
         self.group_rows = group_rows or cfg.group_rows
-        # Rows scored one at a time take scores and top-k in one call
-        # (dsa_index_topk) unless a split count for dsa_topk is asked for.
+        # index_topk: rows scored one at a time take scores and top-k in one
+        # call (dsa_index_topk); the default is the configuration's (the two
+        # calls, which measure as fast at the step level).
         if index_topk is None:
             index_topk = index_splits is None and cfg.index_topk
         self.index_topk = bool(index_topk) and self.group_rows == 1

@@ -72,7 +72,7 @@ class Config:
     planted_factor: float = 8.0
     group_rows: int = 1                   # rows scored together against one key stream
     index_share: int = 0                  # MTP IndexShare: rows per chain sharing one top-k list
-    index_topk: bool = True               # rows scored one at a time: scores and top-k in one call
+    index_topk: bool = False              # rows scored one at a time: scores and top-k in one call
 
 
 CONFIGS = {

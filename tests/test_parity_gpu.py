@@ -274,6 +274,20 @@ def test_bulk_decode_sampled_rows(name):
     mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
 
 
+def test_bulk_decode_step_with_index_topk_sampled_rows():
+    """The step with scores and top-k from one dsa_index_topk call (the
+    indexer keeps candidates, a merge selects), on sampled rows against the
+    oracle."""
+    inp = W.make("c1_l32k", device="cuda")
+    step = dsa.DecodeStep(inp, index_topk=True)
+    assert step.index_topk
+    step.run()
+    torch.cuda.synchronize()
+    dsa.check_status(step.status)
+    ref, sub, swapped = compare_step(inp, step, [0, 17, 40, 63], max_swap_rows=2)
+    say(f"c1_l32k fused: swapped {swapped}")
+
+
 # ------------------------------------------------------------------ edge rows, page sizes, strides
 
 EDGE_DECODE = W.Config("edge_decode", batch=10, kv_lens=(0, 1, 63, 64, 65, 2047, 2048, 2049, 5000, 777),

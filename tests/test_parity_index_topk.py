@@ -149,7 +149,7 @@ def test_index_topk_full_size_equals_two_calls(name, n_splits):
     in the launch configuration the step uses: the fused call against the two
     calls (the oracle checks sampled rows of the same step elsewhere)."""
     inp = W.make(name, device="cuda")
-    st = dsa.DecodeStep(inp)
+    st = dsa.DecodeStep(inp, index_topk=True)
     assert st.index_topk
     say(f"{name}: R={inp.n_rows} stride={st.score_stride}")
     a = fused(inp, inp.top_k, st.score_stride)
@@ -161,7 +161,7 @@ def test_index_topk_phases_apart_equal_the_whole_call():
     """DSA_PHASE_SCORE then DSA_PHASE_SELECT on one workspace gives what one
     call with both gives; a select phase run again gives the same again."""
     inp = W.make("c1", device="cuda")
-    st = dsa.DecodeStep(inp)
+    st = dsa.DecodeStep(inp, index_topk=True)
     k, stride = inp.top_k, st.score_stride
     want = fused(inp, k, stride)
     ws = torch.empty((dsa.index_topk_workspace_size(inp.n_rows, stride, k),), dtype=torch.uint8, device="cuda")
