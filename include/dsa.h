@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 9
+#define DSA_ABI_VERSION 10
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -287,6 +287,27 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
              int32_t* topk_idx, int32_t* topk_count, int32_t* status, hipStream_t stream);
 
 /*
+ * dsa_topk_rows -- dsa_topk that also emits, for each selected slot, its
+ * physical row in the paged caches (subject page, Modifications, indexer
+ * decode: the merge emits the KV rows directly, so the attention needs no
+ * per-layer page-table transform).  The selection, topk_idx and topk_count
+ * are dsa_topk's, bit for bit; in addition
+ *   topk_rows [n_rows, top_k] i32 out: page_table[b][t / page_size] *
+ *     page_size + t % page_size for each selected slot t of row r (b =
+ *     row_req[r]), -1 after topk_count[r].
+ * A slot whose page id lies outside [0, num_pages) gets -1 and
+ * DSA_DEV_PAGE_OOB; a row whose request lies outside [0, batch), or whose
+ * span exceeds max_pages * page_size, gets -1 rows and DSA_DEV_ROW_RANGE.
+ * The block-table row of each request is read once per row.
+ *   row_req [n_rows] i32, page_table [batch, max_pages] i32 (as for the
+ *   attention); other arguments, limits and the workspace as dsa_topk.
+ */
+int dsa_topk_rows(const float* scores, int32_t score_stride, const int32_t* row_vis, const int32_t* row_req,
+                  const int32_t* page_table, int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
+                  int32_t n_rows, int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                  int32_t* topk_idx, int32_t* topk_count, int32_t* topk_rows, int32_t* status, hipStream_t stream);
+
+/*
  * dsa_topk_noalloc -- dsa_topk for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, rules and results as dsa_topk, without the
@@ -340,6 +361,29 @@ int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int3
                           int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
                           float* part_o, float* part_lse, uint16_t* out, float* out_lse,
                           int32_t* status, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_decode_rows -- dsa_sparse_mla_decode over lists of physical
+ * rows (dsa_topk_rows' topk_rows) instead of slots: no block table is read,
+ * so the gathers start as soon as a split's entries arrive (subject page,
+ * Modifications, indexer decode: the merge emits the KV rows directly).
+ * Row r attends the rows topk_rows[r][0 .. topk_count[r]) with the same
+ * splits, arithmetic and outputs as dsa_sparse_mla_decode; given the rows
+ * dsa_topk_rows emits for a selection, the results equal
+ * dsa_sparse_mla_decode's on that selection, bit for bit.  An entry of -1
+ * (a slot on an invalid page, already reported by the top-k) is left out; an
+ * entry below -1 or at or past num_pages * page_size is left out and sets
+ * DSA_DEV_TOPK_OOB; a count above top_k or row_vis[r] empties the row
+ * (DSA_DEV_TOPK_OOB).
+ *   q, kv_cache, outputs, limits: as dsa_sparse_mla_decode
+ *   row_vis [n_rows] i32 (bounds the count), topk_rows [n_rows, top_k] i32,
+ *   topk_count [n_rows] i32
+ */
+int dsa_sparse_mla_decode_rows(const uint16_t* q, const uint8_t* kv_cache, const int32_t* row_vis,
+                               const int32_t* topk_rows, const int32_t* topk_count, int32_t n_rows,
+                               int32_t num_pages, int32_t page_size, int32_t n_heads, int32_t top_k,
+                               int32_t n_splits, float sm_scale, float* part_o, float* part_lse, uint16_t* out,
+                               float* out_lse, int32_t* status, hipStream_t stream);
 
 /*
  * dsa_sparse_mla_decode_shared -- dsa_sparse_mla_decode where rows share

@@ -48,7 +48,7 @@ int mla_checked(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_
                 const int32_t* topk_count, int32_t n_lists, int32_t n_rows, int32_t batch, int32_t num_pages,
                 int32_t max_pages, int32_t page_size, int32_t n_heads, int32_t top_k, int32_t n_splits,
                 float sm_scale, float* part_o, float* part_lse, uint16_t* out, float* out_lse, int32_t* status,
-                hipStream_t stream) {
+                hipStream_t stream, const int32_t* topk_rows = nullptr) {
     if (n_rows < 0 || n_rows > kMaxRows || n_heads < 1) return DSA_ERR_SHAPE;
     if (top_k < 1 || top_k > dsa::kTopkMaxK) return DSA_ERR_SHAPE;
     if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
@@ -56,12 +56,15 @@ int mla_checked(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_
     if (n_heads != 16 && n_heads != 32) return DSA_ERR_UNSUPPORTED;
     int rc = check_page_geometry(batch, num_pages, max_pages, page_size);
     if (rc != DSA_OK) return rc;
-    if (!q || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx ||
-        !topk_count || !status)
+    if (topk_rows != nullptr) {   // physical rows: no block table is read
+        if (!q || !kv_cache || !row_vis || !topk_count || !status) return DSA_ERR_NULL;
+    } else if (!q || !kv_cache || !page_table || !row_req || !row_vis || !topk_idx || !topk_count || !status) {
         return DSA_ERR_NULL;
+    }
     if (n_splits == 1 ? !out : (!part_o || !part_lse)) return DSA_ERR_NULL;
     if (n_rows == 0) return DSA_OK;
-    dsa::MlaArgs a;
+    dsa::MlaArgs a{};
+    a.topk_rows = topk_rows;
     a.q = q; a.kv_cache = kv_cache; a.page_table = page_table;
     a.row_req = row_req; a.row_vis = row_vis; a.topk_idx = topk_idx; a.topk_count = topk_count;
     a.n_rows = n_rows; a.batch = batch; a.num_pages = num_pages; a.max_pages = max_pages;
@@ -272,6 +275,37 @@ int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, 
                             topk_idx, topk_count, status, stream);
 }
 
+int dsa_topk_rows(const float* scores, int32_t score_stride, const int32_t* row_vis, const int32_t* row_req,
+                  const int32_t* page_table, int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
+                  int32_t n_rows, int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                  int32_t* topk_idx, int32_t* topk_count, int32_t* topk_rows, int32_t* status, hipStream_t stream) {
+    int rc = dsa::topk_validate(scores, score_stride, row_vis, n_rows, top_k, n_splits, topk_idx, topk_count,
+                                status);
+    if (rc != DSA_OK) return rc;
+    rc = check_page_geometry(batch, num_pages, max_pages, page_size);
+    if (rc != DSA_OK) return rc;
+    if (!row_req || !page_table || !topk_rows) return DSA_ERR_NULL;
+    if (n_rows == 0) return DSA_OK;
+    dsa::TopkArgs r{};
+    r.topk_rows = topk_rows; r.row_req = row_req; r.page_table = page_table;
+    r.batch = batch; r.num_pages = num_pages; r.max_pages = max_pages;
+    r.page_size = page_size; r.log2_page = log2i(page_size);
+    return dsa::topk_launch(scores, score_stride, row_vis, n_rows, top_k, n_splits, workspace, workspace_bytes,
+                            topk_idx, topk_count, status, stream, &r);
+}
+
+int dsa_sparse_mla_decode_rows(const uint16_t* q, const uint8_t* kv_cache, const int32_t* row_vis,
+                               const int32_t* topk_rows, const int32_t* topk_count, int32_t n_rows,
+                               int32_t num_pages, int32_t page_size, int32_t n_heads, int32_t top_k,
+                               int32_t n_splits, float sm_scale, float* part_o, float* part_lse, uint16_t* out,
+                               float* out_lse, int32_t* status, hipStream_t stream) {
+    if (!topk_rows) return DSA_ERR_NULL;
+    // One request of one page: the geometry a physical-row list needs.
+    return mla_checked(q, kv_cache, nullptr, nullptr, row_vis, nullptr, nullptr, topk_count, n_rows, n_rows, 1,
+                       num_pages, 1, page_size, n_heads, top_k, n_splits, sm_scale, part_o, part_lse, out, out_lse,
+                       status, stream, topk_rows);
+}
+
 int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_table,
                           const int32_t* row_req, const int32_t* row_vis, const int32_t* topk_idx,
                           const int32_t* topk_count, int32_t n_rows,
@@ -330,8 +364,13 @@ int topk_validate(const float* scores, int32_t score_stride, const int32_t* row_
 
 int topk_launch(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
                 int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes, int32_t* topk_idx,
-                int32_t* topk_count, int32_t* status, hipStream_t stream) {
+                int32_t* topk_count, int32_t* status, hipStream_t stream, const TopkArgs* rows) {
     TopkArgs a{};
+    if (rows != nullptr) {
+        a.topk_rows = rows->topk_rows; a.row_req = rows->row_req; a.page_table = rows->page_table;
+        a.batch = rows->batch; a.num_pages = rows->num_pages; a.max_pages = rows->max_pages;
+        a.page_size = rows->page_size; a.log2_page = rows->log2_page;
+    }
     a.scores = scores; a.score_stride = score_stride; a.row_vis = row_vis;
     a.n_rows = n_rows; a.top_k = top_k; a.n_splits = n_splits;
     a.cand_key = nullptr; a.cand_slot = nullptr; a.cand_count = nullptr; a.cand_cut = nullptr;

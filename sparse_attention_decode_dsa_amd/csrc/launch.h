@@ -47,6 +47,12 @@ struct TopkArgs {
     int32_t* topk_idx;
     int32_t* topk_count;
     int32_t* status;
+    // Physical rows of the selected slots (nullptr: not asked for), through
+    // row r's request row_req[r] and the block table.
+    int32_t* topk_rows;
+    const int32_t* row_req;
+    const int32_t* page_table;
+    int32_t batch, num_pages, max_pages, page_size, log2_page;
 };
 
 struct MlaArgs {
@@ -57,6 +63,9 @@ struct MlaArgs {
     const int32_t* row_vis;
     const int32_t* topk_idx;
     const int32_t* topk_count;
+    // Physical rows of the list entries instead of slots (nullptr: topk_idx
+    // holds slots, resolved through the block table).
+    const int32_t* topk_rows;
     int32_t n_rows, batch, num_pages, max_pages, page_size, log2_page, n_heads, top_k, n_splits;
     float sm_scale;
     float* part_o;
@@ -120,7 +129,7 @@ int topk_validate(const float* scores, int32_t score_stride, const int32_t* row_
                   const int32_t* status);
 int topk_launch(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
                 int32_t top_k, int32_t n_splits, void* workspace, size_t workspace_bytes, int32_t* topk_idx,
-                int32_t* topk_count, int32_t* status, hipStream_t stream);
+                int32_t* topk_count, int32_t* status, hipStream_t stream, const TopkArgs* rows = nullptr);
 
 hipError_t launch_quantize_q(const uint16_t* q, int32_t n_pairs, uint8_t* code, float* scale,
                              hipStream_t stream);

@@ -195,7 +195,9 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     // Row metadata (uniform loads) and the split's range of the selected
     // list.  The range depends only on top_k, so the list entries can be
     // loaded together with the metadata.
-    const int b_raw = a.row_req[r];
+    // rows: the list holds physical rows (no request, no block table).
+    const bool rows = a.topk_rows != nullptr;
+    const int b_raw = rows ? 0 : a.row_req[r];
     const int v_raw = a.row_vis[r];
     // The list this row attends: its own, or the shared one row_list names.
     const int list_raw = a.row_list != nullptr ? a.row_list[r] : r;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     const int chunk = (a.top_k + ns - 1) / ns;
     const int lo = min(a.top_k, sp * chunk);
     const int hi_list = min(a.top_k, lo + chunk);
-    const int32_t* sel = a.topk_idx + (size_t)list * a.top_k;
+    const int32_t* sel = (rows ? a.topk_rows : a.topk_idx) + (size_t)list * a.top_k;
 
     // First batch of list entries (8 per thread), issued before anything
     // else; indexes are clamped into the list.
@@ -218,7 +220,8 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     };
     load_slots(lo);
 
-    bool ok = b_raw >= 0 && b_raw < a.batch && v_raw >= 0 && v_raw <= a.max_pages * a.page_size && list_ok;
+    bool ok = (rows || (b_raw >= 0 && b_raw < a.batch && v_raw <= a.max_pages * a.page_size)) && v_raw >= 0 &&
+              list_ok;
     if (!ok && tid == 0) flag(a.status, DSA_DEV_ROW_RANGE);
     if (ok && (c_raw < 0 || c_raw > a.top_k || c_raw > v_raw)) {
         if (tid == 0) flag(a.status, DSA_DEV_TOPK_OOB);
@@ -235,7 +238,22 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     // their indexes are clamped into the table so that they need no branch,
     // and validity is decided afterwards.
     bool bad = false;
+    const int64_t pool_rows = (int64_t)a.num_pages * a.page_size;
     auto walk = [&](int base) {
+        if (rows) {   // physical rows given: -1 (left out by the top-k) stays out quietly
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = base + NT * u + tid;
+                if (base + NT * u < hi && e < hi) {
+                    int32_t row = slot[u];
+                    if (row < -1 || (int64_t)row >= pool_rows) flag(a.status, DSA_DEV_TOPK_OOB);
+                    if (row < 0 || (int64_t)row >= pool_rows) row = -1;
+                    bad |= row < 0;
+                    s_rows[e - lo] = row;
+                }
+            }
+            return;
+        }
         int page[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)

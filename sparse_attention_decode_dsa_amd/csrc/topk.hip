@@ -77,9 +77,72 @@ struct TopkSmem {
     uint32_t sel_digit;
     uint32_t sel_digit2;
     uint32_t sel_need;
+    int32_t pt[1024];      // physical rows asked for: the row's request's page ids, when they fit
 };
+constexpr int kPtLds = 1024;
 
 __device__ __forceinline__ uint32_t bin0(uint32_t key) { return key >> 20; }
+
+// Where a row's selection goes: its slots, and when asked (rows != nullptr)
+// the physical row of each slot through the row's request's block table
+// (pt: page ids, staged in LDS when they fit; nullptr when the request is
+// invalid, which gives -1).  A slot whose page id is outside the pool gives
+// -1 and DSA_DEV_PAGE_OOB.
+template <bool kRows>
+struct OutRow {
+    static constexpr bool kHasRows = kRows;   // the launch asked for physical rows
+    int32_t* idx;
+    int32_t* rows;
+    const int32_t* pt;
+    int32_t* status;
+    int num_pages, page_size, log2_page, max_pages;
+    __device__ __forceinline__ int row_of(int slot) const {
+        if (pt == nullptr) return -1;
+        const int p = slot >> log2_page;
+        const int page = p < max_pages ? pt[p] : -1;
+        if (page < 0 || page >= num_pages) {
+            flag(status, DSA_DEV_PAGE_OOB);
+            return -1;
+        }
+        return page * page_size + (slot & (page_size - 1));
+    }
+    __device__ __forceinline__ void put(int rank, int slot) const {
+        idx[rank] = slot;
+        if constexpr (kRows) rows[rank] = row_of(slot);
+    }
+};
+
+// Row r's output; with physical rows asked for, the page ids of its request
+// start loading into LDS (every user of them comes after a barrier).  v: the
+// row's checked span.
+template <bool kRows>
+__device__ __forceinline__ OutRow<kRows> make_out(const TopkArgs& a, TopkSmem& s, int r, int v) {
+    OutRow<kRows> o;
+    o.idx = a.topk_idx + (size_t)r * a.top_k;
+    if constexpr (kRows) {
+        o.rows = a.topk_rows + (size_t)r * a.top_k;
+        o.pt = nullptr;
+        o.status = a.status;
+        o.num_pages = a.num_pages;
+        o.page_size = a.page_size;
+        o.log2_page = a.log2_page;
+        o.max_pages = a.max_pages;
+        const int b = a.row_req[r];
+        if (b < 0 || b >= a.batch || (int64_t)v > (int64_t)a.max_pages * a.page_size) {
+            if (threadIdx.x == 0) flag(a.status, DSA_DEV_ROW_RANGE);
+        } else {
+            const int32_t* g = a.page_table + (size_t)b * a.max_pages;
+            if (a.max_pages <= kPtLds) {
+                for (int i = threadIdx.x; i < a.max_pages; i += kThreads) s.pt[i] = g[i];
+                o.pt = s.pt;
+            } else {
+                o.pt = g;
+            }
+        }
+    }
+    return o;
+}
+
 
 // Keys per thread for a list of n: a multiple of 4 (whole 16-byte chunks),
 // at most kPer.
@@ -382,9 +445,9 @@ __device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[P
 // Direct emission (one split): the same selection as emit_to_lds, but each
 // thread walks only the set bits of its taken-key mask and writes the list
 // positions straight to `out` at their ranks.
-template <int P>
+template <int P, typename Out>
 __device__ __forceinline__ void emit_direct(TopkSmem& s, const uint32_t (&key)[P], int base, uint32_t thr,
-                                            uint32_t need_eq, int k, int32_t* out, int lo, int& tog) {
+                                            uint32_t need_eq, int k, const Out& out, int lo, int& tog) {
     const uint32_t eq_key = thr != 0u ? thr : 0xFFFFFFFFu;
     const bool eq_ok = thr != 0u;
     uint32_t gtm = 0u, eqm = 0u;
@@ -406,7 +469,7 @@ __device__ __forceinline__ void emit_direct(TopkSmem& s, const uint32_t (&key)[P
     while (tm != 0u) {
         const int i = __ffs(tm) - 1;
         tm &= tm - 1u;
-        if (rank < (uint32_t)k) out[rank] = lo + base + i;
+        if (rank < (uint32_t)k) out.put(rank, lo + base + i);
         ++rank;
     }
 }
@@ -504,8 +567,20 @@ __device__ __forceinline__ int checked_vis(const TopkArgs& a, int r) {
     return v;
 }
 
-__device__ __forceinline__ void pad_tail(int32_t* out, int from, int k) {
-    for (int i = from + threadIdx.x; i < k; i += kThreads) out[i] = -1;
+// Slots only: nothing but the output row.
+template <>
+struct OutRow<false> {
+    static constexpr bool kHasRows = false;
+    int32_t* idx;
+    __device__ __forceinline__ void put(int rank, int slot) const { idx[rank] = slot; }
+};
+
+template <typename Out>
+__device__ __forceinline__ void pad_tail(const Out& o, int from, int k) {
+    for (int i = from + threadIdx.x; i < k; i += kThreads) {
+        o.idx[i] = -1;
+        if constexpr (Out::kHasRows) o.rows[i] = -1;
+    }
 }
 
 // Split j of a row with `v` visible slots: [lo, hi) with split length
@@ -521,7 +596,7 @@ __device__ __forceinline__ SplitRange split_range(int v, int ns, int j) {
 
 // Whole row, one split: grid (1, n_rows); no row is longer than P keys per
 // thread.
-template <int P>
+template <int P, bool kRows>
 __global__ __launch_bounds__(kThreads) void topk_direct_kernel(TopkArgs a) {
     __shared__ TopkSmem s;
     const int r = blockIdx.y;
@@ -529,10 +604,11 @@ __global__ __launch_bounds__(kThreads) void topk_direct_kernel(TopkArgs a) {
     const int k = a.top_k;
     if (threadIdx.x == 0) a.topk_count[r] = min(n, k);
     const float* src = a.scores + (size_t)r * a.score_stride;
-    int32_t* out_idx = a.topk_idx + (size_t)r * k;
+    const auto out_idx = make_out<kRows>(a, s, r, n);
     if (n <= k) {
         // Everything visible is selected.
-        for (int i = threadIdx.x; i < n; i += kThreads) out_idx[i] = i;
+        if constexpr (kRows) __syncthreads();   // the page ids are in LDS
+        for (int i = threadIdx.x; i < n; i += kThreads) out_idx.put(i, i);
         pad_tail(out_idx, n, k);
         return;
     }
@@ -721,7 +797,8 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
 // keys do not hold it: three radix passes of 12, 10 and 10 bits over the
 // whole row, then the emission in rounds of kThreads positions, each round
 // one scan.  Slow, and only for the rows whose cut missed.
-__device__ void topk_row_streamed(TopkSmem& s, const float* row, int v, int k, int32_t* out, int& tog) {
+template <typename Out>
+__device__ void topk_row_streamed(TopkSmem& s, const float* row, int v, int k, const Out& out, int& tog) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0u, mask = 0u, kk = (uint32_t)k;
 #pragma unroll 1
@@ -757,7 +834,7 @@ __device__ void topk_row_streamed(TopkSmem& s, const float* row, int v, int k, i
         const uint32_t eq_quota = need_eq > eq_before_round ? need_eq - eq_before_round : 0u;
         const bool take = gt || (eq && eq_before < need_eq);
         const uint32_t rank = taken_before + (both >> 16) + min(both & 0xFFFFu, eq_quota);
-        if (take && rank < (uint32_t)k) out[rank] = i;
+        if (take && rank < (uint32_t)k) out.put(rank, i);
         taken_before += (tot >> 16) + min(tot & 0xFFFFu, eq_quota);
         eq_before_round += tot & 0xFFFFu;
     }
@@ -767,9 +844,9 @@ __device__ void topk_row_streamed(TopkSmem& s, const float* row, int v, int k, i
 // one list in slot order; its top k (the row's top k, see above) is emitted
 // in that order.  The list is gathered into the staging buffer and selected
 // with as few keys per thread (4, 8, 16 or 32) as its length allows.
-template <int P>
+template <int P, typename Out>
 __device__ __forceinline__ void merge_select(const TopkArgs& a, TopkSmem& s, const int* off, int ns, int nc, int k,
-                                             int32_t* out_idx, int& tog) {
+                                             const Out& out_idx, int& tog) {
     const int tid = threadIdx.x;
     const int per = keys_per_thread(nc);
     const int base = tid * per;
@@ -796,7 +873,7 @@ __device__ __forceinline__ void merge_select(const TopkArgs& a, TopkSmem& s, con
             if (off[mid] <= pos) lo_j = mid;
             else hi_j = mid - 1;
         }
-        out_idx[i] = a.cand_slot[row_base + (size_t)lo_j * k + (pos - off[lo_j])];
+        out_idx.put(i, a.cand_slot[row_base + (size_t)lo_j * k + (pos - off[lo_j])]);
     }
 }
 
@@ -805,9 +882,9 @@ __device__ __forceinline__ void merge_select(const TopkArgs& a, TopkSmem& s, con
 // nc <= kSlotBase); the fast merge needs nc <= kSlotBase.
 constexpr int kSlotBase = kTopkMaxList / 2;
 
-template <int P>
+template <int P, typename Out>
 __device__ __forceinline__ void emit_slots(TopkSmem& s, const uint32_t (&key)[P], int base, int mine, uint32_t thr,
-                                           uint32_t need_eq, int k, int32_t* out_idx, int& tog);
+                                           uint32_t need_eq, int k, const Out& out_idx, int& tog);
 
 // Keys of list positions [base, base + mine) of the staged candidates (keys
 // at stage_index) into registers; per = keys_per_thread(nc).
@@ -827,9 +904,9 @@ __device__ __forceinline__ void load_staged(const TopkSmem& s, int nc, uint32_t 
 // which inb holds, m <= 64 of them) that holds the k-th largest key as its
 // need-th largest: one wavefront ranks the set exactly, then the selection
 // is emitted in list order.
-template <int P, typename InBin>
+template <int P, typename InBin, typename Out>
 __device__ __forceinline__ void rank_bin_emit(TopkSmem& s, const uint32_t (&key)[P], int base, int mine, int k,
-                                              uint32_t need, uint32_t m, InBin inb, int32_t* out_idx, int& tog) {
+                                              uint32_t need, uint32_t m, InBin inb, const Out& out_idx, int& tog) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     if (tid == 0) s.bcount = 0u;
@@ -864,9 +941,9 @@ __device__ __forceinline__ void rank_bin_emit(TopkSmem& s, const uint32_t (&key)
 // 64): thread t holds list positions [t*per, t*per + per) of the kept keys
 // (in the staging buffer, slots at kSlotBase); one wavefront ranks bin b's
 // keys exactly and the selection is emitted in list order.
-template <int P>
+template <int P, typename Out>
 __device__ __forceinline__ void merge_fast(TopkSmem& s, int nc, int k, uint32_t cut, int bstar, uint32_t need,
-                                           uint32_t m, int32_t* out_idx, int& tog) {
+                                           uint32_t m, const Out& out_idx, int& tog) {
     uint32_t key[P];
     int base, mine;
     load_staged<P>(s, nc, key, base, mine);
@@ -877,9 +954,9 @@ __device__ __forceinline__ void merge_fast(TopkSmem& s, int nc, int k, uint32_t 
 // Emission as in the direct selection (keys above thr, then the first
 // need_eq keys equal to it, in list order), each position's slot read from
 // the staging buffer at kSlotBase.
-template <int P>
+template <int P, typename Out>
 __device__ __forceinline__ void emit_slots(TopkSmem& s, const uint32_t (&key)[P], int base, int mine, uint32_t thr,
-                                           uint32_t need_eq, int k, int32_t* out_idx, int& tog) {
+                                           uint32_t need_eq, int k, const Out& out_idx, int& tog) {
     uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
@@ -899,7 +976,7 @@ __device__ __forceinline__ void emit_slots(TopkSmem& s, const uint32_t (&key)[P]
     while (tm != 0u) {
         const int i = __ffs(tm) - 1;
         tm &= tm - 1u;
-        if (rank < (uint32_t)k) out_idx[rank] = (int32_t)s.u.stage[kSlotBase + base + i];
+        if (rank < (uint32_t)k) out_idx.put(rank, (int32_t)s.u.stage[kSlotBase + base + i]);
         ++rank;
     }
 }
@@ -910,6 +987,7 @@ __device__ __forceinline__ void emit_slots(TopkSmem& s, const uint32_t (&key)[P]
 // of the k-th largest kept key, and one wavefront ranks that bin's keys;
 // rows whose bin holds more than 64 keys (or without a cut) take the general
 // selection instead.
+template <bool kRows>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     __shared__ TopkSmem s;
     __shared__ int off[kMaxSplits + 1];
@@ -918,9 +996,9 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     const int tid = threadIdx.x;
     const int k = a.top_k;
     const int ns = a.n_splits;
-    int32_t* out_idx = a.topk_idx + (size_t)r * k;
     const size_t rb = (size_t)r * ns;
     const int v = checked_vis(a, r);
+    const auto out_idx = make_out<kRows>(a, s, r, v);
     const int want = min(v, k);
     if (tid == 0) a.topk_count[r] = want;
     // Everything this row needs goes out at once: the splits' counts, the
@@ -984,7 +1062,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
         // Every kept key is selected (nc == want), in list order.
         for (int i = tid; i < nc; i += kThreads) {
             if (slots_fit) {
-                out_idx[i] = (int32_t)s.u.stage[kSlotBase + i];
+                out_idx.put(i, (int32_t)s.u.stage[kSlotBase + i]);
             } else {
                 int lo_j = 0, hi_j = ns - 1;
                 while (lo_j < hi_j) {
@@ -992,7 +1070,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
                     if (off[mid] <= i) lo_j = mid;
                     else hi_j = mid - 1;
                 }
-                out_idx[i] = a.cand_slot[(rb + lo_j) * k + (i - off[lo_j])];
+                out_idx.put(i, a.cand_slot[(rb + lo_j) * k + (i - off[lo_j])]);
             }
         }
         pad_tail(out_idx, nc, k);
@@ -1070,12 +1148,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_cuts_kernel(TopkArgs a) {
     const int k = a.top_k;
     const int ns = a.n_splits;
     const int cap = a.cand_cap;
-    int32_t* out_idx = a.topk_idx + (size_t)r * k;
     const size_t rb = (size_t)r * ns;
     const int v = checked_vis(a, r);
+    const auto out_idx = make_out<false>(a, s, r, v);
     if (tid == 0) a.topk_count[r] = min(v, k);
     if (v <= k) {
-        for (int i = tid; i < v; i += kThreads) out_idx[i] = i;
+        for (int i = tid; i < v; i += kThreads) out_idx.put(i, i);
         pad_tail(out_idx, v, k);
         return;
     }
@@ -1170,7 +1248,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_cuts_kernel(TopkArgs a) {
             return;
         }
         if (nc == k) {   // every candidate is >= C and selected
-            for (int i = tid; i < nc; i += kThreads) out_idx[i] = (int32_t)s.u.stage[kSlotBase + i];
+            for (int i = tid; i < nc; i += kThreads) out_idx.put(i, (int32_t)s.u.stage[kSlotBase + i]);
             return;
         }
         const uint32_t bstar = s.sel_digit, need = s.sel_need, m = s.khist[bstar];
@@ -1236,7 +1314,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     const int64_t split_max = (((int64_t)a.score_stride + a.n_splits - 1) / a.n_splits + 3) & ~int64_t{3};
     if (a.n_splits == 1) {
         return by_class(keys_class(split_max), [&](auto pc) {
-            topk_direct_kernel<decltype(pc)::value><<<dim3(1, a.n_rows), kThreads, 0, stream>>>(a);
+            if (a.topk_rows != nullptr)
+                topk_direct_kernel<decltype(pc)::value, true><<<dim3(1, a.n_rows), kThreads, 0, stream>>>(a);
+            else
+                topk_direct_kernel<decltype(pc)::value, false><<<dim3(1, a.n_rows), kThreads, 0, stream>>>(a);
             return hipGetLastError();
         });
     }
@@ -1245,7 +1326,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;
-    topk_merge_kernel<<<a.n_rows, kThreads, 0, stream>>>(a);
+    if (a.topk_rows != nullptr) topk_merge_kernel<true><<<a.n_rows, kThreads, 0, stream>>>(a);
+    else topk_merge_kernel<false><<<a.n_rows, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ import os
 
 import torch
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE", 64: "SCALE"}
@@ -44,6 +44,10 @@ _SIGS = {
     "dsa_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
     "dsa_topk": ([_p, _i32, _p, _i32, _i32, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p], ctypes.c_int),
     "dsa_topk_noalloc": ([_p, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p], ctypes.c_int),
+    "dsa_topk_rows": ([_p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, ctypes.c_size_t,
+                       _p, _p, _p, _p, _p], ctypes.c_int),
+    "dsa_sparse_mla_decode_rows": ([_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
+                                    _p, _p, _p], ctypes.c_int),
     "dsa_sparse_mla_decode": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _f32, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "dsa_sparse_mla_decode_shared": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -226,6 +230,36 @@ def topk(scores, row_vis, top_k: int, n_splits: int = 1, workspace=None, topk_id
     return topk_idx, topk_count, status
 
 
+def topk_rows(scores, row_vis, row_req, page_table, num_pages: int, page_size: int, top_k: int,
+              n_splits: int = 1, workspace=None, topk_idx=None, topk_count=None, topk_rows=None, status=None,
+              stream=None):
+    """topk() that also returns each selected slot's physical row in the paged
+    caches (dsa_topk_rows) -> (topk_idx, topk_count, topk_rows, status)."""
+    r, stride = scores.shape
+    dev = scores.device
+    batch, max_pages = page_table.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((r, top_k), dtype=torch.int32, device=dev)
+    if topk_count is None:
+        topk_count = torch.empty((r,), dtype=torch.int32, device=dev)
+    if topk_rows is None:
+        topk_rows = torch.empty((r, top_k), dtype=torch.int32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    need = topk_workspace_size(r, top_k, n_splits)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace, None, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dsa_topk_rows(_ptr(scores, torch.float32, "scores"), stride,
+                               _ptr(row_vis, torch.int32, "row_vis"), _ptr(row_req, torch.int32, "row_req"),
+                               _ptr(page_table, torch.int32, "page_table"), batch, num_pages, max_pages, page_size,
+                               r, top_k, n_splits, ws_ptr, ws_bytes, _ptr(topk_idx, torch.int32, "topk_idx"),
+                               _ptr(topk_count, torch.int32, "topk_count"), _ptr(topk_rows, torch.int32, "topk_rows"),
+                               _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_topk_rows")
+    return topk_idx, topk_count, topk_rows, status
+
+
 def topk_noalloc(scores, row_vis, top_k: int, n_splits: int = 1, topk_idx=None, topk_count=None,
                  status=None, stream=None):
     """topk() with the candidates in the library's fixed device array instead
@@ -283,6 +317,42 @@ def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_
         _ptr(out, _BF16, "out") if n_splits == 1 else None,
         _ptr(out_lse, torch.float32, "out_lse") if n_splits == 1 else None,
         _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_sparse_mla_decode")
+    if n_splits == 1:
+        return out, out_lse, status
+    return part_o, part_lse, status
+
+
+def sparse_mla_decode_rows(q, kv_cache, row_vis, topk_rows, topk_count, n_splits: int, sm_scale: float,
+                           part_o=None, part_lse=None, out=None, out_lse=None, status=None, stream=None):
+    """sparse_mla_decode over physical rows (dsa_sparse_mla_decode_rows); the
+    same returns."""
+    r, h, dq = q.shape
+    n_pages, p, row_bytes = kv_cache.shape
+    if row_bytes != 640:
+        raise DsaError(f"kv_cache rows must be 640 bytes, got {row_bytes}")
+    top_k = topk_rows.shape[1]
+    dev = q.device
+    if status is None:
+        status = new_status(dev)
+    if n_splits == 1:
+        if out is None:
+            out = torch.empty((r, h, 512), dtype=torch.bfloat16, device=dev)
+        if out_lse is None:
+            out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
+    else:
+        if part_o is None:
+            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.float32, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
+    _check(lib().dsa_sparse_mla_decode_rows(
+        _ptr(q, _BF16, "q"), _ptr(kv_cache, torch.uint8, "kv_cache"), _ptr(row_vis, torch.int32, "row_vis"),
+        _ptr(topk_rows, torch.int32, "topk_rows"), _ptr(topk_count, torch.int32, "topk_count"), r, n_pages, p, h,
+        top_k, n_splits, float(sm_scale),
+        _ptr(part_o, torch.float32, "part_o") if n_splits > 1 else None,
+        _ptr(part_lse, torch.float32, "part_lse") if n_splits > 1 else None,
+        _ptr(out, _BF16, "out") if n_splits == 1 else None,
+        _ptr(out_lse, torch.float32, "out_lse") if n_splits == 1 else None,
+        _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_sparse_mla_decode_rows")
     if n_splits == 1:
         return out, out_lse, status
     return part_o, part_lse, status
@@ -391,7 +461,8 @@ class DecodeStep:
 
     def __init__(self, inp, index_splits: int | None = None, attn_splits: int | None = None,
                  group_rows: int | None = None, score_stride: int | None = None,
-                 index_share: int | None = None, index_topk: bool | None = None):
+                 index_share: int | None = None, index_topk: bool | None = None,
+                 phys_rows: bool | None = None):
         self.inp = inp
         cfg = inp.cfg
         self.index_splits = index_splits or cfg.index_splits
@@ -403,6 +474,10 @@ class DecodeStep:
         if index_topk is None:
             index_topk = index_splits is None and cfg.index_topk
         self.index_topk = bool(index_topk) and self.group_rows == 1
+        # phys_rows: the top-k also emits each selected slot's physical row
+        # (dsa_topk_rows) and the attention gathers those rows directly
+        # (dsa_sparse_mla_decode_rows); for rows that select their own lists
+        # with dsa_topk.
         # MTP IndexShare: chains of `index_share` consecutive rows; only each
         # chain's first row is scored and selected, and every row attends
         # that list.  The first rows' inputs are gathered once, here.
@@ -433,6 +508,10 @@ class DecodeStep:
             need = topk_workspace_size(n_sel, k, self.index_splits)
         self.workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
         self.topk_idx = torch.empty((n_sel, k), dtype=torch.int32, device=dev)
+        if phys_rows is None:
+            phys_rows = cfg.phys_rows
+        self.phys_rows = bool(phys_rows) and not self.index_topk and self.index_share <= 1
+        self.topk_rows = torch.empty((n_sel, k), dtype=torch.int32, device=dev) if self.phys_rows else None
         self.topk_count = torch.empty((n_sel,), dtype=torch.int32, device=dev)
         s = self.attn_splits
         self.part_o = torch.empty((r, h, s, 512), dtype=torch.float32, device=dev) if s > 1 else None
@@ -453,8 +532,14 @@ class DecodeStep:
                          i.kv_lens, self.lead_req, self.lead_vis, group_rows=self.group_rows,
                          score_stride=self.score_stride, scores=self.scores, status=self.status,
                          stream=stream)
-            topk(self.scores, self.lead_vis, i.top_k, self.index_splits, workspace=self.workspace,
-                 topk_idx=self.topk_idx, topk_count=self.topk_count, status=self.status, stream=stream)
+            if self.phys_rows:
+                topk_rows(self.scores, self.lead_vis, self.lead_req, i.page_table, i.kv_cache.shape[0],
+                          i.kv_cache.shape[1], i.top_k, self.index_splits, workspace=self.workspace,
+                          topk_idx=self.topk_idx, topk_count=self.topk_count, topk_rows=self.topk_rows,
+                          status=self.status, stream=stream)
+            else:
+                topk(self.scores, self.lead_vis, i.top_k, self.index_splits, workspace=self.workspace,
+                     topk_idx=self.topk_idx, topk_count=self.topk_count, status=self.status, stream=stream)
         if self.row_list is not None:
             s = self.attn_splits
             sparse_mla_decode_shared(i.q_mla, i.kv_cache, i.page_table, i.row_req, i.row_vis,
@@ -464,7 +549,14 @@ class DecodeStep:
             if s > 1:
                 lse_merge(self.part_o, self.part_lse, out=self.out, out_lse=self.out_lse, stream=stream)
             return self.out, self.out_lse
-        if self.attn_splits == 1:
+        if self.phys_rows:
+            s = self.attn_splits
+            sparse_mla_decode_rows(i.q_mla, i.kv_cache, i.row_vis, self.topk_rows, self.topk_count, s, i.sm_scale,
+                                   part_o=self.part_o, part_lse=self.part_lse, out=self.out, out_lse=self.out_lse,
+                                   status=self.status, stream=stream)
+            if s > 1:
+                lse_merge(self.part_o, self.part_lse, out=self.out, out_lse=self.out_lse, stream=stream)
+        elif self.attn_splits == 1:
             sparse_mla_decode(i.q_mla, i.kv_cache, i.page_table, i.row_req,
                               i.row_vis, self.topk_idx, self.topk_count, 1, i.sm_scale, out=self.out,
                               out_lse=self.out_lse, status=self.status, stream=stream)

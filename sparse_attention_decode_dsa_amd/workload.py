@@ -73,6 +73,7 @@ class Config:
     group_rows: int = 1                   # rows scored together against one key stream
     index_share: int = 0                  # MTP IndexShare: rows per chain sharing one top-k list
     index_topk: bool = False              # rows scored one at a time: scores and top-k in one call
+    phys_rows: bool = False               # top-k emits physical rows; the attention gathers them directly
 
 
 CONFIGS = {

@@ -254,3 +254,41 @@ def test_index_topk_validation_and_workspace(L):
     assert _itk(L, workspace_bytes=need - 1) == WS
     assert _itk(L, workspace=P + 2) == WS
     assert _itk(L, n_rows=0) == OK
+
+
+def test_rows_entry_points_validation(L):
+    """dsa_topk_rows applies dsa_topk's rules and the page geometry, then
+    needs its request, block-table and rows arrays; dsa_sparse_mla_decode_rows
+    applies the attention's rules without a block table."""
+    def tk(**kw):
+        a = dict(scores=P, score_stride=32768, row_vis=P, row_req=P, page_table=P, batch=4, num_pages=600,
+                 max_pages=128, page_size=256, n_rows=4, top_k=2048, n_splits=1, workspace=None,
+                 workspace_bytes=0, topk_idx=P, topk_count=P, topk_rows=P, status=P, stream=None)
+        a.update(kw)
+        return L.dsa_topk_rows(*a.values())
+    assert tk(top_k=0) == SHAPE
+    assert tk(n_splits=65) == SHAPE
+    assert tk(page_size=100) == UNSUP
+    assert tk(batch=0) == SHAPE
+    assert tk(row_req=None) == NULL
+    assert tk(page_table=None) == NULL
+    assert tk(topk_rows=None) == NULL
+    assert tk(scores=None) == NULL
+    assert tk(n_splits=16, score_stride=131072) == WS
+    assert tk(n_rows=0) == OK
+
+    def mla(**kw):
+        a = dict(q=P, kv_cache=P, row_vis=P, topk_rows=P, topk_count=P, n_rows=4, num_pages=100,
+                 page_size=256, n_heads=32, top_k=2048, n_splits=4, sm_scale=0.04, part_o=P, part_lse=P,
+                 out=None, out_lse=None, status=P, stream=None)
+        a.update(kw)
+        return L.dsa_sparse_mla_decode_rows(*a.values())
+    assert mla(n_heads=128) == UNSUP
+    assert mla(n_splits=0) == SHAPE
+    assert mla(sm_scale=float("nan")) == SHAPE
+    assert mla(page_size=48) == UNSUP
+    assert mla(topk_rows=None) == NULL
+    assert mla(part_o=None) == NULL
+    assert mla(n_splits=1) == NULL          # a lone split needs out
+    assert mla(row_vis=None) == NULL
+    assert mla(n_rows=0) == OK

@@ -274,6 +274,19 @@ def test_bulk_decode_sampled_rows(name):
     mla_on_oracle_selection(sub, ref, inp.cfg.attn_splits)
 
 
+def test_bulk_decode_step_with_physical_rows_sampled_rows():
+    """The step with the top-k emitting physical rows and the attention
+    gathering them directly, on sampled rows against the oracle."""
+    inp = W.make("c1_l32k", device="cuda")
+    step = dsa.DecodeStep(inp, phys_rows=True)
+    assert step.phys_rows
+    step.run()
+    torch.cuda.synchronize()
+    dsa.check_status(step.status)
+    ref, sub, swapped = compare_step(inp, step, [0, 17, 40, 63], max_swap_rows=2)
+    say(f"c1_l32k rows: swapped {swapped}")
+
+
 def test_bulk_decode_step_with_index_topk_sampled_rows():
     """The step with scores and top-k from one dsa_index_topk call (the
     indexer keeps candidates, a merge selects), on sampled rows against the
