@@ -396,14 +396,16 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
             hw[k] = (uint32_t)h23;
             lw[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rr[2], rr[3], l01, true);
         }
-        __syncthreads();   // every bf16 value of the buffer has been read
+        // LDS-only barriers: the tiles just issued stay in flight (a
+        // __syncthreads() would wait for all of them).
+        lds_sync();   // every bf16 value of the buffer has been read
 #pragma unroll
         for (int k = 0; k < kPart / 4; ++k) {
             *reinterpret_cast<uint32_t*>(hrow + kPart * part + 4 * k) = hw[k];
             *reinterpret_cast<uint32_t*>(hrow + kRowBytes + kPart * part + 4 * k) = lw[k];
         }
         if (part == 0) s_qs[qh] = __builtin_amdgcn_ldexpf(1.0f, e);
-        __syncthreads();
+        lds_sync();
     }
     // This lane's operands (head 16 hb + nn, lane group g) for the whole
     // split: for 128-element MFMA step m the 32 codes at elements
