@@ -286,6 +286,8 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
         kg.scale = a.k_scale[page >= 0 ? (size_t)page * a.page_size + (t & pmask) : 0];
     };
 
+    bool scale_bad = false;   // a checked key of this lane had a bad scale
+
     // Scores of the group at tg for every row of the group.
     auto process = [&](KeyGroup& kg, int tg) {
         // Every path consumes the group's loads here, so none is left
@@ -296,9 +298,9 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
         const int t = tg + lane;
         // A key whose scale is not a positive finite number is not scored
         // (the head reduction relies on a positive scale); one inside a
-        // checked span is reported.
+        // checked span is reported once the range is done.
         const bool sok = scale_ok(kg.scale);
-        if (__ballot(kg.ok && !sok && t < vchk) != 0ull && lane == 0) flag(a.status, DSA_DEV_SCALE);
+        scale_bad |= kg.ok && !sok && t < vchk;
         kg.ok = kg.ok && sok;
 #pragma unroll 1
         for (int rr = 0; rr < G; ++rr) {
@@ -421,6 +423,7 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
             tg = t2;
         }
     }
+    if (__ballot(scale_bad) != 0ull && lane == 0) flag(a.status, DSA_DEV_SCALE);
 
     if constexpr (G == 1) {
         // -inf past the span, then the whole range out: 16-byte stores where

@@ -74,9 +74,10 @@ struct MlaArgs {
     float* out_lse;
     int32_t* status;
     // Shared lists (MTP IndexShare): row r attends list row_list[r] of
-    // [n_lists, top_k]; nullptr: row r attends list r.  chain > 1: the rows
-    // come in chains of that many consecutive rows sharing one list, and the
-    // launch places each chain's work units on one XCD (set by the launcher).
+    // [n_lists, top_k]; nullptr: row r attends list r.  chain: the rows come
+    // in chains of that many consecutive rows sharing one list (1: none
+    // shared), and the launch places each chain's work units on one XCD (set
+    // by the launcher).
     const int32_t* row_list;
     int32_t n_lists;
     int32_t chain;

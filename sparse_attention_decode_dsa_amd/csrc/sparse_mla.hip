@@ -1,25 +1,27 @@
 // Split-K sparse absorbed-MLA decode on gfx950.
 //
-// A workgroup (4 wavefronts) owns one (row, split): the split's entries of
-// the row's selected list, walked in tiles of 64 tokens with an online
-// softmax.  Per tile:
+// A workgroup (four wavefronts per 16 heads) owns one (row, split): the
+// split's entries of the row's selected list, walked in tiles of 64 tokens
+// with an online softmax.  Per tile:
 //   gather  the 64 selected 576-byte fp8 rows through the block table into
 //           LDS (rows padded to 592 bytes), with their fp32 scales;
-//   QK      on bf16 matrix cores: the tokens' fp8 bytes, converted to bf16
-//           (exact), are the A operand (M = tokens), the bf16 query as it
-//           is the B operand (N = heads), v_mfma_f32_16x16x32_bf16 over the
-//           576 dimensions in 18 steps on two accumulator chains.  The query
-//           stays in registers for the whole split.  Wavefront w owns head
-//           block w % HB and 16 HB tokens;
-//   softmax a lane holds 4 tokens of one head per token block, so the
-//           per-head maximum and sum reduce in-lane and then across the four
-//           16-lane rows with two permlane swaps; the tile maximum per head
-//           goes through LDS and every wavefront keeps the same running max
-//           (the output is rescaled only when it moved); P' = exp(l - m) *
-//           token scale goes to LDS in bf16, 4 tokens per 8-byte store;
-//   PV      wavefront w owns output columns [128w, 128w+128) for all heads:
+//   QK      on fp8 matrix cores: the keys' codes as stored (A, M = tokens)
+//           against the bf16 query split into two E4M3 terms with one
+//           power-of-two scale per head (B, N = heads), four 128-deep steps
+//           over the 512 latent values and two 32-deep steps over the 64
+//           rope values per term, on two accumulator chains.  The query
+//           terms stay in registers for the whole split.  Wavefront w owns
+//           head block w % HB and token block w / HB (16 tokens);
+//   softmax a lane holds 4 tokens of one head, so the per-head maximum and
+//           sum reduce in-lane and then across the four 16-lane rows with two
+//           permlane swaps; the tile maximum per head goes through LDS and
+//           every wavefront keeps the same running max (the output is
+//           rescaled only when it moved); P' = exp(l - m) * token scale goes
+//           to LDS in bf16, 4 tokens per 8-byte store;
+//   PV      wavefront w owns output columns [CW w, CW w + CW) for all heads:
 //           A = P' (heads x tokens), B = the fp8 rows read transposed by
-//           ds_read_b64_tr_b8 (8 tokens of one column per lane), in bf16.
+//           ds_read_b64_tr_b8 (8 tokens of one column per lane), converted
+//           exactly to bf16.
 // The value rows are the first 512 entries of the same rows (absorbed MLA),
 // so a tile is read from HBM once for both products.
 //
@@ -42,9 +44,9 @@
 // order therefore gives lane groups g = 0..3 the 16-byte chunks
 // c + {0, 16, 8, 24} of a row: the two groups served together differ by
 // 256 bytes and never collide.  Lane group g reads chunks
-// {2p + h + 16 (g & 1) + 8 (g >> 1) : p < 4, h < 2} and 32 + g, each as two
-// 8-byte K steps; the query takes the same element positions, so the sums
-// are the plain dot products.  P' is laid
+// {2p + h + 16 (g & 1) + 8 (g >> 1) : h < 2} (its 32 codes of 128-deep step
+// p) and 32 + g (its 16 rope codes); the query takes the same element
+// positions, so the sums are the plain dot products.  P' is laid
 // out as [token group of 8][head][8 tokens] with 768 bytes per token group,
 // which makes both its 8-byte stores and its 16-byte A-operand reads
 // conflict-free.  ds_read_b64_tr_b8 over 32 rows of 592 bytes is
@@ -157,13 +159,15 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     const int hb = wv % HB;         // head block of this wavefront in QK
     const int tbk = wv / HB;        // its token block: tokens [16 tbk, 16 tbk + 16) of a tile
     const int ns = a.n_splits;
+    // Chains on XCDs: workgroup L runs on XCD L % 8 (the dispatcher deals
+    // workgroups out to the XCDs in turn); XCD x takes chains x, x + 8, ...
+    // one after the other, all (row, split) units of a chain in a row.  A
+    // chain is `chain` consecutive rows sharing one list (one row when
+    // nothing is shared), so the chain's shared rows and each row's query,
+    // which every split of the row loads, are fetched into that XCD's L2
+    // once.  Padding units past the last chain do nothing.
     int r, sp;
-    if (a.chain > 1) {
-        // Chains on XCDs: workgroup L runs on XCD L % 8 (the dispatcher deals
-        // workgroups out to the XCDs in turn); XCD x takes chains x, x + 8,
-        // ... one after the other, all (row, split) units of a chain in a
-        // row, so the chain's shared rows are fetched into that XCD's L2
-        // once.  Padding units past the last chain do nothing.
+    {
         const int L = blockIdx.x;
         const int per_chain = a.chain * ns;
         const int j = L >> 3;
@@ -172,9 +176,6 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         if (c * a.chain >= a.n_rows) return;
         r = c * a.chain + u / ns;
         sp = u % ns;
-    } else {
-        r = blockIdx.y;
-        sp = blockIdx.x;
     }
 
     // The bf16 query of the row, gathered like a tile (lane i of load j
@@ -442,6 +443,8 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) o_acc[h2][cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
+    bool scale_bad = false;   // a live token of this lane had a bad scale
+
     // Per tile: wait for its data, start the gather NB-1 tiles ahead into the
     // buffer freed by the previous tile, then QK, softmax and PV.
     for (int it = 0, buf = 0; it < n_tiles; ++it, buf = buf == NB - 1 ? 0 : buf + 1) {
@@ -493,16 +496,12 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
             for (int i = 0; i < 4; ++i) live[i] = live[i] && row_at(tile, tk0 + i) >= 0;
         }
         // A selected row whose scale is not a positive finite number is left
-        // out of the attention and reported.
-        {
-            bool sbad = false;
+        // out of the attention, and reported once the loop is done.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = scale_ok(ts[i]);
-                sbad |= live[i] && !ok;
-                live[i] = live[i] && ok;
-            }
-            if (__ballot(sbad) != 0ull && lane == 0) flag(a.status, DSA_DEV_SCALE);
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = scale_ok(ts[i]);
+            scale_bad |= live[i] && !ok;
+            live[i] = live[i] && ok;
         }
         float lg[4];
         float mx = -INFINITY;
@@ -576,6 +575,8 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         }
     }
 
+    if (__ballot(scale_bad) != 0ull && lane == 0) flag(a.status, DSA_DEV_SCALE);
+
     // Denominators (sum of the wavefronts' shares) and the running max,
     // moved to the PV layout through LDS.  s_red and s_m are free: every
     // wavefront read the last tile's maxima before the last barrier.
@@ -611,15 +612,11 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
 
 template <int HB, int NB>
 hipError_t launch_hb(const MlaArgs& a, hipStream_t stream) {
-    if (a.chain > 1) {
-        // Whole groups of eight chains (one per XCD), padded.
-        const int64_t chains = (a.n_rows / a.chain + 7) / 8 * 8;
-        const int64_t wgs = chains * a.chain * a.n_splits;
-        if (wgs > INT32_MAX) return hipErrorInvalidValue;
-        sparse_mla_kernel<HB, NB><<<(unsigned)wgs, 256 * HB, 0, stream>>>(a);
-    } else {
-        sparse_mla_kernel<HB, NB><<<dim3(a.n_splits, a.n_rows), 256 * HB, 0, stream>>>(a);
-    }
+    // Whole groups of eight chains (one per XCD), padded.
+    const int64_t chains = (a.n_rows / a.chain + 7) / 8 * 8;
+    const int64_t wgs = chains * a.chain * a.n_splits;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    sparse_mla_kernel<HB, NB><<<(unsigned)wgs, 256 * HB, 0, stream>>>(a);
     return hipGetLastError();
 }
 
