@@ -69,6 +69,7 @@ constexpr int kDv = 512;
 constexpr int kRowChunks = kXStride / 16;        // 37: 36 data chunks + 1 pad chunk
 constexpr int kTileChunks = kT * kRowChunks;       // 2368 chunks of 16 bytes
 constexpr int kDmaInsts = kTileChunks / kWave;     // 37 wavefront-wide LDS-direct loads
+constexpr float kSlack = 8.0f;   // P = exp(l - running max) < e^8 without the exchange (see the loop)
 
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -141,9 +142,15 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_p[8 * kPGroup];
     __shared__ int32_t s_rows[kRowsCap];
     __shared__ __attribute__((aligned(16))) float s_red[H][4];           // per-head values of the wavefronts
+    // Rescale factors per head, with a flag per head block (some factor is
+    // not 1): pending ones (a tile's, applied before the next tile's PV) and
+    // the exact path's (applied before the same tile's PV).
     __shared__ __attribute__((aligned(16))) float s_alpha[H];
+    __shared__ __attribute__((aligned(16))) float s_alpha_x[H];
     __shared__ __attribute__((aligned(16))) float s_m[H];
     __shared__ int s_moved[HB];
+    __shared__ int s_moved_x[HB];
+    __shared__ __attribute__((aligned(16))) int s_big[NW];   // per wavefront: a logit far above the running max
     __shared__ int s_bad[NW];   // per wavefront: an entry of the split is invalid
     // The bf16 query is staged in the last tile buffer: head h at row h,
     // kQRow bytes apart (72 chunks of 16 bytes and a pad chunk).
@@ -154,6 +161,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
+    if (tid < HB) s_moved[tid] = 0;   // no rescale pending before the first tile (barriers follow)
     const int nn = lane & 15;
     const int g = lane >> 4;
     const int hb = wv % HB;         // head block of this wavefront in QK
@@ -434,8 +442,19 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     }
 
     // Softmax state: in the QK layout a lane owns head 16 hb + nn (m_run,
-    // and l_run: this wavefront's share of the denominator); in the PV
-    // layout accumulator row i of lane group g is head 16 h2 + 4g + i.
+    // and l_run: this wavefront's share of the denominator, relative to
+    // m_run); in the PV layout accumulator row i of lane group g is head
+    // 16 h2 + 4g + i.
+    //
+    // A tile's probabilities are taken against m_run as it stood before the
+    // tile (every wavefront holds the same value for a head), so they need
+    // no exchange of the tile's maxima first: P = exp(l - m_run) stays
+    // below e^kSlack unless the tile holds a logit more than kSlack above
+    // m_run.  The maxima are exchanged at the barrier that publishes P', and
+    // the rescale to the new maximum is applied to the output before the
+    // next tile's PV.  A tile where some logit exceeds m_run + kSlack (every
+    // first tile with a live token, where m_run is -inf) takes the exact
+    // path instead: P against the new maximum, one more barrier.
     float m_run = -INFINITY, l_run = 0.0f;
     v4f o_acc[HB][NCB];
 #pragma unroll
@@ -454,6 +473,15 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         wait_tiles<NW>(wv, min(NB - 2, n_tiles - 1 - it));
         lds_sync();   // tile `it` is in LDS; every wavefront is done with tile it-1
         if (it + NB - 1 < n_tiles) issue(buf == 0 ? NB - 1 : buf - 1, tile + (NB - 1) * kT);
+        // The previous tile's pending rescale, read now (the factors are
+        // rewritten after this tile's second barrier) and applied before PV.
+        int pend[HB];
+        float4 pend_a[HB];
+#pragma unroll
+        for (int h2 = 0; h2 < HB; ++h2) {
+            pend[h2] = s_moved[h2];
+            pend_a[h2] = *reinterpret_cast<const float4*>(&s_alpha[16 * h2 + 4 * g]);
+        }
         if (nt < kT || any_bad) {
             zero_dead(xb, tile);
             lds_sync();
@@ -512,43 +540,77 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         }
         mx = rows4_max(mx);
         const int h = 16 * hb + nn;
+        const bool big = mx > m_run + kSlack;   // false for mx = -inf; true for m_run = -inf < mx
+
+        // Probabilities against m_run; P' to LDS.
+        // tokens t = 16 tbk + 4g + i: group t / 8 = 2 tbk + g / 2, slot 4 (g & 1) + i
+        uint2* const p_dst = reinterpret_cast<uint2*>(s_p + (2 * tbk + (g >> 1)) * kPGroup + h * 16 + 8 * (g & 1));
+        auto probs = [&](float ref) -> float {
+            float pv[4], ps = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = live[i] ? __expf(lg[i] - ref) : 0.0f;
+                ps += pv[i];
+            }
+            float pt4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pt4[i] = live[i] ? pv[i] * ts[i] : 0.0f;   // no 0 * (bad scale)
+            const v2bf p01 = v2bf{(__bf16)pt4[0], (__bf16)pt4[1]};
+            const v2bf p23 = v2bf{(__bf16)pt4[2], (__bf16)pt4[3]};
+            *p_dst = uint2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+            return rows4_sum(ps);
+        };
+        const float psum = probs(m_run);
         if (g == 0) s_red[h][tbk] = mx;
+        s_big[wv] = __ballot(big) != 0ull;   // the same value from every lane
         lds_sync();
 
-        // Running max (over the four token blocks); probabilities.
+        // New running max (over the four token blocks) and its rescale.
         const float4 r4 = *reinterpret_cast<const float4*>(&s_red[h][0]);
         const float mn = fmaxf(m_run, fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)));
         const bool moved = mn != m_run;
         const float alpha = (m_run == -INFINITY) ? 0.0f : __expf(m_run - mn);
-        m_run = mn;
-        float pv[4], ps = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pv[i] = live[i] ? __expf(lg[i] - mn) : 0.0f;
-            ps += pv[i];
-        }
-        l_run = l_run * alpha + rows4_sum(ps);
-        // tokens t = 16 tbk + 4g + i: group t / 8 = 2 tbk + g / 2, slot 4 (g & 1) + i
-        float pt4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pt4[i] = live[i] ? pv[i] * ts[i] : 0.0f;   // no 0 * (bad scale)
-        const v2bf p01 = v2bf{(__bf16)pt4[0], (__bf16)pt4[1]};
-        const v2bf p23 = v2bf{(__bf16)pt4[2], (__bf16)pt4[3]};
-        *reinterpret_cast<uint2*>(s_p + (2 * tbk + (g >> 1)) * kPGroup + h * 16 + 8 * (g & 1)) =
-            uint2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
         const bool any_moved = __ballot(moved) != 0ull;   // same in the 4 wavefronts of head block hb
-        if (tbk == 0) {
-            if (g == 0) s_alpha[h] = alpha;
-            if (lane == 0) s_moved[hb] = any_moved;
+        bool exact = false;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) exact |= s_big[w] != 0;
+        m_run = mn;
+        if (!exact) {
+            l_run = (l_run + psum) * alpha;
+            if (tbk == 0) {   // pending: applied before the next tile's PV
+                if (g == 0) s_alpha[h] = alpha;
+                if (lane == 0) s_moved[hb] = any_moved;
+            }
+        } else {
+            // Exact path: P against the new maximum, rescale now, nothing pending.
+            l_run = l_run * alpha + probs(mn);
+            if (tbk == 0) {
+                if (g == 0) s_alpha_x[h] = alpha;
+                if (lane == 0) {
+                    s_moved_x[hb] = any_moved;
+                    s_moved[hb] = 0;
+                }
+            }
+            lds_sync();
+#pragma unroll
+            for (int h2 = 0; h2 < HB; ++h2) {
+                if (s_moved_x[h2]) {
+                    const float4 al4 = *reinterpret_cast<const float4*>(&s_alpha_x[16 * h2 + 4 * g]);
+                    if (pend[h2]) {
+                        pend_a[h2].x *= al4.x; pend_a[h2].y *= al4.y; pend_a[h2].z *= al4.z; pend_a[h2].w *= al4.w;
+                    } else {
+                        pend_a[h2] = al4;
+                    }
+                    pend[h2] = 1;
+                }
+            }
         }
-        lds_sync();
 
-        // alpha is exactly 1 for every head whose max did not move.
+        // Rescales before PV; alpha is exactly 1 for every head whose max did not move.
 #pragma unroll
         for (int h2 = 0; h2 < HB; ++h2) {
-            if (s_moved[h2]) {
-                const float4 al4 = *reinterpret_cast<const float4*>(&s_alpha[16 * h2 + 4 * g]);
-                const float av[4] = {al4.x, al4.y, al4.z, al4.w};
+            if (pend[h2]) {
+                const float av[4] = {pend_a[h2].x, pend_a[h2].y, pend_a[h2].z, pend_a[h2].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -577,9 +639,23 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
 
     if (__ballot(scale_bad) != 0ull && lane == 0) flag(a.status, DSA_DEV_SCALE);
 
+    // The last tile's pending rescale; the barrier also ends every read of
+    // the last tile's maxima, so s_red and s_m are free below.
+    lds_sync();
+#pragma unroll
+    for (int h2 = 0; h2 < HB; ++h2) {
+        if (s_moved[h2]) {
+            const float4 al4 = *reinterpret_cast<const float4*>(&s_alpha[16 * h2 + 4 * g]);
+            const float av[4] = {al4.x, al4.y, al4.z, al4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) o_acc[h2][cb][i] *= av[i];
+        }
+    }
+
     // Denominators (sum of the wavefronts' shares) and the running max,
-    // moved to the PV layout through LDS.  s_red and s_m are free: every
-    // wavefront read the last tile's maxima before the last barrier.
+    // moved to the PV layout through LDS.
     if (g == 0) s_red[16 * hb + nn][tbk] = l_run;
     if (tbk == 0 && g == 0) s_m[16 * hb + nn] = m_run;
     __syncthreads();

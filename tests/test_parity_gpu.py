@@ -260,6 +260,65 @@ def test_c0_attention_on_oracle_selection(n_splits):
     mla_on_oracle_selection(inp, ref, n_splits)
 
 
+def split_tile_jumps(inp, idx, cnt, n_splits, slack=8.0):
+    """Tiles after a split's first whose largest logit (some head, float32
+    on the host) exceeds the running maximum of the split's tiles before it
+    by more than `slack`."""
+    code = W.kv_code_view(inp.kv_cache).contiguous().view(torch.float8_e4m3fn).float()
+    sc = W.kv_scale_view(inp.kv_cache)
+    q = inp.q_mla.float()
+    p = inp.page_size
+    chunk = -(-inp.top_k // n_splits)
+    jumps = 0
+    for r in range(inp.n_rows):
+        b = int(inp.row_req[r])
+        sel = torch.from_numpy(np.asarray(idx[r, :cnt[r]], dtype=np.int64))
+        pages, offs = inp.page_table[b, sel // p].long(), sel % p
+        lg = (q[r] @ (code[pages, offs] * sc[pages, offs][:, None]).T) * inp.sm_scale
+        for sp in range(n_splits):
+            lo, hi = sp * chunk, min((sp + 1) * chunk, int(cnt[r]))
+            m = None
+            for t0 in range(lo, hi, 64):
+                tm = lg[:, t0:min(t0 + 64, hi)].max(dim=1).values
+                if m is not None and bool((tm > m + slack).any()):
+                    jumps += 1
+                m = tm if m is None else torch.maximum(m, tm)
+    return jumps
+
+
+@pytest.mark.parametrize("n_splits,heads", [(1, 16), (4, 16), (4, 32), (3, 32)])
+def test_attention_logit_jumps_mid_split(n_splits, heads):
+    """Selected rows whose MLA scales are raised 8-fold in tiles 2 and 5 of
+    every split: their positive logits rise more than 8 above the running
+    maximum of the tiles before them (the attention kernel's threshold for
+    its exact path, which the synthetic workloads otherwise take only at a
+    split's first tile), and their negative ones fall below.  The GPU
+    attention on the oracle's selection against the oracle."""
+    base = W.make("c0")
+    inp = W.make(dataclasses.replace(base.cfg, mla_heads=heads))
+    ref = O.decode_step(W.as_numpy(inp), 4, n_splits)
+    idx, cnt = ref["topk_idx"], ref["topk_count"]
+    kv = inp.kv_cache.clone()
+    kvs = W.kv_scale_view(kv)
+    p = inp.page_size
+    chunk = -(-inp.top_k // n_splits)
+    for r in range(inp.n_rows):
+        b = int(inp.row_req[r])
+        for sp in range(n_splits):
+            lo, hi = sp * chunk, min((sp + 1) * chunk, int(cnt[r]))
+            for tile in (2, 5):
+                for j in range(lo + 64 * tile, min(lo + 64 * tile + 8, hi)):
+                    t = int(idx[r, j])
+                    kvs[int(inp.page_table[b, t // p]), t % p] *= 8
+    jumped = dataclasses.replace(inp, kv_cache=kv)
+    jumps = split_tile_jumps(jumped, idx, cnt, n_splits)
+    say(f"logit jumps: splits={n_splits} heads={heads}: {jumps} tiles jump mid-split")
+    assert jumps >= 4
+    ref2 = O.decode_step(W.as_numpy(jumped), 4, n_splits)
+    np.testing.assert_array_equal(ref2["topk_idx"], idx)   # the index keys did not change
+    mla_on_oracle_selection(jumped, ref2, n_splits)
+
+
 # ------------------------------------------------------------------ bulk decode, sampled rows
 
 @pytest.mark.parametrize("name", ["c1", "c1_l32k"])
