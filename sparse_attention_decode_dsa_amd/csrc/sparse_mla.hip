@@ -69,7 +69,9 @@ constexpr int kDv = 512;
 constexpr int kRowChunks = kXStride / 16;        // 37: 36 data chunks + 1 pad chunk
 constexpr int kTileChunks = kT * kRowChunks;       // 2368 chunks of 16 bytes
 constexpr int kDmaInsts = kTileChunks / kWave;     // 37 wavefront-wide LDS-direct loads
-constexpr float kSlack = 8.0f;   // P = exp(l - running max) < e^8 without the exchange (see the loop)
+constexpr float kSlack = 11.5f;  // P = 2^(l - running max) < 2^11.5 (about e^8) without the exchange (see the loop)
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
 
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -292,6 +294,12 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         }
     }
     static_assert(MlaGeom<4>::kRowsCap <= 2048, "a four-buffer split is one batch (kBatch >= 2048)");
+    // The row list padded to whole tiles with row 0 (n_tiles * kT <= kRowsCap:
+    // a split holds at most kRowsCap entries and kRowsCap is a multiple of
+    // kT), so the gathers need no bound check; dead rows are zeroed in LDS
+    // before they are used.
+    static_assert(MlaGeom<4>::kRowsCap % kT == 0 && MlaGeom<2>::kRowsCap % kT == 0, "whole tiles");
+    for (int e = hi - lo + tid; e < n_tiles * kT; e += NT) s_rows[e] = 0;
     const bool wave_bad = __ballot(bad) != 0ull;
     if (lane == 0) s_bad[wv] = wave_bad;
     // Every load of the wavefronts done (the query included, which the
@@ -327,12 +335,13 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
     };
     auto issue = [&](int buf, int base) {
         const uint32_t xl = lds_offset(s_x[buf]);
+        const int32_t* tile_rows = s_rows + (base - lo);   // padded to whole tiles
         int32_t row[kDmaPer], off[kDmaPer];
 #pragma unroll
         for (int jj = 0; jj < kDmaPer; ++jj) {
             int t;
             dma_geo(min(wv + NW * jj, kDmaInsts - 1), t, off[jj]);
-            row[jj] = max(row_at(base, t), 0);
+            row[jj] = max(tile_rows[t], 0);
         }
         // Loads j = wv + NW jj; the last one exists only while j < 37.
 #pragma unroll
@@ -438,18 +447,19 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         }
         qrh = *reinterpret_cast<const v4i*>(hr + 16 * (32 + g));
         qrl = *reinterpret_cast<const v4i*>(hr + kRowBytes + 16 * (32 + g));
-        qsc = cq * s_qs[16 * hb + nn];
+        qsc = cq * kLog2e * s_qs[16 * hb + nn];   // logits in base-2 units
     }
 
-    // Softmax state: in the QK layout a lane owns head 16 hb + nn (m_run,
-    // and l_run: this wavefront's share of the denominator, relative to
-    // m_run); in the PV layout accumulator row i of lane group g is head
-    // 16 h2 + 4g + i.
+    // Softmax state, with logits l in base-2 units (the softmax scale times
+    // log2 e, folded into the query scale), so P = 2^(l - m): in the QK
+    // layout a lane owns head 16 hb + nn (m_run, and l_run: this
+    // wavefront's share of the denominator, relative to m_run); in the PV
+    // layout accumulator row i of lane group g is head 16 h2 + 4g + i.
     //
     // A tile's probabilities are taken against m_run as it stood before the
     // tile (every wavefront holds the same value for a head), so they need
-    // no exchange of the tile's maxima first: P = exp(l - m_run) stays
-    // below e^kSlack unless the tile holds a logit more than kSlack above
+    // no exchange of the tile's maxima first: P = 2^(l - m_run) stays
+    // below 2^kSlack unless the tile holds a logit more than kSlack above
     // m_run.  The maxima are exchanged at the barrier that publishes P', and
     // the rescale to the new maximum is applied to the output before the
     // next tile's PV.  A tile where some logit exceeds m_run + kSlack (every
@@ -549,7 +559,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
             float pv[4], ps = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pv[i] = live[i] ? __expf(lg[i] - ref) : 0.0f;
+                pv[i] = live[i] ? __builtin_amdgcn_exp2f(lg[i] - ref) : 0.0f;
                 ps += pv[i];
             }
             float pt4[4];
@@ -569,7 +579,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         const float4 r4 = *reinterpret_cast<const float4*>(&s_red[h][0]);
         const float mn = fmaxf(m_run, fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)));
         const bool moved = mn != m_run;
-        const float alpha = (m_run == -INFINITY) ? 0.0f : __expf(m_run - mn);
+        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
         const bool any_moved = __ballot(moved) != 0ull;   // same in the 4 wavefronts of head block hb
         bool exact = false;
 #pragma unroll
@@ -669,7 +679,7 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
             const float4 l4 = *reinterpret_cast<const float4*>(&s_red[hh][0]);
             const float l = (l4.x + l4.y) + (l4.z + l4.w);
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-            const float lse = l > 0.0f ? mv[i] + __logf(l) : -INFINITY;
+            const float lse = l > 0.0f ? mv[i] * kLn2 + __logf(l) : -INFINITY;   // natural log
             const size_t rh = (size_t)r * H + hh;
             if (ns == 1) {
                 uint16_t* dst = a.out + rh * kDv + CW * wv + nn;
