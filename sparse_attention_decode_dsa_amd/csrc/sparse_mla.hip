@@ -70,6 +70,7 @@ constexpr int kRowChunks = kXStride / 16;        // 37: 36 data chunks + 1 pad c
 constexpr int kTileChunks = kT * kRowChunks;       // 2368 chunks of 16 bytes
 constexpr int kDmaInsts = kTileChunks / kWave;     // 37 wavefront-wide LDS-direct loads
 constexpr float kSlack = 11.5f;  // P = 2^(l - running max) < 2^11.5 (about e^8) without the exchange (see the loop)
+constexpr float kLazy = 8.0f;    // the running max moves only when a tile's exceeds it by more (base 2)
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -575,9 +576,13 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
         s_big[wv] = __ballot(big) != 0ull;   // the same value from every lane
         lds_sync();
 
-        // New running max (over the four token blocks) and its rescale.
+        // New running max (over the four token blocks) and its rescale.  The
+        // running max moves only when the tile's exceeds it by more than
+        // kLazy, so most tiles after the first need no rescale (P stays below
+        // 2^kLazy against it, 2^kSlack on the tile that moves it).
         const float4 r4 = *reinterpret_cast<const float4*>(&s_red[h][0]);
-        const float mn = fmaxf(m_run, fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w)));
+        const float tmax = fmaxf(fmaxf(r4.x, r4.y), fmaxf(r4.z, r4.w));
+        const float mn = tmax > m_run + kLazy ? tmax : m_run;   // tmax when m_run is -inf
         const bool moved = mn != m_run;
         const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
         const bool any_moved = __ballot(moved) != 0ull;   // same in the 4 wavefronts of head block hb
