@@ -14,10 +14,12 @@
 //           head block w % HB and token block w / HB (16 tokens);
 //   softmax a lane holds 4 tokens of one head, so the per-head maximum and
 //           sum reduce in-lane and then across the four 16-lane rows with two
-//           permlane swaps; the tile maximum per head goes through LDS and
-//           every wavefront keeps the same running max (the output is
-//           rescaled only when it moved); P' = exp(l - m) * token scale goes
-//           to LDS in bf16, 4 tokens per 8-byte store;
+//           permlane swaps; P' = 2^(l - m) * token scale (logits in base-2
+//           units) goes to LDS in bf16, 4 tokens per 8-byte store, against
+//           the running max m of the tiles before, which every wavefront
+//           holds; the tile maxima per head go through LDS with P', and the
+//           output is rescaled when the running max moves (the loop has the
+//           details);
 //   PV      wavefront w owns output columns [CW w, CW w + CW) for all heads:
 //           A = P' (heads x tokens), B = the fp8 rows read transposed by
 //           ds_read_b64_tr_b8 (8 tokens of one column per lane), converted
