@@ -55,12 +55,27 @@ static_assert(kPer == 32, "the largest key count with_keys_per_thread compiles f
 constexpr int kBins0 = 4096;                    // key bits [31:20]
 constexpr int kBins1 = 1024;                    // then [19:10] and [9:0]
 constexpr int kCandCap = 4096;
+constexpr int kComputeUnits = 256;   // MI355X
 
-struct TopkSmem {
+constexpr int kPtLds = 1024;
+
+// LDS of one selection workgroup.  The staging buffer (the list's keys on
+// their way from coalesced loads to each thread's contiguous positions, in
+// XOR-swizzled 16-byte chunks: kStage words, the longest list a launch
+// allows, or half of it for lists staged in two rounds) shares its space
+// with the selection's candidate histograms and with the emitted positions
+// (at word 0) and keys (at word kEmitKey), at most kMaxK each plus one dummy
+// word per lane.  kPt: room for the page ids of the physical-rows variants.
+template <int kStage, bool kPt>
+struct TopkSmemT {
+    static constexpr int kStageWords = kStage;
+    static constexpr int kSelWords = 2 * kBins0 + kCandCap + kWave;
+    static constexpr int kUnionWords = kStage > kSelWords ? kStage : kSelWords;
+    static constexpr int kEmitKey =
+        2 * (kTopkMaxK + kWave) <= kUnionWords ? kTopkMaxK + kWave : kUnionWords / 2;
+    static constexpr int kMaxK = kEmitKey - kWave;
     union {
-        // Staging of the list's keys for the transpose from coalesced loads
-        // to each thread's contiguous positions (16-byte chunks XOR-swizzled).
-        uint32_t stage[kTopkMaxList];
+        uint32_t stage[kUnionWords];
         struct {
             uint32_t hist[kBins0];
             uint32_t cand_key[kCandCap + kWave];   // + one dummy word per lane
@@ -77,9 +92,16 @@ struct TopkSmem {
     uint32_t sel_digit;
     uint32_t sel_digit2;
     uint32_t sel_need;
-    int32_t pt[1024];      // physical rows asked for: the row's request's page ids, when they fit
+    int32_t pt[kPt ? kPtLds : 1];   // physical rows asked for: the row's request's page ids, when they fit
 };
-constexpr int kPtLds = 1024;
+// Every launch's layout but the compact filter's.
+using TopkSmem = TopkSmemT<kTopkMaxList, true>;
+static_assert(TopkSmem::kEmitKey == kTopkMaxK + kWave && TopkSmem::kMaxK == kTopkMaxK, "full emission space");
+// The filter pass for lists of at most 16 keys a thread (16384 keys, staged
+// in two rounds) and top_k <= kMaxK (6112): about 67 KB, so two 1024-thread
+// workgroups share a CU and overlap their barrier chains.
+using TopkSmemCompact = TopkSmemT<kTopkMaxList / 4, false>;
+static_assert(sizeof(TopkSmemCompact) <= 80 * 1024, "two compact workgroups per CU");
 
 __device__ __forceinline__ uint32_t bin0(uint32_t key) { return key >> 20; }
 
@@ -154,7 +176,8 @@ __device__ __forceinline__ int keys_per_thread(int n) {
 // two scratch arrays (`tog` flips on every call and is the same in every
 // thread), so a scan never writes the array the previous one is still
 // being read from.
-__device__ __forceinline__ uint32_t scan2(TopkSmem& s, uint32_t v, uint32_t* total, int& tog) {
+template <class S>
+__device__ __forceinline__ uint32_t scan2(S& s, uint32_t v, uint32_t* total, int& tog) {
     constexpr int NW = kThreads / kWave;
     uint32_t* scratch = s.scan[tog];
     tog ^= 1;
@@ -178,8 +201,8 @@ __device__ __forceinline__ uint32_t scan2(TopkSmem& s, uint32_t v, uint32_t* tot
 // the kk-th largest counted key: s.sel_digit = d, s.sel_need = kk minus the
 // keys in larger bins.  Thread t owns the NB/kThreads bins just below
 // NB - t * (NB / kThreads).
-template <int NB>
-__device__ __forceinline__ void find_digit(TopkSmem& s, const uint32_t* hist, uint32_t kk, int& tog) {
+template <int NB, class S>
+__device__ __forceinline__ void find_digit(S& s, const uint32_t* hist, uint32_t kk, int& tog) {
     constexpr int PER = NB / kThreads;
     const int tid = threadIdx.x;
     uint32_t c[PER];
@@ -205,8 +228,8 @@ __device__ __forceinline__ void find_digit(TopkSmem& s, const uint32_t* hist, ui
 // The bins holding the kk_hi-th and kk_lo-th largest keys of `hist`, in one
 // scan: s.sel_digit (kBins0 - 1 if kk_hi == 0) and s.sel_digit2 (0 if
 // kk_lo == 0).
-template <int NB>
-__device__ __forceinline__ void find_digit2(TopkSmem& s, const uint32_t* hist, uint32_t kk_hi, uint32_t kk_lo,
+template <int NB, class S>
+__device__ __forceinline__ void find_digit2(S& s, const uint32_t* hist, uint32_t kk_hi, uint32_t kk_lo,
                                             int& tog) {
     constexpr int PER = NB / kThreads;
     const int tid = threadIdx.x;
@@ -233,7 +256,8 @@ __device__ __forceinline__ void find_digit2(TopkSmem& s, const uint32_t* hist, u
     __syncthreads();
 }
 
-__device__ __forceinline__ void clear_hist(TopkSmem& s, int nb) {
+template <class S>
+__device__ __forceinline__ void clear_hist(S& s, int nb) {
     for (int i = threadIdx.x; i < nb; i += kThreads) s.u.sel.hist[i] = 0;
     __syncthreads();
 }
@@ -241,8 +265,8 @@ __device__ __forceinline__ void clear_hist(TopkSmem& s, int nb) {
 // Exact kk-th largest key (and the number of equal keys in the top kk)
 // among the keys get(i, &key) yields for i in [0, M) on each thread, by
 // three histogram passes of 12, 10 and 10 bits.
-template <int M, typename Get>
-__device__ __forceinline__ void radix_select(TopkSmem& s, uint32_t kk, Get get, uint32_t* thr_out,
+template <int M, class S, typename Get>
+__device__ __forceinline__ void radix_select(S& s, uint32_t kk, Get get, uint32_t* thr_out,
                                              uint32_t* need_out, int& tog) {
     clear_hist(s, kBins0);
 #pragma unroll
@@ -279,8 +303,8 @@ __device__ __forceinline__ void radix_select(TopkSmem& s, uint32_t kk, Get get, 
 // k-th largest (1 <= k < n) of the n keys, thread t holding `mine` of them
 // in key[0, mine).  s.h0 must be zero (the caller clears it before staging
 // the list).
-template <int P>
-__device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[P], int mine, int n, int k,
+template <int P, class S>
+__device__ __forceinline__ void select_kth(S& s, const uint32_t (&key)[P], int mine, int n, int k,
                                            uint32_t* thr_out, uint32_t* need_out, int& tog) {
     const int tid = threadIdx.x;
     const int per = keys_per_thread(n);
@@ -392,11 +416,10 @@ __device__ __forceinline__ void select_kth(TopkSmem& s, const uint32_t (&key)[P]
         thr_out, need_out, tog);
 }
 
-// LDS words of the emitted list positions and keys (each k + one dummy per
-// lane), inside the staging buffer, which is free once the keys are in
-// registers.
+// LDS word of the emitted list positions (each k + one dummy per lane),
+// inside the staging buffer, which is free once the keys are in registers;
+// the keys follow at the layout's kEmitKey.
 constexpr int kEmitPos = 0;
-constexpr int kEmitKey = kTopkMaxK + kWave;
 static_assert(2 * (kTopkMaxK + kWave) <= kTopkMaxList, "emission buffers fit the staging buffer");
 
 // Selected keys in list order: a key is taken if it is above `thr`, or equal
@@ -405,8 +428,8 @@ static_assert(2 * (kTopkMaxK + kWave) <= kTopkMaxList, "emission buffers fit the
 // i) and keys are written to LDS at those ranks without branches (a key not
 // taken goes to the lane's dummy word), for a coalesced copy out afterwards
 // (after a barrier, by the caller).
-template <int P>
-__device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[P], int base,
+template <int P, class S>
+__device__ __forceinline__ void emit_to_lds(S& s, const uint32_t (&key)[P], int base,
                                             uint32_t thr, uint32_t need_eq, int k, int& tog) {
     // Positions past the thread's share hold key 0, which is never above a
     // threshold; equal keys are only counted for a nonzero threshold (a zero
@@ -437,7 +460,7 @@ __device__ __forceinline__ void emit_to_lds(TopkSmem& s, const uint32_t (&key)[P
         eq_left -= (is_eq && take) ? 1u : 0u;
         const uint32_t slot = take ? min(rank, (uint32_t)k - 1u) : dummy;
         s.u.stage[kEmitPos + slot] = (uint32_t)(base + i);
-        s.u.stage[kEmitKey + slot] = key[i];
+        s.u.stage[S::kEmitKey + slot] = key[i];
         rank += take;
     }
 }
@@ -485,42 +508,75 @@ __device__ __forceinline__ int chunk_swz(int c) { return c ^ ((c >> 5) & 7); }
 // loads (coalesced across lanes, all issued before any use) and 16-byte LDS
 // accesses.  Chunks past the list reload its last chunk and are never read
 // back; positions past n in the last chunk are masked.  Sets `nan` if a
-// listed score is NaN.
-template <int P, bool kScores>
-__device__ __forceinline__ void load_list_vec(TopkSmem& s, const void* src, int n, int base, int mine,
+// listed score is NaN.  A stage smaller than the list takes it in rounds:
+// round r holds chunks [r C, r C + C) (C chunks a round), and each thread
+// reads its chunks in the rounds that hold them.
+template <int P, bool kScores, class S>
+__device__ __forceinline__ void load_list_vec(S& s, const void* src, int n, int base, int mine,
                                               uint32_t (&key)[P], bool& nan) {
-    constexpr int kChunks = kTopkMaxList / 4;
+    constexpr int kStageChunks = S::kStageWords / 4;
+    constexpr int kRounds = (P / 4 * kThreads + kStageChunks - 1) / kStageChunks;
+    constexpr int kPerRound = P / 4 / kRounds;   // loads (of kThreads chunks) a round stages
+    static_assert(kRounds * kPerRound == P / 4 && kPerRound * kThreads <= kStageChunks, "whole rounds");
     const int nch = (n + 3) >> 2;
     uint4* stage4 = reinterpret_cast<uint4*>(s.u.stage);
+    uint4 v[P / 4];   // keys of list chunk u * kThreads + thread
     if constexpr (kScores) {
-        float4 v[P / 4];
+        float4 f4[P / 4];
 #pragma unroll
         for (int u = 0; u < P / 4; ++u)
-            v[u] = reinterpret_cast<const float4*>(src)[min(u * kThreads + (int)threadIdx.x, nch - 1)];
+            f4[u] = reinterpret_cast<const float4*>(src)[min(u * kThreads + (int)threadIdx.x, nch - 1)];
 #pragma unroll
         for (int u = 0; u < P / 4; ++u) {
             const int q = u * kThreads + (int)threadIdx.x;
-            const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            const float f[4] = {f4[u].x, f4[u].y, f4[u].z, f4[u].w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) nan |= (f[j] != f[j]) && 4 * q + j < n;
-            stage4[chunk_swz(q)] = uint4{monotone_key(f[0]), monotone_key(f[1]), monotone_key(f[2]), monotone_key(f[3])};
+            v[u] = uint4{monotone_key(f[0]), monotone_key(f[1]), monotone_key(f[2]), monotone_key(f[3])};
         }
     } else {
-        uint4 v[P / 4];
 #pragma unroll
         for (int u = 0; u < P / 4; ++u)
             v[u] = reinterpret_cast<const uint4*>(src)[min(u * kThreads + (int)threadIdx.x, nch - 1)];
+    }
+    if constexpr (kRounds == 1) {
 #pragma unroll
         for (int u = 0; u < P / 4; ++u) stage4[chunk_swz(u * kThreads + (int)threadIdx.x)] = v[u];
-    }
-    __syncthreads();
+        __syncthreads();
 #pragma unroll
-    for (int m = 0; m < P / 4; ++m) {
-        const uint4 x = stage4[chunk_swz(min((base >> 2) + m, kChunks - 1))];
-        key[4 * m + 0] = 4 * m + 0 < mine ? x.x : 0u;
-        key[4 * m + 1] = 4 * m + 1 < mine ? x.y : 0u;
-        key[4 * m + 2] = 4 * m + 2 < mine ? x.z : 0u;
-        key[4 * m + 3] = 4 * m + 3 < mine ? x.w : 0u;
+        for (int m = 0; m < P / 4; ++m) {
+            const uint4 x = stage4[chunk_swz(min((base >> 2) + m, kStageChunks - 1))];
+            key[4 * m + 0] = 4 * m + 0 < mine ? x.x : 0u;
+            key[4 * m + 1] = 4 * m + 1 < mine ? x.y : 0u;
+            key[4 * m + 2] = 4 * m + 2 < mine ? x.z : 0u;
+            key[4 * m + 3] = 4 * m + 3 < mine ? x.w : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) key[i] = 0u;
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            constexpr int kRound = kPerRound * kThreads;   // chunks a round holds
+            const int c0 = r * kRound;
+            if (r > 0) __syncthreads();   // every thread has read the previous round
+#pragma unroll
+            for (int uu = 0; uu < kPerRound; ++uu) {
+                const int u = r * kPerRound + uu;
+                stage4[chunk_swz(u * kThreads + (int)threadIdx.x - c0)] = v[u];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < P / 4; ++m) {
+                const int c = (base >> 2) + m;
+                if (4 * m < mine && c >= c0 && c < c0 + kRound) {
+                    const uint4 x = stage4[chunk_swz(c - c0)];
+                    key[4 * m + 0] = 4 * m + 0 < mine ? x.x : 0u;
+                    key[4 * m + 1] = 4 * m + 1 < mine ? x.y : 0u;
+                    key[4 * m + 2] = 4 * m + 2 < mine ? x.z : 0u;
+                    key[4 * m + 3] = 4 * m + 3 < mine ? x.w : 0u;
+                }
+            }
+        }
     }
     __syncthreads();
 }
@@ -682,10 +738,15 @@ __device__ __forceinline__ int cut_rank(int v, int k, int S) {
 
 // Filter pass: grid (n_splits, n_rows).  Split j of row r writes its kept
 // keys and slots, in slot order, at the front of its own block of k entries
-// of the workspace, and their number to cand_count[r][j].
-template <int P>
-__global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
-    __shared__ TopkSmem s;
+// of the workspace, and their number to cand_count[r][j].  kCompact: the
+// compact LDS layout (P <= 16, k <= TopkSmemCompact::kMaxK, every split
+// 16-byte aligned and read whole, which the launch checks).
+template <int P, bool kCompact>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kCompact ? 8 : 1)))
+void topk_filter_kernel(TopkArgs a) {
+    using Smem = std::conditional_t<kCompact, TopkSmemCompact, TopkSmem>;
+    static_assert(!kCompact || P <= 16, "compact layout: at most 16 keys a thread");
+    __shared__ Smem s;
     const int r = blockIdx.y;
     const int j = blockIdx.x;
     const int tid = threadIdx.x;
@@ -719,7 +780,9 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
     const float* src = row + lo;
     for (int i = tid; i < kBins0; i += kThreads) s.h0[i] = 0u;   // under the staging barrier
     for (int i = tid; i < kHistBins; i += kThreads) s.khist[i] = 0u;
-    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && lo + ((n + 3) & ~3) <= a.score_stride) {
+    if constexpr (kCompact) {
+        load_list_vec<P, true>(s, src, n, base, mine, key, nan);
+    } else if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && lo + ((n + 3) & ~3) <= a.score_stride) {
         load_list_vec<P, true>(s, src, n, base, mine, key, nan);
     } else {
         load_list<P>(s, n, base, mine, key, [&](int i) {
@@ -756,14 +819,14 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
             const bool in = i < mine && key[i] >= cut;
             const uint32_t d = in ? at : dummy;
             s.u.stage[kEmitPos + d] = (uint32_t)(base + i);
-            s.u.stage[kEmitKey + d] = key[i];
+            s.u.stage[Smem::kEmitKey + d] = key[i];
             if (in) atomicAdd(&s.khist[kept_bin(key[i], cut)], 1u);
             at += in ? 1u : 0u;
         }
         __syncthreads();
         for (int i = tid; i < (int)total; i += kThreads) {
             cslot[i] = lo + (int)s.u.stage[kEmitPos + i];
-            ckey[i] = s.u.stage[kEmitKey + i];
+            ckey[i] = s.u.stage[Smem::kEmitKey + i];
         }
         for (int b = tid; b < kHistBins; b += kThreads) hist_out[b] = s.khist[b];
         if (tid == 0) {
@@ -780,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(TopkArgs a) {
     emit_to_lds<P>(s, key, base, thr, need, k, tog);
     __syncthreads();
     for (int i = tid; i < k; i += kThreads) {
-        const uint32_t kk = s.u.stage[kEmitKey + i];
+        const uint32_t kk = s.u.stage[Smem::kEmitKey + i];
         cslot[i] = lo + (int)s.u.stage[kEmitPos + i];
         ckey[i] = kk;
         atomicAdd(&s.khist[kept_bin(kk, cut)], 1u);
@@ -1321,8 +1384,22 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
             return hipGetLastError();
         });
     }
+    // The compact filter layout (two workgroups per CU) when there are more
+    // workgroups than CUs to run, every split is a whole 16-byte aligned run
+    // of at most 16 keys a thread (rows 16-byte aligned, score_stride a
+    // multiple of 4: the splits start on multiples of 4) and k fits it.
+    const bool compact = (int64_t)a.n_splits * a.n_rows > kComputeUnits && keys_class(split_max) <= 16 &&
+                         a.top_k <= TopkSmemCompact::kMaxK &&
+                         (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && (a.score_stride & 3) == 0;
     hipError_t e = by_class(keys_class(split_max), [&](auto pc) {
-        topk_filter_kernel<decltype(pc)::value><<<dim3(a.n_splits, a.n_rows), kThreads, 0, stream>>>(a);
+        constexpr int P = decltype(pc)::value;
+        if constexpr (P <= 16) {
+            if (compact) {
+                topk_filter_kernel<P, true><<<dim3(a.n_splits, a.n_rows), kThreads, 0, stream>>>(a);
+                return hipGetLastError();
+            }
+        }
+        topk_filter_kernel<P, false><<<dim3(a.n_splits, a.n_rows), kThreads, 0, stream>>>(a);
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;

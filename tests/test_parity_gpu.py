@@ -157,6 +157,31 @@ def test_topk_bit_exact_on_synthetic_scores(k, n_splits):
         np.testing.assert_array_equal(idx[i], ri)
 
 
+@pytest.mark.parametrize("k,n_splits,stride", [(2048, 4, 65536), (6112, 4, 65536), (6113, 4, 65536),
+                                               (2048, 8, 65536), (512, 5, 69632)])
+def test_topk_more_splits_than_cus(k, n_splits, stride):
+    """80 rows, so more split workgroups than the chip's 256 CUs: the launch
+    takes the compact filter layout (two workgroups a CU; lists of up to 16
+    keys a thread staged in two rounds) for k up to its limit, 6112, and the
+    full layout above it.  Spans cover empty rows, k +- 1, split edges and
+    the whole stride.  Bit-exact against the oracle's global top-k."""
+    rng = np.random.default_rng(7 + k + n_splits)
+    rows = 80
+    spans = [0, 1, k - 1, k, k + 1, 5000, stride // 2 + 3, stride, stride - 1, 16383, 16384, 16385]
+    vis = [min(max(v, 0), stride) for v in (spans * (rows // len(spans) + 1))[:rows]]
+    s = _synthetic_scores(rng, rows, stride, vis)
+    say(f"topk k={k} splits={n_splits} rows={rows} stride={stride}")
+    idx, cnt, st = dsa.topk(torch.from_numpy(s).cuda(), torch.tensor(vis, dtype=torch.int32).cuda(),
+                            k, n_splits)
+    torch.cuda.synchronize()
+    dsa.check_status(st)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for i, v in enumerate(vis):
+        gi, gc = O.topk_global(s[i].astype(np.float64), v, k)
+        assert cnt[i] == gc, (i, v)
+        np.testing.assert_array_equal(idx[i], gi)
+
+
 @pytest.mark.parametrize("n_splits", [1, 3])
 def test_topk_with_infinities_matches_oracle(n_splits):
     """Rows with -inf inside the visible span (tokens on invalid pages, keys
