@@ -92,7 +92,10 @@ def _check(rc: int, what: str):
         raise DsaError(f"{what}: {status_string(rc)} ({rc})")
 
 
-def _ptr(t: torch.Tensor | None, dtype=None, name="tensor") -> int | None:
+def _ptr(t: torch.Tensor | None, dtype=None, name="tensor", shape=None) -> int | None:
+    """Device address of t after checking where it lives, its layout, dtype
+    and, given `shape` (None entries match any size), its shape, so that no
+    call hands the library a buffer smaller than the sizes it is told."""
     if t is None:
         return None
     if not t.is_cuda:
@@ -101,6 +104,9 @@ def _ptr(t: torch.Tensor | None, dtype=None, name="tensor") -> int | None:
         raise DsaError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise DsaError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(w is not None and int(d) != int(w) for d, w in zip(t.shape, shape))):
+        raise DsaError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t.data_ptr()
 
 
@@ -132,8 +138,8 @@ def quantize_q(q_bf16, q_code=None, q_scale=None, stream=None):
         q_code = torch.empty((r, h, d), dtype=torch.uint8, device=q_bf16.device)
     if q_scale is None:
         q_scale = torch.empty((r, h), dtype=torch.float32, device=q_bf16.device)
-    _check(lib().dsa_quantize_q(_ptr(q_bf16, _BF16, "q_bf16"), r, h, d, _ptr(q_code, _FP8, "q_code"),
-                                _ptr(q_scale, torch.float32, "q_scale"), _stream(stream)),
+    _check(lib().dsa_quantize_q(_ptr(q_bf16, _BF16, "q_bf16"), r, h, d, _ptr(q_code, _FP8, "q_code", (r, h, d)),
+                                _ptr(q_scale, torch.float32, "q_scale", (r, h)), _stream(stream)),
            "dsa_quantize_q")
     return q_code, q_scale
 
@@ -153,12 +159,12 @@ def index_scores(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_v
     if status is None:
         status = new_status(q.device)
     _check(lib().dsa_index_scores(
-        _ptr(q, _BF16, "q"), _ptr(head_w, torch.float32, "head_w"), _ptr(k_code, _FP8, "k_code"),
-        _ptr(k_scale, torch.float32, "k_scale"), _ptr(page_table, torch.int32, "page_table"),
-        _ptr(kv_lens, torch.int32, "kv_lens"), _ptr(row_req, torch.int32, "row_req"),
-        _ptr(row_vis, torch.int32, "row_vis"), r, batch, n_pages, max_pages, p, h, d, group_rows,
-        _ptr(scores, torch.float32, "scores"), score_stride, _ptr(status, torch.int32, "status"),
-        _stream(stream)), "dsa_index_scores")
+        _ptr(q, _BF16, "q"), _ptr(head_w, torch.float32, "head_w", (r, h)), _ptr(k_code, _FP8, "k_code"),
+        _ptr(k_scale, torch.float32, "k_scale", (n_pages, p)), _ptr(page_table, torch.int32, "page_table"),
+        _ptr(kv_lens, torch.int32, "kv_lens", (batch,)), _ptr(row_req, torch.int32, "row_req", (r,)),
+        _ptr(row_vis, torch.int32, "row_vis", (r,)), r, batch, n_pages, max_pages, p, h, d, group_rows,
+        _ptr(scores, torch.float32, "scores", (r, score_stride)), score_stride,
+        _ptr(status, torch.int32, "status", (None,)), _stream(stream)), "dsa_index_scores")
     return scores, status
 
 
@@ -191,13 +197,14 @@ def index_topk(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis
         workspace = torch.empty((max(index_topk_workspace_size(r, score_stride, top_k), 1),),
                                 dtype=torch.uint8, device=dev)
     _check(lib().dsa_index_topk(
-        _ptr(q, _BF16, "q"), _ptr(head_w, torch.float32, "head_w"), _ptr(k_code, _FP8, "k_code"),
-        _ptr(k_scale, torch.float32, "k_scale"), _ptr(page_table, torch.int32, "page_table"),
-        _ptr(kv_lens, torch.int32, "kv_lens"), _ptr(row_req, torch.int32, "row_req"),
-        _ptr(row_vis, torch.int32, "row_vis"), r, batch, n_pages, max_pages, p, h, d,
-        _ptr(scores, torch.float32, "scores"), score_stride, top_k, phases, _ptr(workspace, None, "workspace"),
-        workspace.numel() * workspace.element_size(), _ptr(topk_idx, torch.int32, "topk_idx"),
-        _ptr(topk_count, torch.int32, "topk_count"), _ptr(status, torch.int32, "status"), _stream(stream)),
+        _ptr(q, _BF16, "q"), _ptr(head_w, torch.float32, "head_w", (r, h)), _ptr(k_code, _FP8, "k_code"),
+        _ptr(k_scale, torch.float32, "k_scale", (n_pages, p)), _ptr(page_table, torch.int32, "page_table"),
+        _ptr(kv_lens, torch.int32, "kv_lens", (batch,)), _ptr(row_req, torch.int32, "row_req", (r,)),
+        _ptr(row_vis, torch.int32, "row_vis", (r,)), r, batch, n_pages, max_pages, p, h, d,
+        _ptr(scores, torch.float32, "scores", (r, score_stride)), score_stride, top_k, phases,
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(topk_idx, torch.int32, "topk_idx", (r, top_k)), _ptr(topk_count, torch.int32, "topk_count", (r,)),
+        _ptr(status, torch.int32, "status", (None,)), _stream(stream)),
         "dsa_index_topk")
     return scores, topk_idx, topk_count, status
 
@@ -223,10 +230,10 @@ def topk(scores, row_vis, top_k: int, n_splits: int = 1, workspace=None, topk_id
     ws_ptr = _ptr(workspace, None, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().dsa_topk(_ptr(scores, torch.float32, "scores"), stride,
-                          _ptr(row_vis, torch.int32, "row_vis"), r, top_k, n_splits, ws_ptr, ws_bytes,
-                          _ptr(topk_idx, torch.int32, "topk_idx"),
-                          _ptr(topk_count, torch.int32, "topk_count"),
-                          _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_topk")
+                          _ptr(row_vis, torch.int32, "row_vis", (r,)), r, top_k, n_splits, ws_ptr, ws_bytes,
+                          _ptr(topk_idx, torch.int32, "topk_idx", (r, top_k)),
+                          _ptr(topk_count, torch.int32, "topk_count", (r,)),
+                          _ptr(status, torch.int32, "status", (None,)), _stream(stream)), "dsa_topk")
     return topk_idx, topk_count, status
 
 
@@ -252,11 +259,14 @@ def topk_rows(scores, row_vis, row_req, page_table, num_pages: int, page_size: i
     ws_ptr = _ptr(workspace, None, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().dsa_topk_rows(_ptr(scores, torch.float32, "scores"), stride,
-                               _ptr(row_vis, torch.int32, "row_vis"), _ptr(row_req, torch.int32, "row_req"),
+                               _ptr(row_vis, torch.int32, "row_vis", (r,)),
+                               _ptr(row_req, torch.int32, "row_req", (r,)),
                                _ptr(page_table, torch.int32, "page_table"), batch, num_pages, max_pages, page_size,
-                               r, top_k, n_splits, ws_ptr, ws_bytes, _ptr(topk_idx, torch.int32, "topk_idx"),
-                               _ptr(topk_count, torch.int32, "topk_count"), _ptr(topk_rows, torch.int32, "topk_rows"),
-                               _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_topk_rows")
+                               r, top_k, n_splits, ws_ptr, ws_bytes,
+                               _ptr(topk_idx, torch.int32, "topk_idx", (r, top_k)),
+                               _ptr(topk_count, torch.int32, "topk_count", (r,)),
+                               _ptr(topk_rows, torch.int32, "topk_rows", (r, top_k)),
+                               _ptr(status, torch.int32, "status", (None,)), _stream(stream)), "dsa_topk_rows")
     return topk_idx, topk_count, topk_rows, status
 
 
@@ -273,10 +283,10 @@ def topk_noalloc(scores, row_vis, top_k: int, n_splits: int = 1, topk_idx=None, 
     if status is None:
         status = new_status(dev)
     _check(lib().dsa_topk_noalloc(_ptr(scores, torch.float32, "scores"), stride,
-                                  _ptr(row_vis, torch.int32, "row_vis"), r, top_k, n_splits,
-                                  _ptr(topk_idx, torch.int32, "topk_idx"),
-                                  _ptr(topk_count, torch.int32, "topk_count"),
-                                  _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_topk_noalloc")
+                                  _ptr(row_vis, torch.int32, "row_vis", (r,)), r, top_k, n_splits,
+                                  _ptr(topk_idx, torch.int32, "topk_idx", (r, top_k)),
+                                  _ptr(topk_count, torch.int32, "topk_count", (r,)),
+                                  _ptr(status, torch.int32, "status", (None,)), _stream(stream)), "dsa_topk_noalloc")
     return topk_idx, topk_count, status
 
 
@@ -288,6 +298,8 @@ def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_
     kv_cache is the packed uint8 [NP, P, 640] MLA cache (codes, fp32 scale at
     byte 576, pad)."""
     r, h, dq = q.shape
+    if dq != 576:
+        raise DsaError(f"q heads must hold 576 values (512 latent + 64 rope), got {dq}")
     n_pages, p, row_bytes = kv_cache.shape
     if row_bytes != 640:
         raise DsaError(f"kv_cache rows must be 640 bytes, got {row_bytes}")
@@ -308,15 +320,15 @@ def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_
             part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
     _check(lib().dsa_sparse_mla_decode(
         _ptr(q, _BF16, "q"), _ptr(kv_cache, torch.uint8, "kv_cache"),
-        _ptr(page_table, torch.int32, "page_table"), _ptr(row_req, torch.int32, "row_req"),
-        _ptr(row_vis, torch.int32, "row_vis"), _ptr(topk_idx, torch.int32, "topk_idx"),
-        _ptr(topk_count, torch.int32, "topk_count"), r, batch, n_pages, max_pages, p, h, top_k,
+        _ptr(page_table, torch.int32, "page_table"), _ptr(row_req, torch.int32, "row_req", (r,)),
+        _ptr(row_vis, torch.int32, "row_vis", (r,)), _ptr(topk_idx, torch.int32, "topk_idx", (r, top_k)),
+        _ptr(topk_count, torch.int32, "topk_count", (r,)), r, batch, n_pages, max_pages, p, h, top_k,
         n_splits, float(sm_scale),
-        _ptr(part_o, torch.float32, "part_o") if n_splits > 1 else None,
-        _ptr(part_lse, torch.float32, "part_lse") if n_splits > 1 else None,
-        _ptr(out, _BF16, "out") if n_splits == 1 else None,
-        _ptr(out_lse, torch.float32, "out_lse") if n_splits == 1 else None,
-        _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_sparse_mla_decode")
+        _ptr(part_o, torch.float32, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
+        _ptr(part_lse, torch.float32, "part_lse", (r, h, n_splits)) if n_splits > 1 else None,
+        _ptr(out, _BF16, "out", (r, h, 512)) if n_splits == 1 else None,
+        _ptr(out_lse, torch.float32, "out_lse", (r, h)) if n_splits == 1 else None,
+        _ptr(status, torch.int32, "status", (None,)), _stream(stream)), "dsa_sparse_mla_decode")
     if n_splits == 1:
         return out, out_lse, status
     return part_o, part_lse, status
@@ -327,6 +339,8 @@ def sparse_mla_decode_rows(q, kv_cache, row_vis, topk_rows, topk_count, n_splits
     """sparse_mla_decode over physical rows (dsa_sparse_mla_decode_rows); the
     same returns."""
     r, h, dq = q.shape
+    if dq != 576:
+        raise DsaError(f"q heads must hold 576 values (512 latent + 64 rope), got {dq}")
     n_pages, p, row_bytes = kv_cache.shape
     if row_bytes != 640:
         raise DsaError(f"kv_cache rows must be 640 bytes, got {row_bytes}")
@@ -345,14 +359,15 @@ def sparse_mla_decode_rows(q, kv_cache, row_vis, topk_rows, topk_count, n_splits
         if part_lse is None:
             part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
     _check(lib().dsa_sparse_mla_decode_rows(
-        _ptr(q, _BF16, "q"), _ptr(kv_cache, torch.uint8, "kv_cache"), _ptr(row_vis, torch.int32, "row_vis"),
-        _ptr(topk_rows, torch.int32, "topk_rows"), _ptr(topk_count, torch.int32, "topk_count"), r, n_pages, p, h,
+        _ptr(q, _BF16, "q"), _ptr(kv_cache, torch.uint8, "kv_cache"), _ptr(row_vis, torch.int32, "row_vis", (r,)),
+        _ptr(topk_rows, torch.int32, "topk_rows", (r, top_k)), _ptr(topk_count, torch.int32, "topk_count", (r,)),
+        r, n_pages, p, h,
         top_k, n_splits, float(sm_scale),
-        _ptr(part_o, torch.float32, "part_o") if n_splits > 1 else None,
-        _ptr(part_lse, torch.float32, "part_lse") if n_splits > 1 else None,
-        _ptr(out, _BF16, "out") if n_splits == 1 else None,
-        _ptr(out_lse, torch.float32, "out_lse") if n_splits == 1 else None,
-        _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_sparse_mla_decode_rows")
+        _ptr(part_o, torch.float32, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
+        _ptr(part_lse, torch.float32, "part_lse", (r, h, n_splits)) if n_splits > 1 else None,
+        _ptr(out, _BF16, "out", (r, h, 512)) if n_splits == 1 else None,
+        _ptr(out_lse, torch.float32, "out_lse", (r, h)) if n_splits == 1 else None,
+        _ptr(status, torch.int32, "status", (None,)), _stream(stream)), "dsa_sparse_mla_decode_rows")
     if n_splits == 1:
         return out, out_lse, status
     return part_o, part_lse, status
@@ -365,6 +380,8 @@ def sparse_mla_decode_shared(q, kv_cache, page_table, row_req, row_vis, row_list
     [n_lists, k] / topk_count [n_lists] (MTP IndexShare).  Returns as
     sparse_mla_decode."""
     r, h, dq = q.shape
+    if dq != 576:
+        raise DsaError(f"q heads must hold 576 values (512 latent + 64 rope), got {dq}")
     n_pages, p, row_bytes = kv_cache.shape
     if row_bytes != 640:
         raise DsaError(f"kv_cache rows must be 640 bytes, got {row_bytes}")
@@ -385,15 +402,15 @@ def sparse_mla_decode_shared(q, kv_cache, page_table, row_req, row_vis, row_list
             part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
     _check(lib().dsa_sparse_mla_decode_shared(
         _ptr(q, _BF16, "q"), _ptr(kv_cache, torch.uint8, "kv_cache"),
-        _ptr(page_table, torch.int32, "page_table"), _ptr(row_req, torch.int32, "row_req"),
-        _ptr(row_vis, torch.int32, "row_vis"), _ptr(row_list, torch.int32, "row_list"),
-        _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_count, torch.int32, "topk_count"), n_lists,
+        _ptr(page_table, torch.int32, "page_table"), _ptr(row_req, torch.int32, "row_req", (r,)),
+        _ptr(row_vis, torch.int32, "row_vis", (r,)), _ptr(row_list, torch.int32, "row_list", (r,)),
+        _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_count, torch.int32, "topk_count", (n_lists,)), n_lists,
         r, batch, n_pages, max_pages, p, h, top_k, n_splits, float(sm_scale),
-        _ptr(part_o, torch.float32, "part_o") if n_splits > 1 else None,
-        _ptr(part_lse, torch.float32, "part_lse") if n_splits > 1 else None,
-        _ptr(out, _BF16, "out") if n_splits == 1 else None,
-        _ptr(out_lse, torch.float32, "out_lse") if n_splits == 1 else None,
-        _ptr(status, torch.int32, "status"), _stream(stream)), "dsa_sparse_mla_decode_shared")
+        _ptr(part_o, torch.float32, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
+        _ptr(part_lse, torch.float32, "part_lse", (r, h, n_splits)) if n_splits > 1 else None,
+        _ptr(out, _BF16, "out", (r, h, 512)) if n_splits == 1 else None,
+        _ptr(out_lse, torch.float32, "out_lse", (r, h)) if n_splits == 1 else None,
+        _ptr(status, torch.int32, "status", (None,)), _stream(stream)), "dsa_sparse_mla_decode_shared")
     if n_splits == 1:
         return out, out_lse, status
     return part_o, part_lse, status
@@ -408,8 +425,8 @@ def lse_merge(part_o, part_lse, out=None, out_lse=None, stream=None):
     if out_lse is None:
         out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
     _check(lib().dsa_lse_merge(_ptr(part_o, torch.float32, "part_o"),
-                               _ptr(part_lse, torch.float32, "part_lse"), r, h, s, dv,
-                               _ptr(out, _BF16, "out"), _ptr(out_lse, torch.float32, "out_lse"),
+                               _ptr(part_lse, torch.float32, "part_lse", (r, h, s)), r, h, s, dv,
+                               _ptr(out, _BF16, "out", (r, h, dv)), _ptr(out_lse, torch.float32, "out_lse", (r, h)),
                                _stream(stream)), "dsa_lse_merge")
     return out, out_lse
 
@@ -425,9 +442,9 @@ def lse_merge_project(part_o, part_lse, w_uv, out=None, out_lse=None, stream=Non
     if out_lse is None:
         out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
     _check(lib().dsa_lse_merge_project(_ptr(part_o, torch.float32, "part_o"),
-                                       _ptr(part_lse, torch.float32, "part_lse"), r, h, s, dl,
-                                       _ptr(w_uv, _BF16, "w_uv"), dv, _ptr(out, _BF16, "out"),
-                                       _ptr(out_lse, torch.float32, "out_lse"), _stream(stream)),
+                                       _ptr(part_lse, torch.float32, "part_lse", (r, h, s)), r, h, s, dl,
+                                       _ptr(w_uv, _BF16, "w_uv", (h, dv, dl)), dv, _ptr(out, _BF16, "out", (r, h, dv)),
+                                       _ptr(out_lse, torch.float32, "out_lse", (r, h)), _stream(stream)),
            "dsa_lse_merge_project")
     return out, out_lse
 
@@ -444,12 +461,14 @@ def cache_write(latent, rope, index_k, tok_req, tok_slot, page_table, kv_cache, 
         status = new_status(latent.device)
     max_pos = rope_cos.shape[0] if rope_cos is not None else 0
     _check(lib().dsa_cache_write(
-        _ptr(latent, _BF16, "latent"), _ptr(rope, _BF16, "rope"), _ptr(index_k, _BF16, "index_k"),
-        _ptr(rope_cos, torch.float32, "rope_cos"), _ptr(rope_sin, torch.float32, "rope_sin"), max_pos,
-        _ptr(tok_req, torch.int32, "tok_req"), _ptr(tok_slot, torch.int32, "tok_slot"), n,
+        _ptr(latent, _BF16, "latent", (n, 512)), _ptr(rope, _BF16, "rope", (n, 64)),
+        _ptr(index_k, _BF16, "index_k", (n, 128)),
+        _ptr(rope_cos, torch.float32, "rope_cos", (max_pos, 32)),
+        _ptr(rope_sin, torch.float32, "rope_sin", (max_pos, 32)), max_pos,
+        _ptr(tok_req, torch.int32, "tok_req", (n,)), _ptr(tok_slot, torch.int32, "tok_slot", (n,)), n,
         _ptr(page_table, torch.int32, "page_table"), batch, n_pages, max_pages, p,
-        _ptr(kv_cache, torch.uint8, "kv_cache"), _ptr(k_code, _FP8, "k_code"),
-        _ptr(k_scale, torch.float32, "k_scale"), _ptr(status, torch.int32, "status"),
+        _ptr(kv_cache, torch.uint8, "kv_cache", (n_pages, p, 640)), _ptr(k_code, _FP8, "k_code", (n_pages, p, 128)),
+        _ptr(k_scale, torch.float32, "k_scale", (n_pages, p)), _ptr(status, torch.int32, "status", (None,)),
         _stream(stream)), "dsa_cache_write")
     return status
 

@@ -553,6 +553,35 @@ def test_bad_page_id_is_reported_not_read():
         dsa.check_status(step.status)
 
 
+def test_undersized_row_inputs_are_rejected_before_launch():
+    """A row-indexed input or a caller's output with fewer rows than the call
+    is told is a DsaError from the binding: nothing is launched on it."""
+    inp = W.to(W.make("c0"), "cuda")
+    step = run_step(inp, attn_splits=2)
+    r = inp.q_mla.shape[0]
+    args = (inp.q_mla, inp.kv_cache, inp.page_table, inp.row_req, inp.row_vis)
+    short = {"topk_idx": (step.topk_idx[:r - 1].contiguous(), step.topk_count),
+             "topk_count": (step.topk_idx, step.topk_count[:r - 1].contiguous())}
+    for name, (idx, cnt) in short.items():
+        with pytest.raises(dsa.DsaError, match=name):
+            dsa.sparse_mla_decode(*args, idx, cnt, 2, inp.sm_scale)
+    with pytest.raises(dsa.DsaError, match="row_vis"):
+        dsa.sparse_mla_decode(*args[:4], inp.row_vis[:r - 1].contiguous(), step.topk_idx, step.topk_count,
+                              2, inp.sm_scale)
+    with pytest.raises(dsa.DsaError, match="part_o"):
+        dsa.sparse_mla_decode(*args, step.topk_idx, step.topk_count, 2, inp.sm_scale,
+                              part_o=torch.empty((r - 1, inp.q_mla.shape[1], 2, 512), device="cuda"))
+    with pytest.raises(dsa.DsaError, match="row_list"):
+        dsa.sparse_mla_decode_shared(*args, torch.zeros(r - 1, dtype=torch.int32, device="cuda"),
+                                     step.topk_idx, step.topk_count, 2, inp.sm_scale)
+    with pytest.raises(dsa.DsaError, match="row_vis"):
+        dsa.topk(step.scores, inp.row_vis[:r - 1].contiguous(), inp.top_k)
+    with pytest.raises(dsa.DsaError, match="topk_idx"):
+        dsa.topk(step.scores, inp.row_vis, inp.top_k,
+                 topk_idx=torch.empty((r, inp.top_k - 1), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("cfg", ["c0", "c2"])
 def test_graph_replays_match_eager(cfg):
     """The step captured in a HIP graph (as bench.py times it) and replayed
