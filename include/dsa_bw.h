@@ -1,5 +1,5 @@
 /*
- * dsa_bw.h -- C ABI of libdsa_bw.so: two plain bandwidth kernels that the
+ * dsa_bw.h -- C ABI of libdsa_bw.so: plain bandwidth kernels that the
  * benchmark runs beside the step, so that its roofline states what this
  * GPU's HBM delivers in the same run next to the vendor peak.  They are
  * measurement tools, not part of the DSA step.
@@ -27,6 +27,10 @@ extern "C" {
  * loads cannot be removed).
  */
 int dsa_bw_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink, hipStream_t stream);
+
+/* dsa_bw_stream_read with the non-temporal hint on every load (each load
+ * instruction reads whole 128-byte lines). */
+int dsa_bw_stream_read_nt(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink, hipStream_t stream);
 
 /* Copies `bytes` from `src` to `dst` in 16-byte loads and stores, the same
  * partition as dsa_bw_stream_read. */

@@ -205,15 +205,18 @@ def test_bandwidth_library_exports_its_header():
     from sparse_attention_decode_dsa_amd import build as B
     src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "dsa_bw.h")).read(), flags=re.S)
     names = set(re.findall(r"^\s*int\s+(dsa_bw_\w+)\s*\(", src, flags=re.M))
-    assert names == {"dsa_bw_stream_read", "dsa_bw_copy"}
+    assert names == {"dsa_bw_stream_read", "dsa_bw_stream_read_nt", "dsa_bw_copy"}
     L = ctypes.CDLL(B.BW_LIB)
     for n in names:
         assert hasattr(L, n)
     L.dsa_bw_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_void_p]
     L.dsa_bw_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
-    assert L.dsa_bw_stream_read(None, 4096, 8, P, None) == -1
-    assert L.dsa_bw_stream_read(P, 4095, 8, P, None) == -1
+    L.dsa_bw_stream_read_nt.argtypes = L.dsa_bw_stream_read.argtypes
+    for read in (L.dsa_bw_stream_read, L.dsa_bw_stream_read_nt):
+        assert read(None, 4096, 8, P, None) == -1
+        assert read(P, 4095, 8, P, None) == -1
+        assert read(P, 4096, 0, P, None) == -1
     assert L.dsa_bw_copy(P, P + 8, 4096, 8, None) == -1
 
 
