@@ -241,6 +241,10 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
+// The same with the non-temporal hint (for data read once).
+__device__ __forceinline__ void lds_dma16_nt(const void* src, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(lds) : "memory");
+}
 
 // A per-token scale is usable when it is a positive finite number: its bit
 // pattern lies in [0x00000001, 0x7F7FFFFF] (zero, negatives, infinities and
