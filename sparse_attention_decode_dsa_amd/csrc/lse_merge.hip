@@ -5,6 +5,10 @@
 // weight 0 adds nothing, whatever its partial holds.  Up to four splits the
 // partials are read one split at a time; above four, eight splits' loads
 // are in flight together (each measured the faster at its split counts).
+// With fewer than 1024 (row, head) pairs a pair's columns are split over two
+// or four wavefronts (each computing the pair's weights itself), so that a
+// launch of few rows and many splits still reads the partials on most of the
+// chip (long context, 8 rows x 32 heads x 32 splits: see the launch).
 // The partials are read once, with the non-temporal hint: the merge itself
 // runs about 0.3 us slower that way, but replayed bulk-decode steps run about
 // 4 us faster, all of it in the next step's indexer (kernel traces of the
@@ -27,26 +31,68 @@ __device__ __forceinline__ float4 load_partial(const float* p) {
 constexpr int kDv = 512;
 constexpr int kBatch = 8;   // splits whose partials are in flight together (many-split kernel)
 
-// The (row, head) pair of this wavefront, its split weights and the merged
-// LSE; false (after writing the empty result) when no split saw a token.
+// CPL (8, 4 or 2) consecutive output columns per lane: 512 / (64 CPL)
+// wavefronts share one (row, head), so a launch with few pairs still spreads
+// over the chip.
+template <int CPL>
+struct Cols {
+    static constexpr int kParts = kDv / (kWave * CPL);   // wavefronts per (row, head)
+    float v[CPL];
+};
+
+// CPL columns of a partial at p (16-, 8- or 4-byte aligned), non-temporal.
+template <int CPL>
+__device__ __forceinline__ void load_cols(const float* p, float (&x)[CPL]) {
+    if constexpr (CPL == 8) {
+        const float4 a = load_partial(p), b = load_partial(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else if constexpr (CPL == 4) {
+        const float4 a = load_partial(p);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    } else {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 a = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+        x[0] = a.x; x[1] = a.y;
+    }
+}
+
+// The wavefront's (row, head) pair and columns, its split weights and the
+// merged LSE; false (after writing the empty result) when no split saw a
+// token.
 struct MergeHead {
-    int rh, lane, ns;
+    int rh, lane, ns, col;   // col: the lane's first output column
     float wmine;   // e^{lse_lane - m} on lanes < ns, else 0
     float inv;     // 1 / sum of the weights
     float m, tot;
 };
 
+template <int CPL>
+__device__ __forceinline__ void store_cols(uint16_t* dst, const float (&acc)[CPL]) {
+    uint32_t w[CPL / 2];
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i)
+        w[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i]) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+    if constexpr (CPL == 8) *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
+    else if constexpr (CPL == 4) *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+    else *reinterpret_cast<uint32_t*>(dst) = w[0];
+}
+
+template <int CPL>
 __device__ __forceinline__ bool merge_head(const MergeArgs& a, MergeHead& h) {
-    h.rh = blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int kParts = Cols<CPL>::kParts;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    h.rh = w / kParts;
     if (h.rh >= a.n_rows * a.n_heads) return false;  // whole wavefront leaves together
     h.lane = threadIdx.x & 63;
+    h.col = (w % kParts) * kWave * CPL + CPL * h.lane;
     h.ns = a.n_splits;
     const float my = h.lane < h.ns ? a.part_lse[(size_t)h.rh * h.ns + h.lane] : -INFINITY;
     h.m = wave_max(my);
     if (h.m == -INFINITY) {
         // No split saw a token.
-        reinterpret_cast<uint4*>(a.out + (size_t)h.rh * kDv + 8 * h.lane)[0] = uint4{0u, 0u, 0u, 0u};
-        if (a.out_lse != nullptr && h.lane == 0) a.out_lse[h.rh] = -INFINITY;
+        const float zero[CPL] = {};
+        store_cols<CPL>(a.out + (size_t)h.rh * kDv + h.col, zero);
+        if (a.out_lse != nullptr && h.col == 0) a.out_lse[h.rh] = -INFINITY;
         return false;
     }
     h.wmine = h.lane < h.ns ? __expf(my - h.m) : 0.0f;  // e^{-inf} = 0 for empty splits
@@ -55,59 +101,60 @@ __device__ __forceinline__ bool merge_head(const MergeArgs& a, MergeHead& h) {
     return true;
 }
 
-__device__ __forceinline__ void merge_store(const MergeArgs& a, const MergeHead& h, const float (&acc)[8]) {
-    uint4 o;
-    o.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-    o.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-    o.z = (uint32_t)f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16);
-    o.w = (uint32_t)f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
-    reinterpret_cast<uint4*>(a.out + (size_t)h.rh * kDv + 8 * h.lane)[0] = o;
-    if (a.out_lse != nullptr && h.lane == 0) a.out_lse[h.rh] = h.m + __logf(h.tot);
+template <int CPL>
+__device__ __forceinline__ void merge_store(const MergeArgs& a, const MergeHead& h, const float (&acc)[CPL]) {
+    store_cols<CPL>(a.out + (size_t)h.rh * kDv + h.col, acc);
+    if (a.out_lse != nullptr && h.col == 0) a.out_lse[h.rh] = h.m + __logf(h.tot);
 }
 
 // Up to four splits: one split's partials at a time, skipped at weight 0.
+template <int CPL>
 __global__ __launch_bounds__(256) void lse_merge_few_kernel(MergeArgs a) {
     MergeHead h;
-    if (!merge_head(a, h)) return;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const float* po = a.part_o + (size_t)h.rh * h.ns * kDv + 8 * h.lane;
+    if (!merge_head<CPL>(a, h)) return;
+    float acc[CPL] = {};
+    const float* po = a.part_o + (size_t)h.rh * h.ns * kDv + h.col;
     for (int s = 0; s < h.ns; ++s) {
         const float w = __shfl(h.wmine, s) * h.inv;
         if (w == 0.0f) continue;  // uniform across the wavefront
-        const float4 x0 = load_partial(po + (size_t)s * kDv);
-        const float4 x1 = load_partial(po + (size_t)s * kDv + 4);
-        acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
-        acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+        float x[CPL];
+        load_cols<CPL>(po + (size_t)s * kDv, x);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) acc[i] += w * x[i];
     }
-    merge_store(a, h, acc);
+    merge_store<CPL>(a, h, acc);
 }
 
 // More splits: kBatch splits' loads issued before any is used; splits past
 // the end reload the last one and get weight 0.
+template <int CPL>
 __global__ __launch_bounds__(256) void lse_merge_many_kernel(MergeArgs a) {
     MergeHead h;
-    if (!merge_head(a, h)) return;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const float* po = a.part_o + (size_t)h.rh * h.ns * kDv + 8 * h.lane;
+    if (!merge_head<CPL>(a, h)) return;
+    float acc[CPL] = {};
+    const float* po = a.part_o + (size_t)h.rh * h.ns * kDv + h.col;
     for (int s0 = 0; s0 < h.ns; s0 += kBatch) {
-        float4 x[kBatch][2];
+        float x[kBatch][CPL];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const float* p = po + (size_t)min(s0 + b, h.ns - 1) * kDv;
-            x[b][0] = load_partial(p);
-            x[b][1] = load_partial(p + 4);
-        }
+        for (int b = 0; b < kBatch; ++b) load_cols<CPL>(po + (size_t)min(s0 + b, h.ns - 1) * kDv, x[b]);
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             const float w = s0 + b < h.ns ? __shfl(h.wmine, min(s0 + b, h.ns - 1)) * h.inv : 0.0f;
             const bool use = w != 0.0f;
-            acc[0] += use ? w * x[b][0].x : 0.0f; acc[1] += use ? w * x[b][0].y : 0.0f;
-            acc[2] += use ? w * x[b][0].z : 0.0f; acc[3] += use ? w * x[b][0].w : 0.0f;
-            acc[4] += use ? w * x[b][1].x : 0.0f; acc[5] += use ? w * x[b][1].y : 0.0f;
-            acc[6] += use ? w * x[b][1].z : 0.0f; acc[7] += use ? w * x[b][1].w : 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) acc[i] += use ? w * x[b][i] : 0.0f;
         }
     }
-    merge_store(a, h, acc);
+    merge_store<CPL>(a, h, acc);
+}
+
+template <int CPL>
+hipError_t launch_cpl(const MergeArgs& a, hipStream_t stream) {
+    const int64_t waves = (int64_t)a.n_rows * a.n_heads * Cols<CPL>::kParts;
+    const unsigned wgs = (unsigned)((waves + 3) / 4);
+    if (a.n_splits <= 4) lse_merge_few_kernel<CPL><<<wgs, 256, 0, stream>>>(a);
+    else lse_merge_many_kernel<CPL><<<wgs, 256, 0, stream>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -115,9 +162,11 @@ __global__ __launch_bounds__(256) void lse_merge_many_kernel(MergeArgs a) {
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
     const int pairs = a.n_rows * a.n_heads;
     if (pairs == 0) return hipSuccess;
-    if (a.n_splits <= 4) lse_merge_few_kernel<<<(pairs + 3) / 4, 256, 0, stream>>>(a);
-    else lse_merge_many_kernel<<<(pairs + 3) / 4, 256, 0, stream>>>(a);
-    return hipGetLastError();
+    // Enough wavefronts to cover the chip: whole (row, head) pairs when there
+    // are many, else each pair split over two or four wavefronts.
+    if (pairs >= 1024) return launch_cpl<8>(a, stream);
+    if (pairs >= 512) return launch_cpl<4>(a, stream);
+    return launch_cpl<2>(a, stream);
 }
 
 }  // namespace dsa

@@ -248,14 +248,17 @@ def test_topk_all_equal_scores_keep_lowest_slots():
 
 # ------------------------------------------------------------------ LSE merge alone
 
-def test_lse_merge_synthetic():
-    rng = np.random.default_rng(7)
-    r, h, s = 5, 32, 7
+@pytest.mark.parametrize("r,h,s", [(5, 32, 7), (20, 32, 3), (40, 32, 9), (33, 32, 2), (3, 16, 64)])
+def test_lse_merge_synthetic(r, h, s):
+    """Pair counts under 512, under 1024 and above, with the few-split and
+    the many-split kernels (a pair's columns go to 4, 2 or 1 wavefronts)."""
+    rng = np.random.default_rng(7 + r + s)
     po = rng.normal(size=(r, h, s, 512)).astype(np.float32)
     pl = (rng.normal(size=(r, h, s)) * 5).astype(np.float32)
-    pl[0, :, 2] = -np.inf                 # an empty split
+    e = min(2, s - 1)
+    pl[0, :, e] = -np.inf                 # an empty split
     pl[1, 3, :] = -np.inf                 # an empty row
-    po[0, :, 2] = 0.0
+    po[0, :, e] = 0.0
     po[1, 3, :] = 0.0
     out, lse = dsa.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
     torch.cuda.synchronize()
