@@ -201,7 +201,7 @@ int dsa_index_topk(const uint16_t* q, const float* head_w, const uint8_t* k_code
     t.scores = scores; t.score_stride = score_stride; t.row_vis = row_vis;
     t.n_rows = n_rows; t.top_k = top_k; t.n_splits = g.n_chunks;
     t.cand_key = a.cand_key; t.cand_slot = a.cand_slot; t.cand_count = a.cand_count; t.cand_cut = a.cand_cut;
-    t.cand_hist = nullptr; t.cand_cap = g.cap;
+    t.cand_top = nullptr; t.cand_hist = nullptr; t.cand_cap = g.cap;
     t.topk_idx = topk_idx; t.topk_count = topk_count; t.status = status;
     if (phases & DSA_PHASE_SCORE) {
         rc = launch_status(dsa::launch_index_scores(a, stream));
@@ -260,9 +260,9 @@ int dsa_lse_merge_project(const float* part_o, const float* part_lse, int32_t n_
 
 size_t dsa_topk_workspace_size(int32_t n_rows, int32_t top_k, int32_t n_splits) {
     if (n_rows <= 0 || top_k <= 0 || n_splits <= 1) return 0;
-    // keys and slots [n_rows, n_splits, top_k]; counts and cuts [n_rows,
-    // n_splits]; kept-key histograms [n_rows, n_splits, 512]
-    return 2 * topk_ws_keys(n_rows, top_k, n_splits) + (size_t)n_rows * n_splits * (2 + 512) * sizeof(int32_t);
+    // keys and slots [n_rows, n_splits, top_k]; counts, cuts and histogram
+    // tops [n_rows, n_splits]; kept-key histograms [n_rows, n_splits, 512]
+    return 2 * topk_ws_keys(n_rows, top_k, n_splits) + (size_t)n_rows * n_splits * (3 + 512) * sizeof(int32_t);
 }
 
 int dsa_topk(const float* scores, int32_t score_stride, const int32_t* row_vis, int32_t n_rows,
@@ -374,7 +374,7 @@ int topk_launch(const float* scores, int32_t score_stride, const int32_t* row_vi
     a.scores = scores; a.score_stride = score_stride; a.row_vis = row_vis;
     a.n_rows = n_rows; a.top_k = top_k; a.n_splits = n_splits;
     a.cand_key = nullptr; a.cand_slot = nullptr; a.cand_count = nullptr; a.cand_cut = nullptr;
-    a.cand_hist = nullptr;
+    a.cand_top = nullptr; a.cand_hist = nullptr;
     if (n_splits > 1) {
         const size_t need = dsa_topk_workspace_size(n_rows, top_k, n_splits);
         if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
@@ -385,7 +385,8 @@ int topk_launch(const float* scores, int32_t score_stride, const int32_t* row_vi
         a.cand_slot = reinterpret_cast<int32_t*>(ws + kb);
         a.cand_count = reinterpret_cast<int32_t*>(ws + 2 * kb);
         a.cand_cut = a.cand_count + (size_t)n_rows * n_splits;
-        a.cand_hist = a.cand_cut + (size_t)n_rows * n_splits;
+        a.cand_top = a.cand_cut + (size_t)n_rows * n_splits;
+        a.cand_hist = a.cand_top + (size_t)n_rows * n_splits;
     }
     a.topk_idx = topk_idx; a.topk_count = topk_count; a.status = status;
     return launch_status(launch_topk(a, stream));

@@ -42,6 +42,7 @@ struct TopkArgs {
     int32_t* cand_slot;   // [n_rows, n_splits, top_k]: their slots
     int32_t* cand_count;  // [n_rows, n_splits]: how many each split kept
     int32_t* cand_cut;    // [n_rows, n_splits]: the row's cut key, as each split used it
+    int32_t* cand_top;    // [n_rows, n_splits]: the key from which the kept-key histogram's last bin starts
     int32_t* cand_hist;   // [n_rows, n_splits, 512]: histogram of each split's kept keys
     int32_t cand_cap;     // candidates' block length per split (the merge of the indexer's candidates)
     int32_t* topk_idx;

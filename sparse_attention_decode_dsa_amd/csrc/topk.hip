@@ -86,6 +86,7 @@ struct TopkSmemT {
     uint32_t khist[512];   // filter pass: histogram of the kept keys above the cut
     uint32_t bkey[kWave];  // merge: the keys of the threshold bin, and the threshold found among them
     uint32_t bcount;
+    uint32_t kept_top;     // filter pass: the key from which the kept-key histogram's last bin starts
     uint32_t sel_thr;
     uint32_t sel_need_eq;
     uint32_t scan[2][kThreads / kWave + 1];
@@ -719,21 +720,58 @@ __global__ __launch_bounds__(kThreads) void topk_direct_kernel(TopkArgs a) {
 
 constexpr int kSample = 512;
 
-// The filter's histogram of its kept keys: bins of 2^16 key values (1/16 of
-// an octave of scores), counted from the cut's bin, the last bin also
-// holding everything above.  Every kept key is at or above the cut.
+// The filter's histogram of its kept keys: kHistBins bins linear in score
+// value from the cut's value up to the top of the 12-bit key bin of the
+// sample key of rank max(1, floor(rho - 4 sigma - 4)) (the other end of the
+// sample's bracket around rank k); keys at or above that top go to the last
+// bin.  Bins in value rather than in key bits: the kept range can straddle
+// zero (a negative cut under a positive k-th key), and bins of key bits
+// counted from the cut then spend themselves on the octaves around zero and
+// put most of the top k in the last one.  Linear bins leave some ten kept
+// keys in the k-th key's bin at long context and prefill.  The same
+// arithmetic in the filter and the merge gives the same bin for a key, and
+// the bin never decreases as the key grows.
 constexpr int kHistBins = 512;
-__device__ __forceinline__ int kept_bin(uint32_t key, uint32_t cut) {
-    return (int)min((key >> 16) - (cut >> 16), (uint32_t)(kHistBins - 1));
+
+struct KeptBins {
+    uint32_t top;      // keys at or above it: the last bin
+    float lo, scale;   // the cut's value, and bins per unit of score
+};
+
+// The score a monotone key stands for.
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// R of the cut above, or kSample + 1 for "no cut".
+__device__ __forceinline__ KeptBins kept_bins(uint32_t cut, uint32_t top) {
+    KeptBins b;
+    b.top = top;
+    b.lo = key_value(cut);
+    const float hi = key_value(top);
+    b.scale = hi > b.lo ? (float)(kHistBins - 1) / (hi - b.lo) : 0.0f;   // NaN or an empty range: one bin
+    return b;
+}
+
+__device__ __forceinline__ int kept_bin(uint32_t key, const KeptBins& b) {
+    if (key >= b.top) return kHistBins - 1;
+    const float t = (key_value(key) - b.lo) * b.scale;
+    return t > 0.0f ? (int)fminf(t, (float)(kHistBins - 1)) : 0;
+}
+
+// The ranks of the row sample's bracket around the k-th key: R (the cut's,
+// kSample + 1 for "no cut") and the upper end's.
 __device__ __forceinline__ int cut_rank(int v, int k, int S) {
     if (S <= 0) return kSample + 1;
     const float rho = (float)k * (float)S / (float)v;
     const float sigma = sqrtf(fmaxf(rho * (1.0f - rho / (float)S), 0.0f));
     const int R = (int)ceilf(rho + 4.0f * sigma + 4.0f);
     return R > S ? kSample + 1 : R;
+}
+
+__device__ __forceinline__ int top_rank(int v, int k, int S) {
+    const float rho = (float)k * (float)S / (float)v;
+    const float sigma = sqrtf(fmaxf(rho * (1.0f - rho / (float)S), 0.0f));
+    return max(1, (int)floorf(rho - 4.0f * sigma - 4.0f));
 }
 
 // Filter pass: grid (n_splits, n_rows).  Split j of row r writes its kept
@@ -765,6 +803,7 @@ void topk_filter_kernel(TopkArgs a) {
         if (tid == 0) {
             a.cand_count[rj] = 0;
             a.cand_cut[rj] = 0;
+            a.cand_top[rj] = 0;
         }
         for (int b = tid; b < kHistBins; b += kThreads) hist_out[b] = 0u;
         return;
@@ -799,9 +838,12 @@ void topk_filter_kernel(TopkArgs a) {
     if (R <= S) {
         if (tid < S) atomicAdd(&s.h0[bin0(monotone_key(sf))], 1u);
         __syncthreads();
-        find_digit<kBins0>(s, s.h0, (uint32_t)R, tog);
-        cut = s.sel_digit << 20;
+        find_digit2<kBins0>(s, s.h0, (uint32_t)min(top_rank(v, k, S), R), (uint32_t)R, tog);
+        cut = s.sel_digit2 << 20;
     }
+    // The histogram's top waits in LDS (read after later barriers): the
+    // loops below run at the register limit.
+    if (tid == 0) s.kept_top = R <= S ? (s.sel_digit << 20) | 0xFFFFFu : 0xFFFFFFFFu;
     uint32_t c = 0;
 #pragma unroll
     for (int i = 0; i < P; ++i) c += (i < mine && key[i] >= cut) ? 1u : 0u;
@@ -813,25 +855,32 @@ void topk_filter_kernel(TopkArgs a) {
         // Kept keys in list order into the staging buffer (free: the keys
         // are in registers), then out in one coalesced pass.
         pin(cut);
+        int pbase = base;   // pinned: else base + i for every key is computed early and spilled
+        pin(pbase);
         const uint32_t dummy = (uint32_t)k + (uint32_t)(tid & (kWave - 1));
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const bool in = i < mine && key[i] >= cut;
             const uint32_t d = in ? at : dummy;
-            s.u.stage[kEmitPos + d] = (uint32_t)(base + i);
+            s.u.stage[kEmitPos + d] = (uint32_t)(pbase + i);
             s.u.stage[Smem::kEmitKey + d] = key[i];
-            if (in) atomicAdd(&s.khist[kept_bin(key[i], cut)], 1u);
             at += in ? 1u : 0u;
         }
         __syncthreads();
+        // The histogram from the kept keys alone (a small part of the list).
+        const KeptBins bins = kept_bins(cut, s.kept_top);
         for (int i = tid; i < (int)total; i += kThreads) {
+            const uint32_t kk = s.u.stage[Smem::kEmitKey + i];
             cslot[i] = lo + (int)s.u.stage[kEmitPos + i];
-            ckey[i] = s.u.stage[Smem::kEmitKey + i];
+            ckey[i] = kk;
+            atomicAdd(&s.khist[kept_bin(kk, bins)], 1u);
         }
+        __syncthreads();
         for (int b = tid; b < kHistBins; b += kThreads) hist_out[b] = s.khist[b];
         if (tid == 0) {
             a.cand_count[rj] = (int)total;
             a.cand_cut[rj] = (int)cut;
+            a.cand_top[rj] = (int)s.kept_top;
         }
         return;
     }
@@ -842,17 +891,19 @@ void topk_filter_kernel(TopkArgs a) {
     select_kth<P>(s, key, mine, n, k, &thr, &need, tog);
     emit_to_lds<P>(s, key, base, thr, need, k, tog);
     __syncthreads();
+    const KeptBins bins = kept_bins(cut, s.kept_top);
     for (int i = tid; i < k; i += kThreads) {
         const uint32_t kk = s.u.stage[Smem::kEmitKey + i];
         cslot[i] = lo + (int)s.u.stage[kEmitPos + i];
         ckey[i] = kk;
-        atomicAdd(&s.khist[kept_bin(kk, cut)], 1u);
+        atomicAdd(&s.khist[kept_bin(kk, bins)], 1u);
     }
     __syncthreads();
     for (int b = tid; b < kHistBins; b += kThreads) hist_out[b] = s.khist[b];
     if (tid == 0) {
         a.cand_count[rj] = k;
         a.cand_cut[rj] = (int)cut;
+        a.cand_top[rj] = (int)s.kept_top;
     }
 }
 
@@ -1005,13 +1056,13 @@ __device__ __forceinline__ void rank_bin_emit(TopkSmem& s, const uint32_t (&key)
 // (in the staging buffer, slots at kSlotBase); one wavefront ranks bin b's
 // keys exactly and the selection is emitted in list order.
 template <int P, typename Out>
-__device__ __forceinline__ void merge_fast(TopkSmem& s, int nc, int k, uint32_t cut, int bstar, uint32_t need,
-                                           uint32_t m, const Out& out_idx, int& tog) {
+__device__ __forceinline__ void merge_fast(TopkSmem& s, int nc, int k, uint32_t cut, const KeptBins& bins, int bstar,
+                                           uint32_t need, uint32_t m, const Out& out_idx, int& tog) {
     uint32_t key[P];
     int base, mine;
     load_staged<P>(s, nc, key, base, mine);
     rank_bin_emit<P>(s, key, base, mine, k, need, m,
-                     [&](uint32_t x) { return x >= cut && kept_bin(x, cut) == bstar; }, out_idx, tog);
+                     [&](uint32_t x) { return x >= cut && kept_bin(x, bins) == bstar; }, out_idx, tog);
 }
 
 // Emission as in the direct selection (keys above thr, then the first
@@ -1073,6 +1124,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     int cnt_lane = 0;
     if (tid < kWave) cnt_lane = tid < ns ? min(max(a.cand_count[rb + tid], 0), k) : 0;
     const uint32_t cut = (uint32_t)a.cand_cut[rb];
+    const uint32_t top = (uint32_t)a.cand_top[rb];
     uint32_t hs = 0u;
     if (tid < kHistBins) {
         const uint32_t* h = reinterpret_cast<const uint32_t*>(a.cand_hist) + rb * kHistBins + tid;
@@ -1157,9 +1209,10 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     const uint32_t need = s.sel_need;
     const uint32_t m = hsum[bstar];
     if (cut != 0u && slots_fit && total == (uint32_t)nc && m <= (uint32_t)kWave && need >= 1u) {
-        if (nc <= 4 * kThreads) merge_fast<4>(s, nc, k, cut, bstar, need, m, out_idx, tog);
-        else if (nc <= 8 * kThreads) merge_fast<8>(s, nc, k, cut, bstar, need, m, out_idx, tog);
-        else merge_fast<16>(s, nc, k, cut, bstar, need, m, out_idx, tog);
+        const KeptBins bins = kept_bins(cut, top);
+        if (nc <= 4 * kThreads) merge_fast<4>(s, nc, k, cut, bins, bstar, need, m, out_idx, tog);
+        else if (nc <= 8 * kThreads) merge_fast<8>(s, nc, k, cut, bins, bstar, need, m, out_idx, tog);
+        else merge_fast<16>(s, nc, k, cut, bins, bstar, need, m, out_idx, tog);
         return;
     }
     if (nc <= 4 * kThreads) merge_select<4>(a, s, off, ns, nc, k, out_idx, tog);

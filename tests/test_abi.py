@@ -85,7 +85,7 @@ def test_topk_validation_and_workspace(L):
     assert L.dsa_topk_workspace_size(4, 2048, 1) == 0
     need = L.dsa_topk_workspace_size(4, 2048, 16)
     # candidate keys and slots, then a count, a cut and a 512-bin histogram per split
-    assert need == 4 * 16 * 2048 * 8 + 4 * 16 * (2 + 512) * 4
+    assert need == 4 * 16 * 2048 * 8 + 4 * 16 * (3 + 512) * 4
     assert _tk(L, top_k=0) == SHAPE
     assert _tk(L, top_k=8193) == SHAPE
     assert _tk(L, score_stride=32769) == SHAPE                   # one split longer than 32768

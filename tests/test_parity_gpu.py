@@ -234,6 +234,36 @@ def test_topk_cut_that_misses_falls_back_to_the_whole_row(n_splits):
         np.testing.assert_array_equal(idx[i], ri)
 
 
+@pytest.mark.parametrize("n_splits", [4, 16])
+def test_topk_split_merge_over_score_shapes(n_splits):
+    """Rows whose kept keys the merge's histogram must resolve: a kept range
+    across zero (negative cut, positive k-th score), scores a few ulps apart,
+    subnormal scores, scores spread over 60 decades, a range too wide for
+    fp32 (cut near -2.5e38, top near +2.5e38), and a row whose k-th score is
+    shared by a block of equal keys.  Bit-exact against the oracle."""
+    rng = np.random.default_rng(90 + n_splits)
+    r, stride, k = 6, 40000, 2048
+    vis = [5000, 40000, 30000, 40000, 24000, 40000]
+    s = rng.normal(size=(r, stride)).astype(np.float32)
+    s[1] = np.float32(1.0) + np.float32(1e-7) * s[1]
+    s[2] = s[2] * np.float32(1e-40)
+    s[3] = np.sign(s[3]) * np.float32(10.0) ** rng.uniform(-30, 30, stride).astype(np.float32)
+    s[4] = np.where(rng.random(stride) < 0.05, np.float32(2.5e38), np.float32(-2.5e38)) + s[4] * np.float32(1e37)
+    s[5, rng.random(stride) < 0.2] = np.float32(2.0)   # the top ~2.3% ties at 2.0
+    for i, v in enumerate(vis):
+        s[i, v:] = -np.inf
+    assert np.isfinite(s[:, :min(vis)]).all()
+    say(f"topk shapes splits={n_splits}")
+    idx, cnt, st = dsa.topk(torch.from_numpy(s).cuda(), torch.tensor(vis, dtype=torch.int32).cuda(), k, n_splits)
+    torch.cuda.synchronize()
+    dsa.check_status(st)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for i, v in enumerate(vis):
+        ri, rc = O.topk_global(s[i].astype(np.float64), v, k)
+        assert cnt[i] == rc, i
+        np.testing.assert_array_equal(idx[i], ri, err_msg=f"row {i}")
+
+
 def test_topk_all_equal_scores_keep_lowest_slots():
     s = np.zeros((2, 9000), dtype=np.float32)
     vis = [9000, 4097]
