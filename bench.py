@@ -73,10 +73,10 @@ CACHE_WRITE_BYTES_PER_TOKEN = 1024 + 128 + 256 + 256 + 12 + 580 + 132
 
 
 def merge_project_bytes(inp, n_splits: int) -> int:
-    """Per (row, head): S fp32 partials of 512 and S lse read, 128 bf16 and
+    """Per (row, head): S bf16 partials of 512 and S lse read, 128 bf16 and
     one lse written; the bf16 weights [H, 128, 512] once."""
     r, h = inp.n_rows, inp.mla_heads
-    return r * h * (n_splits * (512 * 4 + 4) + 128 * 2 + 4) + h * 128 * 512 * 2
+    return r * h * (n_splits * (512 * 2 + 4) + 128 * 2 + 4) + h * 128 * 512 * 2
 
 
 def algorithmic_bytes(inp) -> dict:

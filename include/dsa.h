@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 10
+#define DSA_ABI_VERSION 11
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -137,14 +137,14 @@ int dsa_cache_write(const uint16_t* latent, const uint16_t* rope, const uint16_t
  *   out[r,h,d]  = sum_k latent[r,h,k] * w_uv[h][d][k]   (fp32 accumulation,
  *                 rounded to bf16)
  *   out_lse[r,h] as dsa_lse_merge (may be NULL).
- *   part_o [n_rows, n_heads, n_splits, d_latent] f32 (16-byte aligned),
+ *   part_o [n_rows, n_heads, n_splits, d_latent] bf16 bit patterns (16-byte aligned),
  *   part_lse [n_rows, n_heads, n_splits] f32, w_uv [n_heads, d_v, d_latent]
  *   bf16 (16-byte aligned; each output dimension's weights one contiguous
  *   row), out [n_rows, n_heads, d_v] bf16.
  * A row no split saw gives out = 0 and lse = -inf.
  * Supported: d_latent == 512, d_v == 128, 1 <= n_splits <= 64.
  */
-int dsa_lse_merge_project(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
+int dsa_lse_merge_project(const uint16_t* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
                           int32_t n_splits, int32_t d_latent, const uint16_t* w_uv, int32_t d_v,
                           uint16_t* out, float* out_lse, hipStream_t stream);
 
@@ -348,9 +348,10 @@ int dsa_topk_noalloc(const float* scores, int32_t score_stride, const int32_t* r
  *   topk_idx [n_rows, top_k] i32, topk_count [n_rows] i32
  * n_splits == 1: writes out [n_rows, n_heads, 512] bf16 (round to nearest
  *   even) and, if out_lse != NULL, out_lse [n_rows, n_heads] f32; part_* unused.
- * n_splits > 1: writes part_o [n_rows, n_heads, n_splits, 512] f32 and
- *   part_lse [n_rows, n_heads, n_splits] f32; out / out_lse unused
- *   (dsa_lse_merge finishes the row).
+ * n_splits > 1: writes part_o [n_rows, n_heads, n_splits, 512] bf16 bit
+ *   patterns (o_s rounded to nearest even; 4-byte aligned, else
+ *   DSA_ERR_SHAPE) and part_lse [n_rows, n_heads, n_splits] f32; out /
+ *   out_lse unused (dsa_lse_merge finishes the row).
  * Supported: n_heads in {16, 32}, page_size a power of two in [16, 1024],
  * 1 <= n_splits <= 64, 1 <= top_k <= 8192.
  */
@@ -359,7 +360,7 @@ int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int3
                           const int32_t* topk_count, int32_t n_rows,
                           int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
                           int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
-                          float* part_o, float* part_lse, uint16_t* out, float* out_lse,
+                          uint16_t* part_o, float* part_lse, uint16_t* out, float* out_lse,
                           int32_t* status, hipStream_t stream);
 
 /*
@@ -382,7 +383,7 @@ int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int3
 int dsa_sparse_mla_decode_rows(const uint16_t* q, const uint8_t* kv_cache, const int32_t* row_vis,
                                const int32_t* topk_rows, const int32_t* topk_count, int32_t n_rows,
                                int32_t num_pages, int32_t page_size, int32_t n_heads, int32_t top_k,
-                               int32_t n_splits, float sm_scale, float* part_o, float* part_lse, uint16_t* out,
+                               int32_t n_splits, float sm_scale, uint16_t* part_o, float* part_lse, uint16_t* out,
                                float* out_lse, int32_t* status, hipStream_t stream);
 
 /*
@@ -408,7 +409,7 @@ int dsa_sparse_mla_decode_shared(const uint16_t* q, const uint8_t* kv_cache, con
                                  const int32_t* topk_idx, const int32_t* topk_count, int32_t n_lists,
                                  int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
                                  int32_t page_size, int32_t n_heads, int32_t top_k, int32_t n_splits,
-                                 float sm_scale, float* part_o, float* part_lse, uint16_t* out, float* out_lse,
+                                 float sm_scale, uint16_t* part_o, float* part_lse, uint16_t* out, float* out_lse,
                                  int32_t* status, hipStream_t stream);
 
 /*
@@ -417,12 +418,13 @@ int dsa_sparse_mla_decode_shared(const uint16_t* q, const uint8_t* kv_cache, con
  *   lse = ln sum_s e^{lse_s};  out = sum_s e^{lse_s - lse} o_s
  * Splits with lse_s = -inf are skipped; a row with no finite lse_s gets
  * out = 0 and lse = -inf.
- *   part_o [n_rows, n_heads, n_splits, d_v] f32, part_lse [n_rows, n_heads, n_splits] f32
+ *   part_o [n_rows, n_heads, n_splits, d_v] bf16 bit patterns, part_lse [n_rows, n_heads, n_splits] f32
  *   out [n_rows, n_heads, d_v] bf16 (round to nearest even)
+ *   part_o and out 16-byte aligned, else DSA_ERR_SHAPE
  *   out_lse [n_rows, n_heads] f32, may be NULL
  * Supported: d_v == 512, 1 <= n_splits <= 64.
  */
-int dsa_lse_merge(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
+int dsa_lse_merge(const uint16_t* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
                   int32_t n_splits, int32_t d_v, uint16_t* out, float* out_lse, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -47,7 +47,7 @@ int mla_checked(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_
                 const int32_t* row_vis, const int32_t* row_list, const int32_t* topk_idx,
                 const int32_t* topk_count, int32_t n_lists, int32_t n_rows, int32_t batch, int32_t num_pages,
                 int32_t max_pages, int32_t page_size, int32_t n_heads, int32_t top_k, int32_t n_splits,
-                float sm_scale, float* part_o, float* part_lse, uint16_t* out, float* out_lse, int32_t* status,
+                float sm_scale, uint16_t* part_o, float* part_lse, uint16_t* out, float* out_lse, int32_t* status,
                 hipStream_t stream, const int32_t* topk_rows = nullptr) {
     if (n_rows < 0 || n_rows > kMaxRows || n_heads < 1) return DSA_ERR_SHAPE;
     if (top_k < 1 || top_k > dsa::kTopkMaxK) return DSA_ERR_SHAPE;
@@ -62,6 +62,7 @@ int mla_checked(const uint16_t* q, const uint8_t* kv_cache, const int32_t* page_
         return DSA_ERR_NULL;
     }
     if (n_splits == 1 ? !out : (!part_o || !part_lse)) return DSA_ERR_NULL;
+    if (n_splits > 1 && (reinterpret_cast<uintptr_t>(part_o) & 3) != 0) return DSA_ERR_SHAPE;   // 4-byte stores
     if (n_rows == 0) return DSA_OK;
     dsa::MlaArgs a{};
     a.topk_rows = topk_rows;
@@ -241,7 +242,7 @@ int dsa_cache_write(const uint16_t* latent, const uint16_t* rope, const uint16_t
     return launch_status(dsa::launch_cache_write(a, stream));
 }
 
-int dsa_lse_merge_project(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
+int dsa_lse_merge_project(const uint16_t* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
                           int32_t n_splits, int32_t d_latent, const uint16_t* w_uv, int32_t d_v,
                           uint16_t* out, float* out_lse, hipStream_t stream) {
     if (n_rows < 0 || n_rows > kMaxRows * 8 || n_heads < 1 || n_heads > 65535) return DSA_ERR_SHAPE;
@@ -297,7 +298,7 @@ int dsa_topk_rows(const float* scores, int32_t score_stride, const int32_t* row_
 int dsa_sparse_mla_decode_rows(const uint16_t* q, const uint8_t* kv_cache, const int32_t* row_vis,
                                const int32_t* topk_rows, const int32_t* topk_count, int32_t n_rows,
                                int32_t num_pages, int32_t page_size, int32_t n_heads, int32_t top_k,
-                               int32_t n_splits, float sm_scale, float* part_o, float* part_lse, uint16_t* out,
+                               int32_t n_splits, float sm_scale, uint16_t* part_o, float* part_lse, uint16_t* out,
                                float* out_lse, int32_t* status, hipStream_t stream) {
     if (!topk_rows) return DSA_ERR_NULL;
     // One request of one page: the geometry a physical-row list needs.
@@ -311,7 +312,7 @@ int dsa_sparse_mla_decode(const uint16_t* q, const uint8_t* kv_cache, const int3
                           const int32_t* topk_count, int32_t n_rows,
                           int32_t batch, int32_t num_pages, int32_t max_pages, int32_t page_size,
                           int32_t n_heads, int32_t top_k, int32_t n_splits, float sm_scale,
-                          float* part_o, float* part_lse, uint16_t* out, float* out_lse,
+                          uint16_t* part_o, float* part_lse, uint16_t* out, float* out_lse,
                           int32_t* status, hipStream_t stream) {
     return mla_checked(q, kv_cache, page_table, row_req, row_vis, nullptr, topk_idx, topk_count, n_rows, n_rows,
                        batch, num_pages, max_pages, page_size, n_heads, top_k, n_splits, sm_scale, part_o,
@@ -323,7 +324,7 @@ int dsa_sparse_mla_decode_shared(const uint16_t* q, const uint8_t* kv_cache, con
                                  const int32_t* topk_idx, const int32_t* topk_count, int32_t n_lists,
                                  int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
                                  int32_t page_size, int32_t n_heads, int32_t top_k, int32_t n_splits,
-                                 float sm_scale, float* part_o, float* part_lse, uint16_t* out, float* out_lse,
+                                 float sm_scale, uint16_t* part_o, float* part_lse, uint16_t* out, float* out_lse,
                                  int32_t* status, hipStream_t stream) {
     if (n_lists < 1 || n_lists > kMaxRows) return DSA_ERR_SHAPE;
     if (!row_list) return DSA_ERR_NULL;
@@ -332,13 +333,14 @@ int dsa_sparse_mla_decode_shared(const uint16_t* q, const uint8_t* kv_cache, con
                        part_lse, out, out_lse, status, stream);
 }
 
-int dsa_lse_merge(const float* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
+int dsa_lse_merge(const uint16_t* part_o, const float* part_lse, int32_t n_rows, int32_t n_heads,
                   int32_t n_splits, int32_t d_v, uint16_t* out, float* out_lse, hipStream_t stream) {
     if (n_rows < 0 || n_heads < 1 || d_v < 1) return DSA_ERR_SHAPE;
     if (n_splits < 1 || n_splits > dsa::kMaxSplits) return DSA_ERR_SHAPE;
     if ((int64_t)n_rows * n_heads > INT32_MAX / 256) return DSA_ERR_SHAPE;
     if (d_v != 512) return DSA_ERR_UNSUPPORTED;
     if (!part_o || !part_lse || !out) return DSA_ERR_NULL;
+    if (((reinterpret_cast<uintptr_t>(part_o) | reinterpret_cast<uintptr_t>(out)) & 15) != 0) return DSA_ERR_SHAPE;
     if (n_rows == 0) return DSA_OK;
     dsa::MergeArgs a;
     a.part_o = part_o; a.part_lse = part_lse; a.n_rows = n_rows; a.n_heads = n_heads;

@@ -69,7 +69,7 @@ struct MlaArgs {
     const int32_t* topk_rows;
     int32_t n_rows, batch, num_pages, max_pages, page_size, log2_page, n_heads, top_k, n_splits;
     float sm_scale;
-    float* part_o;
+    uint16_t* part_o;          // bf16 bit patterns
     float* part_lse;
     uint16_t* out;
     float* out_lse;
@@ -102,7 +102,7 @@ struct CacheWriteArgs {
 };
 
 struct MergeProjectArgs {
-    const float* part_o;       // [n_rows, n_heads, n_splits, 512]
+    const uint16_t* part_o;    // [n_rows, n_heads, n_splits, 512] bf16
     const float* part_lse;     // [n_rows, n_heads, n_splits]
     const uint16_t* w_uv;      // [n_heads, 128, 512] bf16
     int32_t n_rows, n_heads, n_splits;
@@ -111,7 +111,7 @@ struct MergeProjectArgs {
 };
 
 struct MergeArgs {
-    const float* part_o;
+    const uint16_t* part_o;    // bf16
     const float* part_lse;
     int32_t n_rows, n_heads, n_splits;
     uint16_t* out;

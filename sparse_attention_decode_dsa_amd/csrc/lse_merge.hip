@@ -1,4 +1,6 @@
-// Merge of split-K partials by their natural-log LSE.
+// Merge of split-K partials by their natural-log LSE.  The partials are bf16
+// (the attention rounds each split's normalised output to nearest even);
+// the weights and the sum are fp32.
 // One wavefront per (row, head): lane s (< n_splits) reads lse_s, the
 // wavefront finds m = max_s lse_s and the weights e^{lse_s - m}; each lane
 // then accumulates 8 of the 512 output columns over the splits.  A split of
@@ -20,13 +22,8 @@ namespace dsa {
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// 16 bytes of a partial, loaded with the non-temporal hint.
-__device__ __forceinline__ float4 load_partial(const float* p) {
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    return float4{v.x, v.y, v.z, v.w};
-}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDv = 512;
 constexpr int kBatch = 8;   // splits whose partials are in flight together (many-split kernel)
@@ -40,19 +37,24 @@ struct Cols {
     float v[CPL];
 };
 
-// CPL columns of a partial at p (16-, 8- or 4-byte aligned), non-temporal.
+// CPL bf16 columns of a partial at p (16-, 8- or 4-byte aligned), loaded
+// with the non-temporal hint and widened to fp32.
 template <int CPL>
-__device__ __forceinline__ void load_cols(const float* p, float (&x)[CPL]) {
+__device__ __forceinline__ void load_cols(const uint16_t* p, float (&x)[CPL]) {
+    uint32_t w[CPL / 2];
     if constexpr (CPL == 8) {
-        const float4 a = load_partial(p), b = load_partial(p + 4);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     } else if constexpr (CPL == 4) {
-        const float4 a = load_partial(p);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        w[0] = v.x; w[1] = v.y;
     } else {
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x2 a = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
-        x[0] = a.x; x[1] = a.y;
+        w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    }
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
 }
 
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void lse_merge_few_kernel(MergeArgs a) {
     MergeHead h;
     if (!merge_head<CPL>(a, h)) return;
     float acc[CPL] = {};
-    const float* po = a.part_o + (size_t)h.rh * h.ns * kDv + h.col;
+    const uint16_t* po = a.part_o + (size_t)h.rh * h.ns * kDv + h.col;
     for (int s = 0; s < h.ns; ++s) {
         const float w = __shfl(h.wmine, s) * h.inv;
         if (w == 0.0f) continue;  // uniform across the wavefront
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256) void lse_merge_many_kernel(MergeArgs a) {
     MergeHead h;
     if (!merge_head<CPL>(a, h)) return;
     float acc[CPL] = {};
-    const float* po = a.part_o + (size_t)h.rh * h.ns * kDv + h.col;
+    const uint16_t* po = a.part_o + (size_t)h.rh * h.ns * kDv + h.col;
     for (int s0 = 0; s0 < h.ns; s0 += kBatch) {
         float x[kBatch][CPL];
 #pragma unroll

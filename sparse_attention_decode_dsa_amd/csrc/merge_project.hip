@@ -73,9 +73,12 @@ __global__ __launch_bounds__(256) void merge_project_kernel(MergeProjectArgs a) 
         for (int b = 0; b < kPairs; ++b) {
             const int p = min(p0 + b, np - 1);
             const int j = p / ns;
-            const float* src = a.part_o + ((size_t)rh[j] * ns + (p - j * ns)) * kLatent + 8 * lane;
-            x[b][0] = reinterpret_cast<const float4*>(src)[0];
-            x[b][1] = reinterpret_cast<const float4*>(src)[1];
+            const uint16_t* src = a.part_o + ((size_t)rh[j] * ns + (p - j * ns)) * kLatent + 8 * lane;
+            const uint4 u = *reinterpret_cast<const uint4*>(src);   // 8 bf16 partials
+            x[b][0] = float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                             __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+            x[b][1] = float4{__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xFFFF0000u),
+                             __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xFFFF0000u)};
         }
     };
     // The first pairs go out with the LSEs, before their weights are known.

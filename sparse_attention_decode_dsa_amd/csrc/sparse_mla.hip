@@ -700,9 +700,22 @@ __global__ __launch_bounds__(256 * HB) void sparse_mla_kernel(MlaArgs a) {
                 for (int cb = 0; cb < NCB; ++cb) dst[16 * cb] = f32_to_bf16_rne(o_acc[h2][cb][i] * inv);
                 if (a.out_lse != nullptr && wv == 0 && nn == 0) a.out_lse[rh] = lse;
             } else {
-                float* dst = a.part_o + (rh * ns + sp) * kDv + CW * wv + nn;
+                // bf16 partials, two columns a lane: lanes nn and nn ^ 1
+                // swap one value of a block pair, so the even lane writes
+                // columns (nn, nn + 1) of block cb and the odd lane those of
+                // block cb + 1.
+                static_assert(NCB % 2 == 0, "column blocks in pairs");
+                const bool odd = (nn & 1) != 0;
+                uint16_t* dst = a.part_o + (rh * ns + sp) * kDv + CW * wv + (nn & ~1);
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) dst[16 * cb] = o_acc[h2][cb][i] * inv;
+                for (int cb = 0; cb < NCB; cb += 2) {
+                    const uint32_t v0 = f32_to_bf16_rne(o_acc[h2][cb][i] * inv);
+                    const uint32_t v1 = f32_to_bf16_rne(o_acc[h2][cb + 1][i] * inv);
+                    const uint32_t got =
+                        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(odd ? v0 : v1), 0xB1, 0xF, 0xF, false);
+                    *reinterpret_cast<uint32_t*>(dst + 16 * (cb + (odd ? 1 : 0))) =
+                        odd ? (got | (v1 << 16)) : (v0 | (got << 16));
+                }
                 if (wv == 0 && nn == 0) a.part_lse[rh * ns + sp] = lse;
             }
         }

@@ -17,7 +17,7 @@ import os
 
 import torch
 
-ABI_VERSION = 10
+ABI_VERSION = 11
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE", 64: "SCALE"}
@@ -294,7 +294,7 @@ def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_
                       n_splits: int = 1, sm_scale: float = 1.0 / 24.0, part_o=None, part_lse=None,
                       out=None, out_lse=None, status=None, stream=None):
     """Split-K sparse MLA of the bf16 query q [R, H, 576].  n_splits == 1 -> (out bf16 [R,H,512], out_lse f32
-    [R,H]); otherwise -> (part_o f32 [R,H,S,512], part_lse f32 [R,H,S]).
+    [R,H]); otherwise -> (part_o bf16 [R,H,S,512], part_lse f32 [R,H,S]).
     kv_cache is the packed uint8 [NP, P, 640] MLA cache (codes, fp32 scale at
     byte 576, pad)."""
     r, h, dq = q.shape
@@ -315,7 +315,7 @@ def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_
             out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
     else:
         if part_o is None:
-            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.float32, device=dev)
+            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.bfloat16, device=dev)
         if part_lse is None:
             part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
     _check(lib().dsa_sparse_mla_decode(
@@ -324,7 +324,7 @@ def sparse_mla_decode(q, kv_cache, page_table, row_req, row_vis, topk_idx, topk_
         _ptr(row_vis, torch.int32, "row_vis", (r,)), _ptr(topk_idx, torch.int32, "topk_idx", (r, top_k)),
         _ptr(topk_count, torch.int32, "topk_count", (r,)), r, batch, n_pages, max_pages, p, h, top_k,
         n_splits, float(sm_scale),
-        _ptr(part_o, torch.float32, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
+        _ptr(part_o, torch.bfloat16, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
         _ptr(part_lse, torch.float32, "part_lse", (r, h, n_splits)) if n_splits > 1 else None,
         _ptr(out, _BF16, "out", (r, h, 512)) if n_splits == 1 else None,
         _ptr(out_lse, torch.float32, "out_lse", (r, h)) if n_splits == 1 else None,
@@ -355,7 +355,7 @@ def sparse_mla_decode_rows(q, kv_cache, row_vis, topk_rows, topk_count, n_splits
             out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
     else:
         if part_o is None:
-            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.float32, device=dev)
+            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.bfloat16, device=dev)
         if part_lse is None:
             part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
     _check(lib().dsa_sparse_mla_decode_rows(
@@ -363,7 +363,7 @@ def sparse_mla_decode_rows(q, kv_cache, row_vis, topk_rows, topk_count, n_splits
         _ptr(topk_rows, torch.int32, "topk_rows", (r, top_k)), _ptr(topk_count, torch.int32, "topk_count", (r,)),
         r, n_pages, p, h,
         top_k, n_splits, float(sm_scale),
-        _ptr(part_o, torch.float32, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
+        _ptr(part_o, torch.bfloat16, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
         _ptr(part_lse, torch.float32, "part_lse", (r, h, n_splits)) if n_splits > 1 else None,
         _ptr(out, _BF16, "out", (r, h, 512)) if n_splits == 1 else None,
         _ptr(out_lse, torch.float32, "out_lse", (r, h)) if n_splits == 1 else None,
@@ -397,7 +397,7 @@ def sparse_mla_decode_shared(q, kv_cache, page_table, row_req, row_vis, row_list
             out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
     else:
         if part_o is None:
-            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.float32, device=dev)
+            part_o = torch.empty((r, h, n_splits, 512), dtype=torch.bfloat16, device=dev)
         if part_lse is None:
             part_lse = torch.empty((r, h, n_splits), dtype=torch.float32, device=dev)
     _check(lib().dsa_sparse_mla_decode_shared(
@@ -406,7 +406,7 @@ def sparse_mla_decode_shared(q, kv_cache, page_table, row_req, row_vis, row_list
         _ptr(row_vis, torch.int32, "row_vis", (r,)), _ptr(row_list, torch.int32, "row_list", (r,)),
         _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_count, torch.int32, "topk_count", (n_lists,)), n_lists,
         r, batch, n_pages, max_pages, p, h, top_k, n_splits, float(sm_scale),
-        _ptr(part_o, torch.float32, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
+        _ptr(part_o, torch.bfloat16, "part_o", (r, h, n_splits, 512)) if n_splits > 1 else None,
         _ptr(part_lse, torch.float32, "part_lse", (r, h, n_splits)) if n_splits > 1 else None,
         _ptr(out, _BF16, "out", (r, h, 512)) if n_splits == 1 else None,
         _ptr(out_lse, torch.float32, "out_lse", (r, h)) if n_splits == 1 else None,
@@ -424,7 +424,7 @@ def lse_merge(part_o, part_lse, out=None, out_lse=None, stream=None):
         out = torch.empty((r, h, dv), dtype=torch.bfloat16, device=dev)
     if out_lse is None:
         out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
-    _check(lib().dsa_lse_merge(_ptr(part_o, torch.float32, "part_o"),
+    _check(lib().dsa_lse_merge(_ptr(part_o, torch.bfloat16, "part_o"),
                                _ptr(part_lse, torch.float32, "part_lse", (r, h, s)), r, h, s, dv,
                                _ptr(out, _BF16, "out", (r, h, dv)), _ptr(out_lse, torch.float32, "out_lse", (r, h)),
                                _stream(stream)), "dsa_lse_merge")
@@ -441,7 +441,7 @@ def lse_merge_project(part_o, part_lse, w_uv, out=None, out_lse=None, stream=Non
         out = torch.empty((r, h, dv), dtype=torch.bfloat16, device=dev)
     if out_lse is None:
         out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)
-    _check(lib().dsa_lse_merge_project(_ptr(part_o, torch.float32, "part_o"),
+    _check(lib().dsa_lse_merge_project(_ptr(part_o, torch.bfloat16, "part_o"),
                                        _ptr(part_lse, torch.float32, "part_lse", (r, h, s)), r, h, s, dl,
                                        _ptr(w_uv, _BF16, "w_uv", (h, dv, dl)), dv, _ptr(out, _BF16, "out", (r, h, dv)),
                                        _ptr(out_lse, torch.float32, "out_lse", (r, h)), _stream(stream)),
@@ -533,7 +533,7 @@ class DecodeStep:
         self.topk_rows = torch.empty((n_sel, k), dtype=torch.int32, device=dev) if self.phys_rows else None
         self.topk_count = torch.empty((n_sel,), dtype=torch.int32, device=dev)
         s = self.attn_splits
-        self.part_o = torch.empty((r, h, s, 512), dtype=torch.float32, device=dev) if s > 1 else None
+        self.part_o = torch.empty((r, h, s, 512), dtype=torch.bfloat16, device=dev) if s > 1 else None
         self.part_lse = torch.empty((r, h, s), dtype=torch.float32, device=dev) if s > 1 else None
         self.out = torch.empty((r, h, 512), dtype=torch.bfloat16, device=dev)
         self.out_lse = torch.empty((r, h), dtype=torch.float32, device=dev)

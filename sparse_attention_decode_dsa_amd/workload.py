@@ -402,7 +402,7 @@ def make_w_uv(n_heads: int, seed: int = 0, device="cpu") -> torch.Tensor:
 
 
 def make_partials(n_rows: int, n_heads: int, n_splits: int, seed: int = 0, device="cpu"):
-    """Seeded split partials for the merge: part_o N(0, 1) f32 [R, H, S, 512],
+    """Seeded split partials for the merge: part_o N(0, 1) bf16 [R, H, S, 512],
     part_lse N(0, 9) f32 [R, H, S], with an empty split (lse -inf, o 0) and,
     for R >= 3, a row whose splits are all empty."""
     g = torch.Generator().manual_seed(seed)
@@ -414,4 +414,4 @@ def make_partials(n_rows: int, n_heads: int, n_splits: int, seed: int = 0, devic
     if n_rows >= 3:
         pl[2, :, :] = -math.inf
         po[2, :, :, :] = 0.0
-    return po.to(device), pl.to(device)
+    return po.to(torch.bfloat16).to(device), pl.to(device)

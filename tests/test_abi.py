@@ -114,6 +114,7 @@ def test_sparse_mla_validation(L):
     assert _mla(L, sm_scale=float("nan")) == SHAPE
     assert _mla(L, sm_scale=float("inf")) == SHAPE
     assert _mla(L, part_o=None) == NULL                      # split path needs partials
+    assert _mla(L, part_o=P + 2) == SHAPE                    # bf16 partials go out 4 bytes a lane
     assert _mla(L, n_splits=1, out=None) == NULL             # lone split needs out
     assert _mla(L, page_size=48) == UNSUP
     assert _mla(L, q=None) == NULL
@@ -127,6 +128,8 @@ def test_lse_merge_and_quantize_validation(L):
     assert m(P, P, 4, 32, 65, 512, P, None, None) == SHAPE
     assert m(None, P, 4, 32, 4, 512, P, None, None) == NULL
     assert m(P, P, 4, 32, 4, 512, None, None, None) == NULL
+    assert m(P + 8, P, 4, 32, 4, 512, P, None, None) == SHAPE   # 16-byte aligned partials and output
+    assert m(P, P, 4, 32, 4, 512, P + 2, None, None) == SHAPE
     assert m(P, P, 0, 32, 4, 512, P, None, None) == OK
     q = L.dsa_quantize_q
     assert q(P, 4, 64, 64, P, P, None) == UNSUP

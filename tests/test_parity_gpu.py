@@ -290,9 +290,10 @@ def test_lse_merge_synthetic(r, h, s):
     pl[1, 3, :] = -np.inf                 # an empty row
     po[0, :, e] = 0.0
     po[1, 3, :] = 0.0
-    out, lse = dsa.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    po_b = torch.from_numpy(po).to(torch.bfloat16)     # the partials' format; the oracle merges the same values
+    out, lse = dsa.lse_merge(po_b.cuda(), torch.from_numpy(pl).cuda())
     torch.cuda.synchronize()
-    ro, rl = O.lse_merge(po.astype(np.float64), pl.astype(np.float64))
+    ro, rl = O.lse_merge(po_b.double().numpy(), pl.astype(np.float64))
     check_out(bf16_to_f64(out), lse.cpu().double().numpy(), ro, rl)
     assert np.all(out[1, 3].float().cpu().numpy() == 0) and np.isneginf(lse[1, 3].item())
 
@@ -603,7 +604,8 @@ def test_undersized_row_inputs_are_rejected_before_launch():
                               2, inp.sm_scale)
     with pytest.raises(dsa.DsaError, match="part_o"):
         dsa.sparse_mla_decode(*args, step.topk_idx, step.topk_count, 2, inp.sm_scale,
-                              part_o=torch.empty((r - 1, inp.q_mla.shape[1], 2, 512), device="cuda"))
+                              part_o=torch.empty((r - 1, inp.q_mla.shape[1], 2, 512), dtype=torch.bfloat16,
+                                                 device="cuda"))
     with pytest.raises(dsa.DsaError, match="row_list"):
         dsa.sparse_mla_decode_shared(*args, torch.zeros(r - 1, dtype=torch.int32, device="cuda"),
                                      step.topk_idx, step.topk_count, 2, inp.sm_scale)
