@@ -249,8 +249,9 @@ int dsa_index_topk(const uint16_t* q, const float* head_w, const uint8_t* k_code
 
 /*
  * Workspace bytes dsa_topk needs for n_splits > 1: room for top_k candidate
- * keys and slots per split and row, and one count per split and row.  0 when
- * n_splits == 1.  The caller
+ * keys and slots per split and row; per split and row a count, the cut, the
+ * top of the kept-key histogram and a 512-bin histogram (all 32-bit).  0 when
+ * n_splits == 1.  The contents are internal to the call.  The caller
  * reserves the workspace once, up front, and a call with a smaller one is
  * rejected (DSA_ERR_WORKSPACE) rather than served by an allocation (page
  * "Harden DeepSeek V4 DSpark DP2 serving", section 6.3: workspaces reserved
