@@ -381,7 +381,7 @@ def main():
                 "index_scores": lambda: dsa.index_scores(
                     st.lead_q, st.lead_w, i.k_code, i.k_scale, i.page_table, i.kv_lens,
                     st.lead_req, st.lead_vis, group_rows=st.group_rows, score_stride=st.score_stride,
-                    scores=st.scores, status=st.status),
+                    scores=st.scores, status=st.status, whole_rows=st.whole_rows),
                 "topk": lambda: dsa.topk(st.scores, st.lead_vis, i.top_k, st.index_splits,
                                          workspace=st.workspace, topk_idx=st.topk_idx,
                                          topk_count=st.topk_count, status=st.status),

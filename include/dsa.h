@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 11
+#define DSA_ABI_VERSION 12
 
 /* Host validation status (return value of every entry point). */
 enum {
@@ -196,15 +196,23 @@ int dsa_quantize_q(const uint16_t* q_bf16, int32_t n_rows, int32_t n_heads, int3
  * group_rows (1..8, dividing n_rows): that many consecutive rows are scored
  * against one stream of keys (MTP verify and prefill rows of one request);
  * all rows of a group must share a request, else DSA_DEV_GROUP.
+ * flags: 0, or DSA_INDEX_WHOLE_ROWS with group_rows == 1: the caller knows
+ * (from the lengths it holds on the host) that every row's span is at least
+ * three quarters of score_stride, so the launch streams keys on the whole
+ * chip to its end; the keys are then read as whole 128-byte rows with the
+ * non-temporal hint (faster there, slower for ragged rows).  The scores are
+ * the same either way.  Other bits: DSA_ERR_SHAPE.
  * Supported: n_heads == 64, head_dim == 128, page_size a power of two in
  * [16, 1024].  All scales must be finite and > 0.
  */
+#define DSA_INDEX_WHOLE_ROWS 1
 int dsa_index_scores(const uint16_t* q, const float* head_w,
                      const uint8_t* k_code, const float* k_scale, const int32_t* page_table,
                      const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,
                      int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
                      int32_t page_size, int32_t n_heads, int32_t head_dim, int32_t group_rows,
-                     float* scores, int32_t score_stride, int32_t* status, hipStream_t stream);
+                     int32_t flags, float* scores, int32_t score_stride, int32_t* status,
+                     hipStream_t stream);
 
 /*
  * dsa_index_topk -- steps 1 and 2 for decode rows (one row per scoring

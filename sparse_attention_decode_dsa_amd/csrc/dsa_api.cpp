@@ -155,12 +155,17 @@ int dsa_index_scores(const uint16_t* q, const float* head_w,
                      const int32_t* kv_lens, const int32_t* row_req, const int32_t* row_vis,
                      int32_t n_rows, int32_t batch, int32_t num_pages, int32_t max_pages,
                      int32_t page_size, int32_t n_heads, int32_t head_dim, int32_t group_rows,
-                     float* scores, int32_t score_stride, int32_t* status, hipStream_t stream) {
+                     int32_t flags, float* scores, int32_t score_stride, int32_t* status,
+                     hipStream_t stream) {
     dsa::IndexArgs a{};
     const int rc = index_checked(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis, n_rows, batch,
                                  num_pages, max_pages, page_size, n_heads, head_dim, group_rows, scores,
                                  score_stride, status, a);
-    if (rc != DSA_OK || n_rows == 0) return rc;
+    if (rc != DSA_OK) return rc;
+    if ((flags & ~DSA_INDEX_WHOLE_ROWS) != 0 || ((flags & DSA_INDEX_WHOLE_ROWS) && group_rows != 1))
+        return DSA_ERR_SHAPE;
+    if (n_rows == 0) return DSA_OK;
+    a.whole_rows = (flags & DSA_INDEX_WHOLE_ROWS) ? 1 : 0;
     return launch_status(dsa::launch_index_scores(a, stream));
 }
 

@@ -63,6 +63,25 @@ __device__ __forceinline__ v8i load_q_operand(const uint8_t* head_row, int g) {
     return r;
 }
 
+// Whole-row key loads of a 16-token block (kWhole): load A reads rows 0-7
+// of the block, load B rows 8-15, each 8 whole 128-byte rows.  Lane (n, g)
+// with n < 8 gets (row n, bytes 16g) in A and (row n + 8, bytes 64 + 16g) in
+// B; with n >= 8 it gets (row n - 8, bytes 64 + 16g) in A and (row n, bytes
+// 16g) in B.  Lanes n and n ^ 8 trade the piece that belongs to the other's
+// row (a DPP rotation of each 16-lane row by 8), which leaves every lane the
+// operand of the half-row loads: bytes [16g, 16g + 16) and [64 + 16g, + 16)
+// of row n.  x holds A in [0, 4) and B in [4, 8) as loaded.
+__device__ __forceinline__ v8i trade_whole_rows(const v8i& x, int n) {
+    const bool low = n < 8;
+    v8i r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = low ? x[i] : x[4 + i];
+        r[4 + i] = __builtin_amdgcn_update_dpp(0, low ? x[4 + i] : x[i], 0x128, 0xF, 0xF, false);   // row_ror:8
+    }
+    return r;
+}
+
 // The keys of one 64-token group in MFMA B layout: block j (tokens
 // 16j..16j+15) in b[j]; lane l holds the scale of token l of the group and
 // whether that token is scored at all (inside the span, on a valid page).
@@ -141,7 +160,9 @@ struct IndexSmem {
 // more of them, and the rows' geometry comes checked and reported from the
 // caller (geo_vis: the rows' checked spans, geo_b: their request); otherwise
 // wavefront w takes groups w, w + NT/64, ... and the geometry is read here.
-template <int G, int NT, bool kDynamic>
+// kWhole: whole-row key loads with the non-temporal hint (see
+// trade_whole_rows), for launches whose rows all stream most of the stride.
+template <int G, int NT, bool kDynamic, bool kWhole = false>
 __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>& s, int r0, int t0, int t_end,
                                             int fill_lo, int fill_hi, bool report, bool quantize,
                                             const int* geo_vis = nullptr, int geo_b = 0) {
@@ -277,8 +298,20 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
         for (int j = 0; j < 4; ++j) {
             const int tb = tg + 16 * j;
             const int page = tb < vmax ? s.page[(tb >> a.log2_page) - p0] : -1;
-            const size_t row = page >= 0 ? (size_t)page * a.page_size + (tb & pmask) + n : (size_t)n;
-            kg.b[j] = load_q_operand(a.k_code + row * 128, g);
+            if constexpr (kWhole) {
+                typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+                const size_t base = page >= 0 ? (size_t)page * a.page_size + (tb & pmask) : 0;
+                const int lo_row = n & 7, lo_chunk = n < 8 ? g : 4 + g;
+                const int hi_row = (n & 7) + 8, hi_chunk = n < 8 ? 4 + g : g;
+                const i32x4 x = __builtin_nontemporal_load(
+                    reinterpret_cast<const i32x4*>(a.k_code + (base + lo_row) * 128 + 16 * lo_chunk));
+                const i32x4 y = __builtin_nontemporal_load(
+                    reinterpret_cast<const i32x4*>(a.k_code + (base + hi_row) * 128 + 16 * hi_chunk));
+                kg.b[j] = v8i{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+            } else {
+                const size_t row = page >= 0 ? (size_t)page * a.page_size + (tb & pmask) + n : (size_t)n;
+                kg.b[j] = load_q_operand(a.k_code + row * 128, g);
+            }
         }
         const int t = tg + lane;
         const int page = t < vmax ? s.page[(t >> a.log2_page) - p0] : -1;
@@ -295,6 +328,10 @@ __device__ __forceinline__ void score_range(const IndexArgs& a, IndexSmem<G, NT>
 #pragma unroll
         for (int j = 0; j < 4; ++j) pin(kg.b[j]);
         pin(kg.scale);
+        if constexpr (kWhole) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kg.b[j] = trade_whole_rows(kg.b[j], n);
+        }
         const int t = tg + lane;
         // A key whose scale is not a positive finite number is not scored
         // (the head reduction relies on a positive scale); one inside a
@@ -637,12 +674,12 @@ __device__ void keep_candidates(const IndexArgs& a, IndexSmem<1, NT>& s, int r, 
 // workgroup whose wavefronts claim tiles as they go ends them together, and
 // quantizes each group's queries once per unit instead of twice.
 // kKeep (one row a group): the chunk's top-k candidates are kept as well.
-template <int G, bool kKeep>
+template <int G, bool kKeep, bool kWhole = false>
 __global__ __launch_bounds__(256) void index_scores_kernel(IndexArgs a) {
     __shared__ IndexSmem<G, 256> s;
     const int t0 = blockIdx.x * a.chunk;
     const int t_end = min(t0 + a.chunk, a.score_stride);
-    score_range<G, 256, false>(a, s, blockIdx.y * G, t0, t_end, 0, 0, blockIdx.x == 0, true);
+    score_range<G, 256, false, kWhole>(a, s, blockIdx.y * G, t0, t_end, 0, 0, blockIdx.x == 0, true);
     if constexpr (kKeep) keep_candidates<256>(a, s, blockIdx.y, blockIdx.x, t0, t_end - t0);
 }
 
@@ -777,6 +814,10 @@ hipError_t launch_g(IndexArgs a, hipStream_t stream) {
     if constexpr (G == 1) {
         if (a.cand_key != nullptr) {
             index_scores_kernel<1, true><<<grid, 256, 0, stream>>>(a);
+            return hipGetLastError();
+        }
+        if (a.whole_rows) {
+            index_scores_kernel<1, false, true><<<grid, 256, 0, stream>>>(a);
             return hipGetLastError();
         }
     }

@@ -22,6 +22,7 @@ struct IndexArgs {
     int32_t score_stride;
     int32_t* status;
     int32_t chunk;     // chunked launch: tokens per workgroup (set by the launcher)
+    int32_t whole_rows;   // decode launch: whole-row key loads with the non-temporal hint
     // Top-k candidates kept by the decode launch (one row a group), or
     // cand_key == nullptr for scores only.  Chunk j of row r writes to block
     // r * n_chunks + j: up to cand_cap keys and slots, their count (-1: more

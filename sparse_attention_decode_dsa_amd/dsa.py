@@ -17,7 +17,7 @@ import os
 
 import torch
 
-ABI_VERSION = 11
+ABI_VERSION = 12
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DEV_BITS = {1: "PAGE_OOB", 2: "TOPK_OOB", 4: "ROW_RANGE", 8: "GROUP", 16: "NAN", 32: "WRITE", 64: "SCALE"}
@@ -37,7 +37,7 @@ _SIGS = {
     "dsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dsa_quantize_q": ([_p, _i32, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "dsa_index_scores": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
-                          _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
+                          _i32, _i32, _i32, _p, _i32, _p, _p], ctypes.c_int),
     "dsa_index_topk_workspace_size": ([_i32, _i32, _i32], ctypes.c_size_t),
     "dsa_index_topk": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                         _p, _i32, _i32, _i32, _p, ctypes.c_size_t, _p, _p, _p, _p], ctypes.c_int),
@@ -146,9 +146,12 @@ def quantize_q(q_bf16, q_code=None, q_scale=None, stream=None):
 
 def index_scores(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_vis,
                  group_rows: int = 1, score_stride: int | None = None, scores=None, status=None,
-                 stream=None):
+                 stream=None, whole_rows: bool = False):
     """fp8 indexer scores [R, score_stride] f32 (-inf past each row's span) of
-    the bf16 queries q [R, 64, 128] (quantized in the kernel as quantize_q does)."""
+    the bf16 queries q [R, 64, 128] (quantized in the kernel as quantize_q does).
+    whole_rows: the caller's word that every row spans at least 3/4 of
+    score_stride (one row a group); the keys are then read whole-row with the
+    non-temporal hint.  Same scores either way."""
     r, h, d = q.shape
     n_pages, p, dk = k_code.shape
     batch, max_pages = page_table.shape
@@ -163,7 +166,7 @@ def index_scores(q, head_w, k_code, k_scale, page_table, kv_lens, row_req, row_v
         _ptr(k_scale, torch.float32, "k_scale", (n_pages, p)), _ptr(page_table, torch.int32, "page_table"),
         _ptr(kv_lens, torch.int32, "kv_lens", (batch,)), _ptr(row_req, torch.int32, "row_req", (r,)),
         _ptr(row_vis, torch.int32, "row_vis", (r,)), r, batch, n_pages, max_pages, p, h, d, group_rows,
-        _ptr(scores, torch.float32, "scores", (r, score_stride)), score_stride,
+        1 if whole_rows else 0, _ptr(scores, torch.float32, "scores", (r, score_stride)), score_stride,
         _ptr(status, torch.int32, "status", (None,)), _stream(stream)), "dsa_index_scores")
     return scores, status
 
@@ -520,6 +523,11 @@ class DecodeStep:
         n_sel = self.lead_q.shape[0]
         # Rows start 16-byte aligned (the top-k then reads them in 16-byte loads).
         self.score_stride = score_stride or max(64, (int(self.lead_vis.max()) + 63) // 64 * 64)
+        # Rows that all span at least 3/4 of the stride keep every workgroup
+        # streaming keys to the end: whole-row loads with the non-temporal
+        # hint pay there and cost ragged rows (lengths known here, on the host).
+        self.whole_rows = (self.group_rows == 1 and n_sel > 0
+                           and 4 * int(self.lead_vis.min()) >= 3 * self.score_stride)
         self.scores = torch.empty((n_sel, self.score_stride), dtype=torch.float32, device=dev)
         if self.index_topk:
             need = index_topk_workspace_size(n_sel, self.score_stride, k)
@@ -550,7 +558,7 @@ class DecodeStep:
             index_scores(self.lead_q, self.lead_w, i.k_code, i.k_scale, i.page_table,
                          i.kv_lens, self.lead_req, self.lead_vis, group_rows=self.group_rows,
                          score_stride=self.score_stride, scores=self.scores, status=self.status,
-                         stream=stream)
+                         stream=stream, whole_rows=self.whole_rows)
             if self.phys_rows:
                 topk_rows(self.scores, self.lead_vis, self.lead_req, i.page_table, i.kv_cache.shape[0],
                           i.kv_cache.shape[1], i.top_k, self.index_splits, workspace=self.workspace,

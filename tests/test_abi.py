@@ -52,13 +52,16 @@ def test_abi_version_and_status_strings(L):
 def _idx(L, **kw):
     a = dict(q=P, head_w=P, k_code=P, k_scale=P, page_table=P, kv_lens=P,
              row_req=P, row_vis=P, n_rows=4, batch=2, num_pages=10, max_pages=5, page_size=256,
-             n_heads=64, head_dim=128, group_rows=1, scores=P, score_stride=1280, status=P,
+             n_heads=64, head_dim=128, group_rows=1, flags=0, scores=P, score_stride=1280, status=P,
              stream=None)
     a.update(kw)
     return L.dsa_index_scores(*a.values())
 
 
 def test_index_scores_validation(L):
+    assert _idx(L, flags=2) == SHAPE                            # unknown flag bits
+    assert _idx(L, flags=1, group_rows=2) == SHAPE              # whole-row loads: one row a group
+    assert _idx(L, flags=1, n_rows=0) == OK
     assert _idx(L, n_heads=32) == UNSUP
     assert _idx(L, head_dim=64) == UNSUP
     assert _idx(L, page_size=100) == UNSUP

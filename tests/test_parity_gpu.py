@@ -554,6 +554,27 @@ def test_long_prefix_prefill_sampled_rows():
 
 # ------------------------------------------------------------------ properties
 
+@pytest.mark.parametrize("name", ["c1_l32k", "c1", "c2"])
+def test_whole_row_key_loads_give_the_same_scores(name):
+    """The decode indexer's whole-row, non-temporal key loads (the caller's
+    flag) score exactly as its half-row loads, on uniform and on ragged rows
+    (the flag only promises long rows; it never changes a score), with every
+    row of the workload in one launch.  The step sets the flag only when
+    every row spans at least 3/4 of the score stride."""
+    inp = W.to(W.make(name), "cuda")
+    step = dsa.DecodeStep(inp)
+    assert step.whole_rows == (name == "c1_l32k")
+    say(f"whole-row loads {name}")
+    args = (inp.q_idx, inp.head_w, inp.k_code, inp.k_scale, inp.page_table, inp.kv_lens, inp.row_req,
+            inp.row_vis)
+    half, st0 = dsa.index_scores(*args, score_stride=step.score_stride)
+    whole, st1 = dsa.index_scores(*args, score_stride=step.score_stride, whole_rows=True)
+    torch.cuda.synchronize()
+    dsa.check_status(st0)
+    dsa.check_status(st1)
+    assert torch.equal(half.view(torch.int32), whole.view(torch.int32))
+
+
 def test_page_permutation_and_run_to_run_determinism():
     inp = W.to(W.make("c0"), "cuda")
     a = run_step(inp)
