@@ -910,9 +910,11 @@ void topk_filter_kernel(TopkArgs a) {
 // Row r's exact top k straight from its scores [0, v), v > k, when the kept
 // keys do not hold it: three radix passes of 12, 10 and 10 bits over the
 // whole row, then the emission in rounds of kThreads positions, each round
-// one scan.  Slow, and only for the rows whose cut missed.
+// one scan.  Slow, and only for the rows whose cut missed.  The scan toggle comes
+// by value (every caller returns right after), so the callers' own toggle
+// stays in a register rather than in scratch memory.
 template <typename Out>
-__device__ void topk_row_streamed(TopkSmem& s, const float* row, int v, int k, const Out& out, int& tog) {
+__device__ void topk_row_streamed(TopkSmem& s, const float* row, int v, int k, const Out& out, int tog) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0u, mask = 0u, kk = (uint32_t)k;
 #pragma unroll 1
