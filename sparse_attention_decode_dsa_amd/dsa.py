@@ -484,7 +484,7 @@ class DecodeStep:
     def __init__(self, inp, index_splits: int | None = None, attn_splits: int | None = None,
                  group_rows: int | None = None, score_stride: int | None = None,
                  index_share: int | None = None, index_topk: bool | None = None,
-                 phys_rows: bool | None = None):
+                 phys_rows: bool | None = None, whole_rows: bool = False):
         self.inp = inp
         cfg = inp.cfg
         self.index_splits = index_splits or cfg.index_splits
@@ -523,10 +523,12 @@ class DecodeStep:
         n_sel = self.lead_q.shape[0]
         # Rows start 16-byte aligned (the top-k then reads them in 16-byte loads).
         self.score_stride = score_stride or max(64, (int(self.lead_vis.max()) + 63) // 64 * 64)
-        # Rows that all span at least 3/4 of the stride keep every workgroup
-        # streaming keys to the end: whole-row loads with the non-temporal
-        # hint pay there and cost ragged rows (lengths known here, on the host).
-        self.whole_rows = (self.group_rows == 1 and n_sel > 0
+        # whole_rows (opt-in): the indexer's whole-row, non-temporal key loads,
+        # taken only when every row spans at least 3/4 of the stride (lengths
+        # known here, on the host).  Off by default: measured steps come out
+        # from 3 us faster to 0.6 us slower depending on the box, and the
+        # indexer alone is slower with them.
+        self.whole_rows = (bool(whole_rows) and self.group_rows == 1 and n_sel > 0
                            and 4 * int(self.lead_vis.min()) >= 3 * self.score_stride)
         self.scores = torch.empty((n_sel, self.score_stride), dtype=torch.float32, device=dev)
         if self.index_topk:

@@ -559,10 +559,11 @@ def test_whole_row_key_loads_give_the_same_scores(name):
     """The decode indexer's whole-row, non-temporal key loads (the caller's
     flag) score exactly as its half-row loads, on uniform and on ragged rows
     (the flag only promises long rows; it never changes a score), with every
-    row of the workload in one launch.  The step sets the flag only when
-    every row spans at least 3/4 of the score stride."""
+    row of the workload in one launch.  A step asked for it takes it only
+    when every row spans at least 3/4 of the score stride; by default never."""
     inp = W.to(W.make(name), "cuda")
-    step = dsa.DecodeStep(inp)
+    assert not dsa.DecodeStep(inp).whole_rows
+    step = dsa.DecodeStep(inp, whole_rows=True)
     assert step.whole_rows == (name == "c1_l32k")
     say(f"whole-row loads {name}")
     args = (inp.q_idx, inp.head_w, inp.k_code, inp.k_scale, inp.page_table, inp.kv_lens, inp.row_req,
