@@ -278,10 +278,11 @@ def test_topk_all_equal_scores_keep_lowest_slots():
 
 # ------------------------------------------------------------------ LSE merge alone
 
-@pytest.mark.parametrize("r,h,s", [(5, 32, 7), (20, 32, 3), (40, 32, 9), (33, 32, 2), (3, 16, 64)])
+@pytest.mark.parametrize("r,h,s", [(5, 32, 7), (20, 32, 3), (40, 32, 9), (33, 32, 2), (3, 16, 64),
+                                   (64, 32, 4), (6, 32, 1)])
 def test_lse_merge_synthetic(r, h, s):
-    """Pair counts under 512, under 1024 and above, with the few-split and
-    the many-split kernels (a pair's columns go to 4, 2 or 1 wavefronts)."""
+    """Pair counts under 512, under 1024 and above, with the one-split and
+    the batched kernels (a pair's columns go to 4, 2 or 1 wavefronts)."""
     rng = np.random.default_rng(7 + r + s)
     po = rng.normal(size=(r, h, s, 512)).astype(np.float32)
     pl = (rng.normal(size=(r, h, s)) * 5).astype(np.float32)
