@@ -5,9 +5,9 @@
 // wavefront finds m = max_s lse_s and the weights e^{lse_s - m}; each lane
 // then accumulates 8 of the 512 output columns over the splits.  A split of
 // weight 0 adds nothing, whatever its partial holds.  From two splits on,
-// eight splits' loads are in flight together (with bf16 partials that is
-// faster at four splits too: bulk decode's merge 4.95 -> 4.20 us, paired);
-// a lone split is read directly.
+// four (up to four splits) or eight splits' loads are in flight together
+// (with bf16 partials that is faster at four splits too: bulk decode's merge
+// 4.95 -> 3.74 us, paired); a lone split is read directly.
 // With fewer than 1024 (row, head) pairs a pair's columns are split over two
 // or four wavefronts (each computing the pair's weights itself), so that a
 // launch of few rows and many splits still reads the partials on most of the
@@ -27,7 +27,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDv = 512;
-constexpr int kBatch = 8;   // splits whose partials are in flight together (many-split kernel)
 
 // CPL (8, 4 or 2) consecutive output columns per lane: 512 / (64 CPL)
 // wavefronts share one (row, head), so a launch with few pairs still spreads
@@ -128,9 +127,9 @@ __global__ __launch_bounds__(256) void lse_merge_few_kernel(MergeArgs a) {
     merge_store<CPL>(a, h, acc);
 }
 
-// More splits: kBatch splits' loads issued before any is used; splits past
-// the end reload the last one and get weight 0.
-template <int CPL>
+// More splits: kBatch (4 or 8) splits' loads issued before any is used;
+// splits past the end reload the last one and get weight 0.
+template <int CPL, int kBatch>
 __global__ __launch_bounds__(256) void lse_merge_many_kernel(MergeArgs a) {
     MergeHead h;
     if (!merge_head<CPL>(a, h)) return;
@@ -156,7 +155,8 @@ hipError_t launch_cpl(const MergeArgs& a, hipStream_t stream) {
     const int64_t waves = (int64_t)a.n_rows * a.n_heads * Cols<CPL>::kParts;
     const unsigned wgs = (unsigned)((waves + 3) / 4);
     if (a.n_splits == 1) lse_merge_few_kernel<CPL><<<wgs, 256, 0, stream>>>(a);
-    else lse_merge_many_kernel<CPL><<<wgs, 256, 0, stream>>>(a);
+    else if (a.n_splits <= 4) lse_merge_many_kernel<CPL, 4><<<wgs, 256, 0, stream>>>(a);
+    else lse_merge_many_kernel<CPL, 8><<<wgs, 256, 0, stream>>>(a);
     return hipGetLastError();
 }
 
